@@ -1,0 +1,49 @@
+// Internal interface between the C-ABI layer (gdn_api.cpp) and the kernel
+// launchers.  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gdn.h"
+
+namespace gdn {
+
+// A validated problem with plain integer sizes.
+struct Problem {
+  int B, H, dk, dv, F, S;
+  long long T;         // F * S
+  bool qkv_bf16;       // q/k/v element type (else fp32)
+  bool out_bf16;       // out element type (else fp32)
+  float key_scale;
+};
+
+// Device pointers of one call.
+struct Tensors {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;      // log-gate
+  const float* beta;
+  const float* h0;     // may be null (zeros)
+  void* out;
+  float* hT;           // may be null
+};
+
+// Token-sequential reference path (gdn_recurrent.hip).
+size_t recurrent_workspace(const Problem& p, int direction);
+hipError_t recurrent_launch(const Problem& p, int direction, const Tensors& t,
+                            void* workspace, hipStream_t stream);
+
+// Frame-chunked MFMA path (gdn_chunked.hip).
+// Returns null when supported, else a static reason string.
+const char* chunked_unsupported_reason(const Problem& p);
+size_t chunked_workspace(const Problem& p, int direction);
+hipError_t chunked_launch(const Problem& p, int direction, const Tensors& t,
+                          void* workspace, hipStream_t stream);
+
+// Round-up helper for workspace carving.
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace gdn

@@ -1,0 +1,154 @@
+/*
+ * libgdn -- frame-wise gated delta rule (Gated DeltaNet) layer forward on
+ * AMD Instinct MI355X (gfx950).  C ABI: plain pointers and sizes only.
+ *
+ * What is computed.  Per (batch b, head h) the layer carries a state
+ * H in R^{d_k x d_v} (fp32).  For every token t of a frame-ordered sequence
+ * (token t = f * tokens_per_frame + s, raster order inside a frame):
+ *
+ *     H   <- exp(g_t) * H                                  decay gate
+ *     e   <- v_t - H^T (c k_t)                             value residual
+ *     H   <- H + beta_t * (c k_t) e^T                      delta-rule write
+ *     o_t  = H^T q_t                                       read after write
+ *
+ * with c = key_scale.  This is the token-wise Gated DeltaNet update of
+ * "SANA-WM: Efficient Minute-Scale World Modeling with Hybrid Linear
+ * Diffusion Transformer" (summary page), section 3.2 "Frame-wise Gated
+ * DeltaNet (GDN)", token-wise update equation, written for the stored
+ * orientation H = S^T (the page's S is d_v x d_k).  The sequence is scanned
+ * one latent frame at a time with the state handed from frame to frame (same
+ * section, frame-wise recurrence; "SANA-WM: a minute of camera-controlled
+ * world, and where its memory actually lives", section "The linear part": 880
+ * tokens per 704x1280 frame, 121 frames per minute, 112x112 state per head).
+ *
+ * Directions (same summary page, section 3.2 "Bidirectional and Chunk-Causal
+ * GDN Variants"): GDN_FORWARD scans past -> future; GDN_BACKWARD scans the
+ * whole token axis reversed (frames and the raster order inside frames);
+ * GDN_BIDIRECTIONAL returns the sum of the two scans' outputs, the forward
+ * scan starting from initial_state and the reversed scan from zero.
+ *
+ * Layouts (all tensors dense, row-major, caller-owned DEVICE memory):
+ *   q, k        [B, T, H, d_k]    qkv_dtype (fp32 or bf16)
+ *   v           [B, T, H, d_v]    qkv_dtype
+ *   log_gate    [B, T, H]         fp32, g_t <= 0 on the documented domain
+ *   beta        [B, T, H]         fp32, in [0, 1] on the documented domain
+ *   states      [B, H, d_k, d_v]  fp32, element [b][h][i][j] maps key
+ *                                 component i to value component j
+ *   out         [B, T, H, d_v]    out_dtype
+ * with T = frames * tokens_per_frame.  Every tensor pointer must be 16-byte
+ * aligned.
+ *
+ * Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream)
+ * and return after enqueueing.  The library allocates no device memory: the
+ * caller passes a workspace of at least gdn_workspace_size() bytes.  All
+ * arguments are validated on the host before anything is enqueued; on any
+ * error nothing is enqueued and a status other than GDN_OK is returned, with
+ * a description available from gdn_last_error_message() on the same thread.
+ * Input values are not checked: outside the documented domain, and for
+ * NaN/Inf inputs, values propagate.  No C++ exception crosses this boundary
+ * and the library never prints.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef int32_t gdn_status;
+enum {
+  GDN_OK = 0,
+  GDN_ERR_INVALID_ARGUMENT = 1,     /* null pointer, bad size, bad enum, misalignment */
+  GDN_ERR_UNSUPPORTED = 2,          /* valid request this build does not implement */
+  GDN_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes < gdn_workspace_size() */
+  GDN_ERR_HIP = 4                   /* a HIP runtime call or kernel launch failed */
+};
+
+enum { GDN_F32 = 0, GDN_BF16 = 1 };                                   /* tensor dtypes */
+enum { GDN_FORWARD = 0, GDN_BACKWARD = 1, GDN_BIDIRECTIONAL = 2 };    /* directions */
+
+/* Algorithm selection.  AUTO picks the frame-chunked MFMA path for bf16 q/k/v
+ * and the token-recurrent fp32 path for fp32 q/k/v (whose tolerance needs fp32
+ * products).  RECURRENT forces the token-sequential kernel (any dtype). */
+enum { GDN_ALGO_AUTO = 0, GDN_ALGO_CHUNKED = 1, GDN_ALGO_RECURRENT = 2 };
+
+typedef struct gdn_problem {
+  int32_t abi_version;        /* must equal GDN_ABI_VERSION */
+  int32_t batch;              /* B >= 1 */
+  int32_t heads;              /* H >= 1 */
+  int32_t d_k;                /* key/query width: multiple of 16, <= 128 */
+  int32_t d_v;                /* value width: multiple of 16, <= 128 */
+  int32_t frames;             /* F >= 1 */
+  int32_t tokens_per_frame;   /* S >= 1; T = F * S */
+  int32_t qkv_dtype;          /* GDN_F32 or GDN_BF16 */
+  int32_t out_dtype;          /* GDN_F32 or GDN_BF16 */
+  int32_t algo;               /* GDN_ALGO_* */
+  float key_scale;            /* keys are multiplied by this on load (finite) */
+  int32_t reserved[5];        /* must be zero */
+} gdn_problem;
+
+/* Version of this ABI (GDN_ABI_VERSION of the built library). */
+int32_t gdn_abi_version(void);
+
+/* Static, never-NULL text for a status code. */
+const char* gdn_status_string(gdn_status status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none).
+ * The pointer stays valid until the next libgdn call on that thread. */
+const char* gdn_last_error_message(void);
+
+/* Bytes of device workspace gdn_forward needs for (problem, direction).
+ * Pure host computation.  Errors as gdn_forward's argument checks. */
+gdn_status gdn_workspace_size(const gdn_problem* problem, int32_t direction,
+                              size_t* bytes_out);
+
+/* Whole-sequence layer forward (offline / bidirectional mode).
+ *   direction      GDN_FORWARD, GDN_BACKWARD or GDN_BIDIRECTIONAL
+ *   initial_state  [B,H,d_k,d_v] fp32 or NULL (= zeros); seeds the forward scan
+ *                  (the reversed scan in GDN_BACKWARD mode)
+ *   final_state    [B,H,d_k,d_v] fp32 or NULL; receives the state after the
+ *                  last token of the forward scan (of the reversed scan in
+ *                  GDN_BACKWARD mode).  May alias initial_state; no other
+ *                  aliasing between arguments is allowed.
+ *   workspace      device scratch of workspace_bytes >= gdn_workspace_size();
+ *                  may be NULL when that size is 0.  Its contents on entry are
+ *                  ignored; it must not be used by anything else until the
+ *                  enqueued work has finished.
+ * Pages: the direction combination is the summary page's section 3.2,
+ * "Bidirectional and Chunk-Causal GDN Variants" (independent scans, outputs
+ * summed). */
+gdn_status gdn_forward(const gdn_problem* problem, int32_t direction,
+                       const void* q, const void* k, const void* v,
+                       const float* log_gate, const float* beta,
+                       const float* initial_state,
+                       void* out, float* final_state,
+                       void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* One frame of the chunk-causal streaming forward scan with the state carried
+ * between calls (summary page, section 3.2: in chunk-causal inference the
+ * forward scan stays global; the state is the only thing passed on).
+ *   problem->frames must be 1 (GDN_ERR_INVALID_ARGUMENT otherwise).
+ *   state_in   [B,H,d_k,d_v] fp32 or NULL (= zeros)
+ *   state_out  [B,H,d_k,d_v] fp32, required; may alias state_in (in place).
+ *   workspace  as gdn_forward with GDN_FORWARD.
+ * Calling it once per frame with state_out fed back as state_in reproduces
+ * gdn_forward(GDN_FORWARD) over the concatenated frames. */
+gdn_status gdn_step(const gdn_problem* problem,
+                    const void* q, const void* k, const void* v,
+                    const float* log_gate, const float* beta,
+                    const float* state_in, float* state_out,
+                    void* out,
+                    void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif  /* GDN_H_ */

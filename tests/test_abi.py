@@ -1,0 +1,117 @@
+"""libgdn's C ABI on the host: exports, version, status text, workspace sizing
+and argument validation.  No compute call is made, so no GPU is needed: every
+check below fails (or sizes) before the library makes any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_frame_amd as G
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = G.lib()
+    names = declared_functions()
+    assert {"gdn_forward", "gdn_step", "gdn_workspace_size"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in gdn.h but not exported"
+
+
+def test_version_and_status_strings():
+    L = G.lib()
+    assert L.gdn_abi_version() == G.ABI_VERSION == 1
+    for s, text in enumerate(["GDN_OK", "GDN_ERR_INVALID_ARGUMENT", "GDN_ERR_UNSUPPORTED",
+                              "GDN_ERR_WORKSPACE_TOO_SMALL", "GDN_ERR_HIP"]):
+        assert L.gdn_status_string(s).decode() == text
+    assert L.gdn_status_string(99).decode() == "GDN_ERR_UNKNOWN_STATUS"
+
+
+def prob(**kw):
+    base = dict(batch=1, heads=2, d_k=64, d_v=64, frames=3, tokens_per_frame=100,
+                qkv_dtype=G.BF16, out_dtype=G.BF16, algo="auto")
+    base.update(kw)
+    return G.make_problem(**base)
+
+
+def test_recurrent_workspace_is_the_bidirectional_accumulator():
+    p = prob(algo="recurrent")
+    assert G.workspace_size(p, "fwd") == 0
+    assert G.workspace_size(p, "bwd") == 0
+    assert G.workspace_size(p, "bidir") == 1 * 300 * 2 * 64 * 4
+
+
+@pytest.mark.parametrize("field,value", [
+    ("abi_version", 2), ("batch", 0), ("heads", -1), ("frames", 0), ("tokens_per_frame", 0),
+    ("d_k", 20), ("d_k", 144), ("d_v", 8), ("qkv_dtype", 7), ("out_dtype", -1), ("algo", 9),
+])
+def test_bad_problem_fields_are_rejected(field, value):
+    p = prob()
+    setattr(p, field, value)
+    with pytest.raises(G.GdnError) as e:
+        G.workspace_size(p, "bidir")
+    assert e.value.status == G.ERR_INVALID_ARGUMENT
+    assert G.lib().gdn_last_error_message().decode() != ""
+
+
+def test_reserved_and_key_scale_and_direction_checks():
+    p = prob()
+    p.reserved[2] = 1
+    with pytest.raises(G.GdnError):
+        G.workspace_size(p, "bidir")
+    p = prob(key_scale=float("nan"))
+    with pytest.raises(G.GdnError):
+        G.workspace_size(p, "bidir")
+    n = ctypes.c_size_t()
+    assert G.lib().gdn_workspace_size(ctypes.byref(prob()), 7, ctypes.byref(n)) == G.ERR_INVALID_ARGUMENT
+    assert G.lib().gdn_workspace_size(None, 0, ctypes.byref(n)) == G.ERR_INVALID_ARGUMENT
+    assert G.lib().gdn_workspace_size(ctypes.byref(prob()), 0, None) == G.ERR_INVALID_ARGUMENT
+
+
+FAKE = 0x10000  # never dereferenced: validation fails before any use
+
+
+def call_forward(p, direction=G.BIDIRECTIONAL, q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, h0=None,
+                 out=FAKE, hT=None, ws=None, ws_bytes=0):
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return G.lib().gdn_forward(ctypes.byref(p), direction, vp(q), vp(k), vp(v), vp(g), vp(b),
+                               vp(h0), vp(out), vp(hT), vp(ws), ws_bytes, None)
+
+
+def test_forward_rejects_null_and_misaligned_pointers_without_launching():
+    p = prob(algo="recurrent")
+    for name in ("q", "k", "v", "g", "b", "out"):
+        assert call_forward(p, **{name: None}) == G.ERR_INVALID_ARGUMENT
+        assert call_forward(p, **{name: FAKE + 2}) == G.ERR_INVALID_ARGUMENT
+    assert call_forward(p, h0=FAKE + 4) == G.ERR_INVALID_ARGUMENT
+    assert call_forward(p, direction=5) == G.ERR_INVALID_ARGUMENT
+
+
+def test_forward_rejects_small_workspace():
+    p = prob(algo="recurrent")
+    assert call_forward(p) == G.ERR_WORKSPACE_TOO_SMALL
+    need = G.workspace_size(p, "bidir")
+    assert call_forward(p, ws=FAKE, ws_bytes=need - 1) == G.ERR_WORKSPACE_TOO_SMALL
+    assert "needed" in G.lib().gdn_last_error_message().decode()
+
+
+def test_step_requires_one_frame_and_state_out():
+    L = G.lib()
+    vp = ctypes.c_void_p
+    p = prob(frames=2, algo="recurrent")
+    args = [vp(FAKE)] * 5
+    assert L.gdn_step(ctypes.byref(p), *args, None, vp(FAKE), vp(FAKE), None, 0, None) \
+        == G.ERR_INVALID_ARGUMENT
+    p = prob(frames=1, algo="recurrent")
+    assert L.gdn_step(ctypes.byref(p), *args, None, None, vp(FAKE), None, 0, None) \
+        == G.ERR_INVALID_ARGUMENT
+    assert "state_out" in L.gdn_last_error_message().decode()
