@@ -15,6 +15,7 @@ import ctypes
 import os
 
 __all__ = ["forward", "step", "workspace_size", "make_problem", "lib", "GdnError",
+           "set_segment_tokens",
            "FORWARD", "BACKWARD", "BIDIRECTIONAL", "ABI_VERSION", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
@@ -66,6 +67,8 @@ def lib():
         L.gdn_workspace_size.argtypes = [P, i32, ctypes.POINTER(sz)]
         L.gdn_forward.restype = i32
         L.gdn_forward.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.gdn_set_segment_tokens.restype = None
+        L.gdn_set_segment_tokens.argtypes = [i32]
         L.gdn_step.restype = i32
         L.gdn_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         if L.gdn_abi_version() != ABI_VERSION:
@@ -97,6 +100,11 @@ def workspace_size(problem: Problem, direction=BIDIRECTIONAL) -> int:
     n = ctypes.c_size_t(0)
     _check(lib().gdn_workspace_size(ctypes.byref(problem), DIRECTION[direction], ctypes.byref(n)))
     return n.value
+
+
+def set_segment_tokens(tokens: int) -> None:
+    """Tokens per segment of the chunked path (0 = automatic); see gdn.h."""
+    lib().gdn_set_segment_tokens(int(tokens))
 
 
 def _torch():

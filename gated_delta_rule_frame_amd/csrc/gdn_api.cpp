@@ -132,6 +132,8 @@ const char* gdn_status_string(gdn_status s) {
 
 const char* gdn_last_error_message(void) { return g_last_error.c_str(); }
 
+void gdn_set_segment_tokens(int32_t tokens) { gdn::set_segment_tokens(tokens); }
+
 gdn_status gdn_workspace_size(const gdn_problem* pr, int32_t direction, size_t* bytes_out) {
   try {
     if (!bytes_out) return fail(GDN_ERR_INVALID_ARGUMENT, "bytes_out is NULL");

@@ -43,6 +43,8 @@ size_t chunked_workspace(const Problem& p, int direction);
 hipError_t chunked_launch(const Problem& p, int direction, const Tensors& t,
                           void* workspace, hipStream_t stream);
 
+void set_segment_tokens(int tokens);
+
 // Round-up helper for workspace carving.
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

@@ -147,6 +147,12 @@ gdn_status gdn_step(const gdn_problem* problem,
                     void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/* Tuning knob of the chunked path: tokens per segment (rounded up to a
+ * multiple of 64; 0 restores the automatic choice).  Process-wide; results do
+ * not depend on it beyond rounding, but gdn_workspace_size() does, so size
+ * the workspace after setting it.  Thread-safe. */
+void gdn_set_segment_tokens(int32_t tokens);
+
 #ifdef __cplusplus
 }  /* extern "C" */
 #endif
