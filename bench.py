@@ -1,0 +1,259 @@
+#!/usr/bin/env python3
+"""One-GPU benchmark of the frame-wise gated delta rule layer forward.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one whole-sequence layer forward (gdn_forward) over one batch of
+synthetic inputs already resident in HBM.  The default workload is the 60 s
+720p clip: batch 1, 20 heads x 112, 121 latent frames x 880 tokens (106,480
+tokens), bf16 q/k/v, fp32 gates/state/accumulation and fp32 output, run in
+bidirectional mode (forward scan + reversed scan, summed), as in the SANA-WM
+summary page, section 3.2 "Bidirectional and Chunk-Causal GDN Variants".
+
+Before timing, the run checks parity against the float64 CPU oracle on one
+sampled head over the whole sequence (heads are independent, so that head's
+outputs and final state are exact targets); that same oracle run, limited to
+one CPU thread, is the reported CPU baseline.  Prints exactly one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN layer fwd tokens/s & % bf16 MFMA peak, 121×880-token 60 s clip, 1 GPU"
+PEAK_TFLOPS = 2516.6        # MI355X dense fp16/bf16 MFMA, 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+KERNEL_SOURCES = ("gdn_chunked.hip", "gdn_mfma.h", "gdn_common.h")
+
+
+# --------------------------------------------------------------- FLOP models
+
+def canonical_flops(C, dk, dv):
+    """Frame-as-chunk count per (batch, head, frame, direction): strict-lower
+    K K^T plus forward substitution on [W|U], causal Q K^T and its product with
+    U', and the three C x d x d state products."""
+    return C * (C - 1) * (2 * dk + dv) + C * (C + 1) * (dk + dv) + 6 * C * dk * dv
+
+
+def subchunk_sizes(T, L, c=64):
+    """Token counts of the 64-token sub-chunks, per segment of L tokens."""
+    segs = []
+    for s0 in range(0, T, L):
+        n = min(L, T - s0)
+        segs.append([min(c, n - a) for a in range(0, n, c)])
+    return segs
+
+
+def out_flops(n, d):
+    """Algorithmic flops of the output pass on one sub-chunk of n tokens."""
+    return n * (n - 1) * d + 4 * n * (n + 1) * d + 6 * n * d * d + n ** 3 // 3
+
+
+def map_flops(n, d):
+    """Algorithmic flops of the segment-map pass on one sub-chunk (state [P|Q])."""
+    return n * (n - 1) * d + 2 * n * (n + 1) * d + 8 * n * d * d + n ** 3 // 3
+
+
+def executed_flops(T, L, d, bh, ndir):
+    """Per-kernel algorithmic flops of one call of the chunked path."""
+    segs = subchunk_sizes(T, L)
+    per_out = sum(out_flops(n, d) for seg in segs for n in seg)
+    # maps are formed for every segment but the last one of each scan
+    per_map_f = sum(map_flops(n, d) for seg in segs[:-1] for n in seg)
+    per_map_b = sum(map_flops(n, d) for seg in segs[1:] for n in seg)
+    maps = per_map_f if ndir == 1 else per_map_f + per_map_b
+    chain = (len(segs) - 1) * 2 * d ** 3
+    return {"seg_out_kernel": per_out * bh * ndir, "seg_map_kernel": maps * bh,
+            "seg_chain_kernel": chain * bh * ndir}
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "gated_delta_rule_frame_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None if it is missing or was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except OSError:
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+# --------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="clip60s_121x880_h20d112")
+    ap.add_argument("--direction", default=None, choices=["fwd", "bwd", "bidir"])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--segment", type=int, default=0, help="tokens per segment (0 = automatic)")
+    ap.add_argument("--parity-head", type=int, default=7)
+    ap.add_argument("--no-parity", action="store_true", help="skip the oracle check and CPU baseline")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        sys.exit(f"bench.py measures one GPU only (got --gpus {args.gpus}); the layer's multi-GPU "
+                 "sharding is a design note, not a runnable path in this build")
+
+    import torch
+    import gated_delta_rule_frame_amd as G
+    from gdn_inputs import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    w = {wl.name: wl for wl in WORKLOADS}[args.workload]
+    direction = args.direction or ("bidir" if w.mode == "bidir" else "fwd")
+    dev = torch.device("cuda:0")
+    G.set_segment_tokens(args.segment)
+
+    x = make_inputs(w, args.seed)
+    qkv_dt = torch.bfloat16 if w.qkv_dtype == "bf16" else torch.float32
+    d = {n: torch.from_numpy(x[n]).to(dev, qkv_dt) for n in ("q", "k", "v")}
+    for n in ("log_gate", "beta"):
+        d[n] = torch.from_numpy(x[n]).to(dev)
+    h0 = torch.from_numpy(x["h0"]).to(dev) if np.any(x["h0"]) else None
+    B, T, H, dk, dv = w.batch, w.tokens, w.heads, w.d_k, w.d_v
+    prob = G.make_problem(B, H, dk, dv, w.frames, w.tokens_per_frame, G.BF16 if w.qkv_dtype == "bf16" else G.F32,
+                          G.F32, "auto")
+    ws = torch.empty(max(G.workspace_size(prob, direction), 16), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    hT = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+
+    def step():
+        G.forward(d["q"], d["k"], d["v"], d["log_gate"], d["beta"], h0, direction,
+                  tokens_per_frame=w.tokens_per_frame, out=out, final_state=hT, workspace=ws)
+
+    # ---- parity on a sampled head + CPU baseline (the same oracle run)
+    parity, cpu_baseline = None, None
+    step()
+    torch.cuda.synchronize()
+    if not args.no_parity:
+        from threadpoolctl import threadpool_limits
+        from oracle import gdn_oracle as O
+        hh = min(args.parity_head, H - 1)
+        a = [x[n][:1, :, hh:hh + 1] for n in ("q", "k", "v", "log_gate", "beta")]
+        with threadpool_limits(1):
+            t0 = time.perf_counter()
+            ro, rH = O.forward(direction, *a, x["h0"][:1, hh:hh + 1])
+            cpu_s = time.perf_counter() - t0
+        o = out[:1, :, hh:hh + 1].double().cpu().numpy()
+        s = hT[:1, hh:hh + 1].double().cpu().numpy()
+        rel = lambda u, r: float(np.max(np.abs(u - r)) / np.sqrt(np.mean(r * r)))
+        eo, es = rel(o, ro), rel(s, rH)
+        tol = TOL[w.qkv_dtype]
+        parity = {"head": hh, "out_err": eo, "state_err": es, "tol": tol, "pass": eo <= tol and es <= tol}
+        if not parity["pass"]:
+            print(json.dumps({"metric": METRIC, "error": "parity failed", "parity": parity}))
+            sys.exit(1)
+        # oracle tokens/s for the whole workload: it handled 1 of B*H heads
+        cpu_rate = T / cpu_s / (B * H)
+        cpu_baseline = {"value": cpu_rate, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                        "sample": f"float64 NumPy oracle, {direction} over all {T} tokens of 1 of {B * H} "
+                                  f"heads ({cpu_s:.1f} s on 1 thread of {cpu_model()}), scaled to {B * H} heads"}
+
+    # ---- timing
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    G.profile_reset()
+    G.profile_enable(True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    G.profile_enable(False)
+    ms = ev0.elapsed_time(ev1) / args.steps
+    prof = G.profile_read()
+
+    tokens_per_s = B * T / (ms / 1e3)
+    ndir = 2 if direction == "bidir" else 1
+    L = G.segment_plan(prob, direction) if hasattr(G, "segment_plan") else None
+    canon = canonical_flops(w.tokens_per_frame, dk, dv) * B * H * w.frames * ndir
+    kern = {k: {"launches": n, "avg_ms": (t / n if n else None)} for k, (n, t) in prof.items() if n}
+    roof, flops_exec = None, None
+    if "seg_out_kernel" in kern and L:
+        fl = executed_flops(T, L, dk, B * H, ndir)
+        flops_exec = sum(fl.values())
+        for k in fl:
+            if k in kern:
+                kern[k]["tflops"] = fl[k] / (kern[k]["avg_ms"] / 1e3) / 1e12
+        dom = max(kern, key=lambda k: kern[k]["avg_ms"] * kern[k]["launches"])
+        achieved = fl.get(dom, 0) / (kern[dom]["avg_ms"] / 1e3) / 1e12
+        traffic = read_traffic(dom, w.name)
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_TFLOPS, "traffic": traffic, "kernel": dom}
+    credited = min(canon, flops_exec) if flops_exec else canon
+    layer_tflops = credited / (ms / 1e3) / 1e12
+
+    line = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "direction": direction, "batch": B, "heads": H, "d_k": dk, "d_v": dv,
+            "frames": w.frames, "tokens_per_frame": w.tokens_per_frame, "tokens": T,
+            "inputs": f"{w.qkv_dtype} q/k/v, fp32 log-gate/beta/state, fp32 out; fp16 MFMA operands, fp32 accumulation",
+            "segment_tokens": L, "seed": args.seed,
+        },
+        "layer": {"canonical_gflop": canon / 1e9, "executed_gflop": (flops_exec or 0) / 1e9,
+                  "credited_tflops": layer_tflops, "pct_peak": 100 * layer_tflops / PEAK_TFLOPS,
+                  "recurrent_min_gflop": 6 * dk * dv * B * H * T * ndir / 1e9},
+        "kernels": kern,
+        "parity": parity,
+        "roofline": roof,
+        "cpu_baseline": cpu_baseline,
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

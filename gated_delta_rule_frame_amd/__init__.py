@@ -15,7 +15,7 @@ import ctypes
 import os
 
 __all__ = ["forward", "step", "workspace_size", "make_problem", "lib", "GdnError",
-           "set_segment_tokens",
+           "set_segment_tokens", "segment_plan", "profile_enable", "profile_reset", "profile_read",
            "FORWARD", "BACKWARD", "BIDIRECTIONAL", "ABI_VERSION", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
@@ -69,6 +69,16 @@ def lib():
         L.gdn_forward.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.gdn_set_segment_tokens.restype = None
         L.gdn_set_segment_tokens.argtypes = [i32]
+        L.gdn_profile_enable.restype = i32
+        L.gdn_profile_enable.argtypes = [i32]
+        L.gdn_profile_reset.restype = i32
+        L.gdn_profile_reset.argtypes = []
+        L.gdn_profile_read.restype = i32
+        L.gdn_profile_read.argtypes = [i32, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
+        L.gdn_kernel_name.restype = ctypes.c_char_p
+        L.gdn_kernel_name.argtypes = [i32]
+        L.gdn_plan_segment_tokens.restype = i32
+        L.gdn_plan_segment_tokens.argtypes = [P, i32, ctypes.POINTER(i32)]
         L.gdn_step.restype = i32
         L.gdn_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         if L.gdn_abi_version() != ABI_VERSION:
@@ -105,6 +115,35 @@ def workspace_size(problem: Problem, direction=BIDIRECTIONAL) -> int:
 def set_segment_tokens(tokens: int) -> None:
     """Tokens per segment of the chunked path (0 = automatic); see gdn.h."""
     lib().gdn_set_segment_tokens(int(tokens))
+
+
+KERNELS = ("seg_map_kernel", "seg_chain_kernel", "seg_out_kernel", "recurrent_kernel")
+
+
+def profile_enable(on: bool = True) -> None:
+    """Bracket every libgdn kernel launch with HIP events (see gdn.h)."""
+    _check(lib().gdn_profile_enable(1 if on else 0))
+
+
+def profile_reset() -> None:
+    _check(lib().gdn_profile_reset())
+
+
+def profile_read() -> dict:
+    """{kernel name: (launches, total ms)} since the last reset; waits for the events."""
+    out = {}
+    for i, name in enumerate(KERNELS):
+        n, ms = ctypes.c_int64(0), ctypes.c_double(0.0)
+        _check(lib().gdn_profile_read(i, ctypes.byref(n), ctypes.byref(ms)))
+        out[name] = (n.value, ms.value)
+    return out
+
+
+def segment_plan(problem: Problem, direction=BIDIRECTIONAL) -> int:
+    """Tokens per segment the chunked path uses (0 = token-recurrent path)."""
+    n = ctypes.c_int32(0)
+    _check(lib().gdn_plan_segment_tokens(ctypes.byref(problem), DIRECTION[direction], ctypes.byref(n)))
+    return n.value
 
 
 def _torch():

@@ -23,7 +23,7 @@ BUILD = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["gdn_recurrent.hip", "gdn_chunked.hip"]
-HOST_SOURCES = ["gdn_api.cpp"]
+HOST_SOURCES = ["gdn_api.cpp", "gdn_profile.cpp"]
 
 
 def _hipcc():

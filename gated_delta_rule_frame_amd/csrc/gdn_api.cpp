@@ -134,6 +134,23 @@ const char* gdn_last_error_message(void) { return g_last_error.c_str(); }
 
 void gdn_set_segment_tokens(int32_t tokens) { gdn::set_segment_tokens(tokens); }
 
+gdn_status gdn_plan_segment_tokens(const gdn_problem* pr, int32_t direction, int32_t* tokens_out) {
+  try {
+    if (!tokens_out) return fail(GDN_ERR_INVALID_ARGUMENT, "tokens_out is NULL");
+    gdn::Problem p;
+    gdn_status s = check_problem(pr, direction, &p);
+    if (s != GDN_OK) return s;
+    Path path;
+    s = choose_path(pr, p, &path);
+    if (s != GDN_OK) return s;
+    *tokens_out = path == Path::Chunked ? gdn::chunked_segment_tokens(p, direction) : 0;
+    g_last_error.clear();
+    return GDN_OK;
+  } catch (...) {
+    return fail(GDN_ERR_INVALID_ARGUMENT, "internal error while planning");
+  }
+}
+
 gdn_status gdn_workspace_size(const gdn_problem* pr, int32_t direction, size_t* bytes_out) {
   try {
     if (!bytes_out) return fail(GDN_ERR_INVALID_ARGUMENT, "bytes_out is NULL");

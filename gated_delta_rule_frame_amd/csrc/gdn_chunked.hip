@@ -814,15 +814,22 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
   a.c = p.key_scale;
   const unsigned bhc = (unsigned)(p.B * p.H);
   if (pl.NS > 1) {
+    prof_begin(stream, GDN_KERNEL_SEG_MAP);
     hipLaunchKernelGGL((seg_map_kernel<D>), dim3(pl.NS - 1, bhc, pl.ndir), dim3(NT), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    prof_end(stream, GDN_KERNEL_SEG_MAP);
   }
+  prof_begin(stream, GDN_KERNEL_SEG_CHAIN);
   hipLaunchKernelGGL((seg_chain_kernel<D>), dim3(D / 16, bhc, pl.ndir), dim3(NTC), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  prof_end(stream, GDN_KERNEL_SEG_CHAIN);
+  prof_begin(stream, GDN_KERNEL_SEG_OUT);
   hipLaunchKernelGGL((seg_out_kernel<D>), dim3(pl.NS, bhc, 1), dim3(NT), 0, stream, a);
-  return hipGetLastError();
+  e = hipGetLastError();
+  prof_end(stream, GDN_KERNEL_SEG_OUT);
+  return e;
 }
 
 }  // namespace
@@ -854,6 +861,8 @@ hipError_t chunked_launch(const Problem& p, int direction, const Tensors& t, voi
     default: return hipErrorInvalidValue;
   }
 }
+
+int chunked_segment_tokens(const Problem& p, int direction) { return make_plan(p, direction).L; }
 
 void set_segment_tokens(int tokens) { g_segment_override.store(tokens > 0 ? tokens : 0); }
 

@@ -44,6 +44,11 @@ hipError_t chunked_launch(const Problem& p, int direction, const Tensors& t,
                           void* workspace, hipStream_t stream);
 
 void set_segment_tokens(int tokens);
+int chunked_segment_tokens(const Problem& p, int direction);
+
+// Kernel timing hooks (gdn_profile.cpp): no-ops unless profiling is enabled.
+void prof_begin(hipStream_t stream, int kernel);
+void prof_end(hipStream_t stream, int kernel);
 
 // Round-up helper for workspace carving.
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }

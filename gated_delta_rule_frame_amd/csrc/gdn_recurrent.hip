@@ -110,6 +110,7 @@ hipError_t launch_dk(const Problem& p, const Tensors& t, bool reverse, const flo
                      float* acc, bool write_state, hipStream_t stream) {
   dim3 grid(p.dv / kCols, p.H, p.B), block(64);
   float* hT = write_state ? t.hT : nullptr;
+  prof_begin(stream, GDN_KERNEL_RECURRENT);
 #define GDN_REC_CASE(D)                                                                       \
   case D:                                                                                     \
     hipLaunchKernelGGL((recurrent_kernel<BF16IN, D>), grid, block, 0, stream, t.q, t.k, t.v, \
@@ -122,7 +123,9 @@ hipError_t launch_dk(const Problem& p, const Tensors& t, bool reverse, const flo
     default: return hipErrorInvalidValue;
   }
 #undef GDN_REC_CASE
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  prof_end(stream, GDN_KERNEL_RECURRENT);
+  return e;
 }
 
 }  // namespace

@@ -147,11 +147,32 @@ gdn_status gdn_step(const gdn_problem* problem,
                     void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/* Kernel timing (diagnostics).  While enabled, every kernel launch made by
+ * libgdn is bracketed by two HIP events recorded on the call's stream;
+ * gdn_profile_read() waits for the recorded events and returns, per kernel,
+ * the number of launches and their summed duration in milliseconds since the
+ * last reset.  Process-wide; intended for one measuring thread. */
+enum {
+  GDN_KERNEL_SEG_MAP = 0,     /* chunked path: per-segment affine state maps */
+  GDN_KERNEL_SEG_CHAIN = 1,   /* chunked path: serial chain of segment maps */
+  GDN_KERNEL_SEG_OUT = 2,     /* chunked path: outputs and final state */
+  GDN_KERNEL_RECURRENT = 3,   /* token-sequential path */
+  GDN_KERNEL_COUNT = 4
+};
+gdn_status gdn_profile_enable(int32_t on);
+gdn_status gdn_profile_reset(void);
+gdn_status gdn_profile_read(int32_t kernel, int64_t* launches, double* total_ms);
+const char* gdn_kernel_name(int32_t kernel);   /* static text; "" if unknown */
+
 /* Tuning knob of the chunked path: tokens per segment (rounded up to a
  * multiple of 64; 0 restores the automatic choice).  Process-wide; results do
  * not depend on it beyond rounding, but gdn_workspace_size() does, so size
  * the workspace after setting it.  Thread-safe. */
 void gdn_set_segment_tokens(int32_t tokens);
+
+/* Tokens per segment the chunked path would use for (problem, direction), or
+ * 0 when the call would take the token-recurrent path.  Host only. */
+gdn_status gdn_plan_segment_tokens(const gdn_problem* problem, int32_t direction, int32_t* tokens_out);
 
 #ifdef __cplusplus
 }  /* extern "C" */
