@@ -34,7 +34,9 @@ def _hipcc():
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 # Packed fp32 ops are disabled in device code (the host pass warns that it does
-# not know the feature; that warning is harmless).
+# not know the feature; that warning is harmless).  (LLVM's option to force
+# MFMA accumulators into architectural VGPRs is deliberately not used: with
+# this toolchain it produced wrong results on gfx950.)
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-munsafe-fp-atomics"]
 

@@ -190,25 +190,46 @@ __device__ __forceinline__ f16x8_t fragA2(const hb* arow, int q, int g) {
 }
 __device__ __forceinline__ f16x4_t fragA1(const hb* arow, int q, int g) { return ld4(arow + 16 * q + 4 * g); }
 
-// acc[j] += A[row(lane), 0:16 n] * B_j for the wavefront's strips j < SPW with
-// st(j) < lim, B_j given as n fp16 accumulator tiles bt[j][0..n).  Each A
-// fragment is read from LDS once and used for every strip.
-template <int SPW, int NB>
-__device__ __forceinline__ void mma_regB_strips(const hb* arow, const f16x4_t (*bt)[NB], int n, int g, int wave,
-                                                int lim, f32x4* acc) {
+__device__ __forceinline__ f16x8_t tof16x8(f32x4 u, f32x4 v) { return cat8(tof16(u), tof16(v)); }
+__device__ __forceinline__ f16x4_t lo4(f16x8_t v) { return __builtin_shufflevector(v, v, 0, 1, 2, 3); }
+
+// acc[j] += A[row(lane), 0:16 n] * B_j for all SPW strips of the wavefront,
+// contracting over NP pairs of fp16 accumulator tiles bp[j][p] = (tile 2p,
+// tile 2p + 1) and, if TAIL, one more tile bt[j].  Each A fragment is read from
+// LDS once and used for every strip.  Strips past the state's width are
+// computed on clamped data and never stored: a wave with fewer real strips
+// would wait at the next barrier anyway, and branch-free code keeps the
+// accumulators in place (no merge copies).
+template <int SPW, int NP, bool TAIL>
+__device__ __forceinline__ void mma_dB(const hb* arow, const f16x8_t (*bp)[NP > 0 ? NP : 1], const f16x4_t* bt,
+                                       int g, f32x4* acc) {
 #pragma unroll
-  for (int q = 0; q < NB; q += 2) {
-    if (q + 1 < n) {
-      const f16x8_t x = fragA2(arow, q, g);
+  for (int p = 0; p < NP; ++p) {
+    const f16x8_t x = fragA2(arow, 2 * p, g);
 #pragma unroll
-      for (int j = 0; j < SPW; ++j)
-        if (wave + NW * j < lim) acc[j] = mfma32(x, cat8(bt[j][q], bt[j][q + 1]), acc[j]);
-    } else if (q < n) {
-      // K = 16 tail into a fresh accumulator, summed on the VALU (see mfma16_add)
-      const f16x4_t x = fragA1(arow, q, g);
+    for (int j = 0; j < SPW; ++j) acc[j] = mfma32(x, bp[j][p], acc[j]);
+  }
+  if constexpr (TAIL) {
+    const f16x4_t x = fragA1(arow, 2 * NP, g);
 #pragma unroll
-      for (int j = 0; j < SPW; ++j)
-        if (wave + NW * j < lim) acc[j] = mfma16_add(x, bt[j][q], acc[j]);
+    for (int j = 0; j < SPW; ++j) acc[j] = mfma16_add(x, bt[j], acc[j]);
+  }
+}
+
+// Same, contracting over the first n (1..4) token tiles held as the pairs
+// vp[j][0] = (tiles 0, 1) and vp[j][1] = (tiles 2, 3).
+template <int SPW>
+__device__ __forceinline__ void mma_tB(const hb* arow, const f16x8_t (*vp)[2], int n, int g, f32x4* acc) {
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    if (2 * p + 1 < n) {
+      const f16x8_t x = fragA2(arow, 2 * p, g);
+#pragma unroll
+      for (int j = 0; j < SPW; ++j) acc[j] = mfma32(x, vp[j][p], acc[j]);
+    } else if (2 * p < n) {
+      const f16x4_t x = fragA1(arow, 2 * p, g);
+#pragma unroll
+      for (int j = 0; j < SPW; ++j) acc[j] = mfma16_add(x, lo4(vp[j][p]), acc[j]);
     }
   }
 }
@@ -232,49 +253,86 @@ __device__ __forceinline__ long long token_of(long long t0, int n, bool rev, int
 
 // --- per-sub-chunk preparation (shared by all wavefronts) -------------------
 
-// Stage one sub-chunk (rows in scan order, zero-padded to 64) into LDS as fp16
-// and form the scan-order gate cumsum (log2 units) and beta.
+// Per-thread staging registers of one sub-chunk: a 4-token x 8-component
+// block of K, V (and Q) and one token's log-gate and beta.  Loading into
+// registers is split from writing LDS so that the next sub-chunk's global
+// loads are in flight while the current one is being computed.
+struct Stage {
+  uint4 k[4], v[4], q[4];
+  float g, b;
+};
+
+// Issue the global loads of sub-chunk [t0, t0 + n) (rows in scan order,
+// zero-padded to 64 tokens).
 template <int D, bool OUT>
-__device__ void load_subchunk(const Args& a, const Smem<D, OUT>& S, int b, int h, long long t0,
-                              int n, bool rev) {
-  using L = Lay<D, OUT>;
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void fetch_subchunk(const Args& a, int b, int h, long long t0, int n, bool rev,
+                                               Stage& st) {
   constexpr int C8 = D / 8;
-  for (int idx = tid; idx < CH * C8; idx += NT) {
-    const int i = idx / C8, c8 = idx % C8;
-    uint4 kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-    if (i < n) {
-      const size_t off = ((size_t)((size_t)b * a.T + token_of(t0, n, rev, i)) * a.H + h) * D + 8 * c8;
-      kv = bf16x8_to_f16x8(*reinterpret_cast<const uint4*>(a.k + off));
-      vv = bf16x8_to_f16x8(*reinterpret_cast<const uint4*>(a.v + off));
-      if constexpr (OUT) qv = bf16x8_to_f16x8(*reinterpret_cast<const uint4*>(a.q + off));
+  const int tid = threadIdx.x;
+  if (tid < 16 * C8) {
+    const int i4 = tid / C8, c8 = tid % C8;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 4 * i4 + r;
+      st.k[r] = st.v[r] = st.q[r] = make_uint4(0u, 0u, 0u, 0u);
+      if (i < n) {
+        const size_t off = ((size_t)((size_t)b * a.T + token_of(t0, n, rev, i)) * a.H + h) * D + 8 * c8;
+        st.k[r] = *reinterpret_cast<const uint4*>(a.k + off);
+        st.v[r] = *reinterpret_cast<const uint4*>(a.v + off);
+        if constexpr (OUT) st.q[r] = *reinterpret_cast<const uint4*>(a.q + off);
+      }
     }
-    *reinterpret_cast<uint4*>(S.kr + i * L::LDK + 8 * c8) = kv;
-    if constexpr (OUT) *reinterpret_cast<uint4*>(S.qr + i * L::LDK + 8 * c8) = qv;
-    const hb* ke = reinterpret_cast<const hb*>(&kv);
-    const hb* ve = reinterpret_cast<const hb*>(&vv);
+  }
+  st.g = 0.f;
+  st.b = 0.f;
+  if (tid < 64 && tid < n) {
+    const size_t go = ((size_t)b * a.T + token_of(t0, n, rev, tid)) * a.H + h;
+    st.g = a.g[go];
+    st.b = a.beta[go];
+  }
+}
+
+__device__ __forceinline__ uint2 pack4(hb x, hb y, hb z, hb w) {
+  return make_uint2(static_cast<uint32_t>(x) | (static_cast<uint32_t>(y) << 16),
+                    static_cast<uint32_t>(z) | (static_cast<uint32_t>(w) << 16));
+}
+
+// Write the staged sub-chunk into LDS as fp16 (K and Q row-major, K and V
+// transposed) and form the scan-order gate cumsum (log2 units) and beta.
+template <int D, bool OUT>
+__device__ __forceinline__ void stage_subchunk(const Smem<D, OUT>& S, const Stage& st) {
+  using L = Lay<D, OUT>;
+  constexpr int C8 = D / 8;
+  const int tid = threadIdx.x;
+  if (tid < 16 * C8) {
+    const int i4 = tid / C8, c8 = tid % C8;
+    uint4 kh[4], vh[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      kh[r] = bf16x8_to_f16x8(st.k[r]);
+      vh[r] = bf16x8_to_f16x8(st.v[r]);
+      *reinterpret_cast<uint4*>(S.kr + (4 * i4 + r) * L::LDK + 8 * c8) = kh[r];
+      if constexpr (OUT) *reinterpret_cast<uint4*>(S.qr + (4 * i4 + r) * L::LDK + 8 * c8) = bf16x8_to_f16x8(st.q[r]);
+    }
+    const hb* ke[4] = {reinterpret_cast<const hb*>(&kh[0]), reinterpret_cast<const hb*>(&kh[1]),
+                       reinterpret_cast<const hb*>(&kh[2]), reinterpret_cast<const hb*>(&kh[3])};
+    const hb* ve[4] = {reinterpret_cast<const hb*>(&vh[0]), reinterpret_cast<const hb*>(&vh[1]),
+                       reinterpret_cast<const hb*>(&vh[2]), reinterpret_cast<const hb*>(&vh[3])};
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      S.kt[(8 * c8 + u) * LDT + i] = ke[u];
-      S.vt[(8 * c8 + u) * LDT + i] = ve[u];
+      *reinterpret_cast<uint2*>(S.kt + (8 * c8 + u) * LDT + 4 * i4) = pack4(ke[0][u], ke[1][u], ke[2][u], ke[3][u]);
+      *reinterpret_cast<uint2*>(S.vt + (8 * c8 + u) * LDT + 4 * i4) = pack4(ve[0][u], ve[1][u], ve[2][u], ve[3][u]);
     }
   }
   if (tid < 64) {
-    const int i = tid;
-    float gi = 0.f, bi = 0.f;
-    if (i < n) {
-      const size_t go = ((size_t)b * a.T + token_of(t0, n, rev, i)) * a.H + h;
-      gi = a.g[go];
-      bi = a.beta[go];
-    }
-    float s = gi * kLog2e;
+    float s = st.g * kLog2e;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
       const float t = __shfl_up(s, d);
-      if (i >= d) s += t;
+      if (tid >= d) s += t;
     }
-    S.g2[i] = s;
-    S.bt[i] = bi;
+    S.g2[tid] = s;
+    S.bt[tid] = st.b;
   }
 }
 
@@ -387,13 +445,15 @@ __device__ void w_stage(const Smem<D, OUT>& S) {
   }
 }
 
-// Common per-sub-chunk preparation: stage, Gram, Tm, -W.
+// Common per-sub-chunk preparation: write the staged sub-chunk to LDS, start
+// fetching the next one (if any), then Gram, Tm and -W.
 template <int D, bool OUT>
-__device__ __forceinline__ void prepare(const Args& a, const Smem<D, OUT>& S, int b, int h, long long t0,
-                                        int n, bool rev) {
+__device__ __forceinline__ void prepare(const Args& a, const Smem<D, OUT>& S, Stage& st, int b, int h,
+                                        bool has_next, long long t0n, int nn, bool rev) {
   const int wave = wave_id();
   __syncthreads();
-  load_subchunk<D, OUT>(a, S, b, h, t0, n, rev);
+  stage_subchunk<D, OUT>(S, st);
+  if (has_next) fetch_subchunk<D, OUT>(a, b, h, t0n, nn, rev, st);
   __syncthreads();
   gram_stage<D, OUT>(a, S);
   __syncthreads();
@@ -404,18 +464,15 @@ __device__ __forceinline__ void prepare(const Args& a, const Smem<D, OUT>& S, in
   w_stage<D, OUT>(S);
 }
 
-// Per-lane row factors of a sub-chunk: exp(G_i) (eg) and c exp(G_n - G_i) (sc)
-// for the four rows 4g + r of each token tile mt.
-__device__ __forceinline__ void row_factors(const float* g2, float c, int g, f32x4* eg, f32x4* sc) {
-  const float glast = g2[CH - 1];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float gi = g2[mt * 16 + 4 * g + r];
-      eg[mt][r] = exp2f(gi);
-      sc[mt][r] = c * exp2f(glast - gi);
-    }
+// Per-lane row factors of token tile mt (rows 16 mt + 4 g + r):
+// exp(G_i) and c exp(G_n - G_i).
+__device__ __forceinline__ f32x4 row_decay(const float* g2, int mt, int g) {
+  const float4 v = *reinterpret_cast<const float4*>(g2 + mt * 16 + 4 * g);
+  return f32x4{exp2f(v.x), exp2f(v.y), exp2f(v.z), exp2f(v.w)};
+}
+__device__ __forceinline__ f32x4 row_scale(const float* g2, float glast, float c, int mt, int g) {
+  const float4 v = *reinterpret_cast<const float4*>(g2 + mt * 16 + 4 * g);
+  return f32x4{c * exp2f(glast - v.x), c * exp2f(glast - v.y), c * exp2f(glast - v.z), c * exp2f(glast - v.w)};
 }
 
 // ---------------------------------------------------------------------------
@@ -440,48 +497,75 @@ __global__ __launch_bounds__(NT) void seg_map_kernel(Args a) {
   for (int i = threadIdx.x; i < 4 * CH * LDT / 2; i += NT) reinterpret_cast<uint32_t*>(S.ab)[i] = 0u;
 
   f32x4 X[SPW][MD];
-  f16x4_t Xh[SPW][MD];
 #pragma unroll
   for (int j = 0; j < SPW; ++j) {
     const int st = wave + NW * j;
 #pragma unroll
-    for (int md = 0; md < MD; ++md) {
+    for (int md = 0; md < MD; ++md)
 #pragma unroll
       for (int r = 0; r < 4; ++r) X[j][md][r] = (st == md && 4 * g + r == cl) ? 1.f : 0.f;
-      Xh[j][md] = tof16(X[j][md]);
-    }
   }
 
-  for (int jj = 0; jj < nsub; ++jj) {
+  // sub-chunk jj of the scan: its first original token and size
+  auto piece = [&](int jj, long long& t0, int& n) {
     const int jc = rev ? nsub - 1 - jj : jj;
-    const long long t0 = s0 + (long long)jc * CH;
-    const int n = (int)((s1 - t0) < CH ? (s1 - t0) : CH);
-    prepare<D, false>(a, S, b, h, t0, n, rev);
+    t0 = s0 + (long long)jc * CH;
+    n = (int)((s1 - t0) < CH ? (s1 - t0) : CH);
+  };
+  Stage st;
+  {
+    long long t0;
+    int n;
+    piece(0, t0, n);
+    fetch_subchunk<D, false>(a, b, h, t0, n, rev, st);
+  }
+  for (int jj = 0; jj < nsub; ++jj) {
+    long long t0, t0n = 0;
+    int n, nn = 0;
+    piece(jj, t0, n);
+    if (jj + 1 < nsub) piece(jj + 1, t0n, nn);
+    prepare<D, false>(a, S, st, b, h, jj + 1 < nsub, t0n, nn, rev);
     // U strips (values part only)
     f32x4 V[SPW][4];
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
       const int st = wave + NW * j;
+      const int vs = st < MD ? 0 : (st < NS_ ? st - MD : MD - 1);   // value strip (clamped)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        V[j][mt] = (st >= MD && st < NS_)
-                       ? mma_lds(S.t1 + (mt * 16 + cl) * LDT, S.vt + ((st - MD) * 16 + cl) * LDT, mt + 1, g, zero4())
-                       : zero4();
+      for (int mt = 0; mt < 4; ++mt) {
+        const f32x4 u = mma_lds(S.t1 + (mt * 16 + cl) * LDT, S.vt + (vs * 16 + cl) * LDT, mt + 1, g, zero4());
+        V[j][mt] = st >= MD ? u : zero4();          // the P part has no values
+      }
     }
     __syncthreads();
-    f32x4 eg[4], sc[4];
-    row_factors(S.g2, a.c, g, eg, sc);
-    const float dec = exp2f(S.g2[CH - 1]);
+    const float glast = S.g2[CH - 1];
+    const float dec = exp2f(glast);
+    // fp16 copy of the state as MFMA B pairs (rows = d)
+    f16x8_t Xp[SPW][MD / 2 > 0 ? MD / 2 : 1];
+    f16x4_t Xq[SPW];
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+#pragma unroll
+      for (int p = 0; p < MD / 2; ++p) Xp[j][p] = tof16x8(X[j][2 * p], X[j][2 * p + 1]);
+      if constexpr (MD & 1) Xq[j] = tof16(X[j][MD - 1]);
+    }
     // V'aug = [0 | U] - W X   (per token tile mt, all strips at once)
-    f16x4_t Vs[SPW][4];
+    f32x4 Vf[SPW][4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       f32x4 acc[SPW];
 #pragma unroll
       for (int j = 0; j < SPW; ++j) acc[j] = V[j][mt];
-      mma_regB_strips<SPW, MD>(S.kr + (mt * 16 + cl) * L::LDK, Xh, MD, g, wave, NS_, acc);
+      mma_dB<SPW, MD / 2, (MD & 1) != 0>(S.kr + (mt * 16 + cl) * L::LDK, Xp, Xq, g, acc);
+      const f32x4 sc = row_scale(S.g2, glast, a.c, mt, g);
 #pragma unroll
-      for (int j = 0; j < SPW; ++j) Vs[j][mt] = tof16(acc[j] * sc[mt]);
+      for (int j = 0; j < SPW; ++j) Vf[j][mt] = acc[j] * sc;
+    }
+    f16x8_t Vs[SPW][2];
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      Vs[j][0] = tof16x8(Vf[j][0], Vf[j][1]);
+      Vs[j][1] = tof16x8(Vf[j][2], Vf[j][3]);
     }
     // X <- e^{G_n} X + c K^T diag(e^{G_n - G}) V'aug
 #pragma unroll
@@ -489,12 +573,9 @@ __global__ __launch_bounds__(NT) void seg_map_kernel(Args a) {
       f32x4 acc[SPW];
 #pragma unroll
       for (int j = 0; j < SPW; ++j) acc[j] = X[j][md] * dec;
-      mma_regB_strips<SPW, 4>(S.kt + (md * 16 + cl) * LDT, Vs, 4, g, wave, NS_, acc);
+      mma_tB<SPW>(S.kt + (md * 16 + cl) * LDT, Vs, 4, g, acc);
 #pragma unroll
-      for (int j = 0; j < SPW; ++j) {
-        X[j][md] = acc[j];
-        Xh[j][md] = tof16(acc[j]);
-      }
+      for (int j = 0; j < SPW; ++j) X[j][md] = acc[j];
     }
   }
   // store X = [P | Q] (fp32, row-major [D][2D])
@@ -651,75 +732,102 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(Args a) {
     const int pos = rev ? a.NS - 1 - seg : seg;
     const float* stp = a.starts + ((((size_t)slot * a.B + b) * a.H + h) * a.NS + pos) * (size_t)D * D;
     f32x4 H[SPW][MD];
-    f16x4_t Hh[SPW][MD];
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
       const int st = wave + NW * j;
 #pragma unroll
-      for (int md = 0; md < MD; ++md) {
+      for (int md = 0; md < MD; ++md)
 #pragma unroll
         for (int r = 0; r < 4; ++r) H[j][md][r] = (st < MD) ? stp[(size_t)(md * 16 + 4 * g + r) * D + st * 16 + cl] : 0.f;
-        Hh[j][md] = tof16(H[j][md]);
-      }
+    }
+    auto piece = [&](int jj, long long& t0, int& n) {
+      const int jc = rev ? nsub - 1 - jj : jj;
+      t0 = s0 + (long long)jc * CH;
+      n = (int)((s1 - t0) < CH ? (s1 - t0) : CH);
+    };
+    Stage st;
+    {
+      long long t0;
+      int n;
+      piece(0, t0, n);
+      fetch_subchunk<D, true>(a, b, h, t0, n, rev, st);
     }
     for (int jj = 0; jj < nsub; ++jj) {
-      const int jc = rev ? nsub - 1 - jj : jj;
-      const long long t0 = s0 + (long long)jc * CH;
-      const int n = (int)((s1 - t0) < CH ? (s1 - t0) : CH);
-      prepare<D, true>(a, S, b, h, t0, n, rev);
+      long long t0, t0n = 0;
+      int n, nn = 0;
+      piece(jj, t0, n);
+      if (jj + 1 < nsub) piece(jj + 1, t0n, nn);
+      prepare<D, true>(a, S, st, b, h, jj + 1 < nsub, t0n, nn, rev);
       f32x4 V[SPW][4];
 #pragma unroll
       for (int j = 0; j < SPW; ++j) {
         const int st = wave + NW * j;
+        const int vs = st < MD ? st : MD - 1;      // clamped strip
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
-          V[j][mt] = (st < MD) ? mma_lds(S.t1 + (mt * 16 + cl) * LDT, S.vt + (st * 16 + cl) * LDT, mt + 1, g, zero4())
-                               : zero4();
+          V[j][mt] = mma_lds(S.t1 + (mt * 16 + cl) * LDT, S.vt + (vs * 16 + cl) * LDT, mt + 1, g, zero4());
       }
       __syncthreads();
-      f32x4 eg[4], sc[4];
-      row_factors(S.g2, a.c, g, eg, sc);
-      const float dec = exp2f(S.g2[CH - 1]);
+      const float glast = S.g2[CH - 1];
+      const float dec = exp2f(glast);
+      f16x8_t Hp[SPW][MD / 2 > 0 ? MD / 2 : 1];
+      f16x4_t Hq[SPW];
+#pragma unroll
+      for (int j = 0; j < SPW; ++j) {
+#pragma unroll
+        for (int p = 0; p < MD / 2; ++p) Hp[j][p] = tof16x8(H[j][2 * p], H[j][2 * p + 1]);
+        if constexpr (MD & 1) Hq[j] = tof16(H[j][MD - 1]);
+      }
       // V' = U - W H
-      f16x4_t Vh[SPW][4], Vs[SPW][4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         f32x4 acc[SPW];
 #pragma unroll
         for (int j = 0; j < SPW; ++j) acc[j] = V[j][mt];
-        mma_regB_strips<SPW, MD>(S.kr + (mt * 16 + cl) * L::LDK, Hh, MD, g, wave, MD, acc);
+        mma_dB<SPW, MD / 2, (MD & 1) != 0>(S.kr + (mt * 16 + cl) * L::LDK, Hp, Hq, g, acc);
 #pragma unroll
-        for (int j = 0; j < SPW; ++j) {
-          Vh[j][mt] = tof16(acc[j]);
-          Vs[j][mt] = tof16(acc[j] * sc[mt]);
-        }
+        for (int j = 0; j < SPW; ++j) V[j][mt] = acc[j];
+      }
+      f16x8_t Vh[SPW][2], Vs[SPW][2];
+#pragma unroll
+      for (int j = 0; j < SPW; ++j) {
+        Vh[j][0] = tof16x8(V[j][0], V[j][1]);
+        Vh[j][1] = tof16x8(V[j][2], V[j][3]);
+        const f32x4 s0 = row_scale(S.g2, glast, a.c, 0, g), s1 = row_scale(S.g2, glast, a.c, 1, g);
+        const f32x4 s2 = row_scale(S.g2, glast, a.c, 2, g), s3 = row_scale(S.g2, glast, a.c, 3, g);
+        Vs[j][0] = tof16x8(V[j][0] * s0, V[j][1] * s1);
+        Vs[j][1] = tof16x8(V[j][2] * s2, V[j][3] * s3);
       }
       // O = diag(e^G) Q H + P V'
+      const long long tstride = rev ? -(long long)a.H * D : (long long)a.H * D;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         f32x4 acc[SPW];
 #pragma unroll
         for (int j = 0; j < SPW; ++j) acc[j] = zero4();
-        mma_regB_strips<SPW, MD>(S.qr + (mt * 16 + cl) * L::LDK, Hh, MD, g, wave, MD, acc);
+        mma_dB<SPW, MD / 2, (MD & 1) != 0>(S.qr + (mt * 16 + cl) * L::LDK, Hp, Hq, g, acc);
+        const f32x4 eg = row_decay(S.g2, mt, g);
 #pragma unroll
-        for (int j = 0; j < SPW; ++j) acc[j] = acc[j] * eg[mt];
-        mma_regB_strips<SPW, 4>(S.p + (mt * 16 + cl) * LDT, Vh, mt + 1, g, wave, MD, acc);
+        for (int j = 0; j < SPW; ++j) acc[j] = acc[j] * eg;
+        mma_tB<SPW>(S.p + (mt * 16 + cl) * LDT, Vh, mt + 1, g, acc);
+        const int i0 = mt * 16 + 4 * g;                       // scan-local row of r = 0
+        const size_t e0 = ((size_t)b * a.T + token_of(t0, n, rev, i0)) * a.H * D + (size_t)h * D;
 #pragma unroll
         for (int j = 0; j < SPW; ++j) {
           const int st = wave + NW * j;
           if (st < MD) {
-            const int col = st * 16 + cl;
+            const size_t base = e0 + st * 16 + cl;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const int i = mt * 16 + 4 * g + r;
-              if (i < n) {
-                const size_t off = ((size_t)((size_t)b * a.T + token_of(t0, n, rev, i)) * a.H + h) * D + col;
+              if (i0 + r < n) {
+                const size_t off = base + r * tstride;
                 float val = acc[j][r];
                 if (mode == 1) {
                   a.acc[off] = val;
                 } else {
                   if (mode == 2) val += a.acc[off];
-                  store_scalar(a.out, off, val, a.out_bf16 != 0);
+                  if (a.out_bf16) static_cast<uint16_t*>(a.out)[off] = f32_to_bf16_bits(val);
+                  else static_cast<float*>(a.out)[off] = val;
                 }
               }
             }
@@ -732,12 +840,9 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(Args a) {
         f32x4 acc[SPW];
 #pragma unroll
         for (int j = 0; j < SPW; ++j) acc[j] = H[j][md] * dec;
-        mma_regB_strips<SPW, 4>(S.kt + (md * 16 + cl) * LDT, Vs, 4, g, wave, MD, acc);
+        mma_tB<SPW>(S.kt + (md * 16 + cl) * LDT, Vs, 4, g, acc);
 #pragma unroll
-        for (int j = 0; j < SPW; ++j) {
-          H[j][md] = acc[j];
-          Hh[j][md] = tof16(acc[j]);
-        }
+        for (int j = 0; j < SPW; ++j) H[j][md] = acc[j];
       }
     }
     // final state: the scan's last segment
