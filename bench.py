@@ -125,6 +125,8 @@ def main():
     ap.add_argument("--segment", type=int, default=0, help="tokens per segment (0 = automatic)")
     ap.add_argument("--parity-head", type=int, default=7)
     ap.add_argument("--no-parity", action="store_true", help="skip the oracle check and CPU baseline")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="after timing, run one device-to-device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -203,6 +205,16 @@ def main():
     G.profile_enable(False)
     ms = ev0.elapsed_time(ev1) / args.steps
     prof = G.profile_read()
+
+    if args.copy_bytes > 0:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE under rocprofv3
+        # calibrate the byte counters read for the layer's kernels
+        src = torch.empty(args.copy_bytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     tokens_per_s = B * T / (ms / 1e3)
     ndir = 2 if direction == "bidir" else 1
