@@ -11,10 +11,12 @@
 // <= 0 on the documented domain), keys scaled by c = key_scale:
 //     A   = strict_lower(c^2 diag(beta) K K^T * E)                     (64x64)
 //     Tm  = (I + A)^-1                       (blocked triangular inverse)
-//     W   = c Tm diag(beta e^G) K,   U = Tm diag(beta) V              (WY/UT form)
-//     V'  = U - W H                          (values minus the state's prediction)
+//     R   = V - c diag(e^G) K H              (values minus the decayed prediction)
+//     V'  = Tm diag(beta) R                  (the per-token corrections)
 //     O   = diag(e^G) Q H + (c tril(Q K^T) * E) V'       (read after write)
 //     H  <- e^{G_n} H + c K^T diag(e^{G_n - G}) V'
+// (V' equals the WY/UT form U - W H with U = Tm diag(beta) V and
+// W = c Tm diag(beta e^G) K; the R form needs neither W nor U.)
 //
 // Schedule.  The token axis is cut, in original order, into segments of L
 // tokens (a multiple of 64) and each segment into 64-token sub-chunks; a scan
@@ -28,12 +30,22 @@
 //   3. seg_out_kernel   (parallel over segments): each segment re-run from its
 //      true start state, writing outputs (both scan directions of a segment in
 //      one workgroup, summed before the single store) and the final state.
-// All states and accumulations are fp32.  MFMA operands of the chunk kernels
-// are fp16: the bf16 inputs convert to fp16 exactly (in fp16's normal range)
-// and each rounded intermediate (Tm, W, H, V', P) keeps 11 significant bits
-// instead of bf16's 8, which holds the result well inside the bf16-input
-// tolerance at no extra MFMA work.  Precondition of this path: inputs and
-// intermediate magnitudes stay below fp16's maximum (65504).
+//
+// Workgroups of the map and output kernels: one wavefront per 16-column strip
+// of the state ("strip waves", the state strip lives in its registers) plus
+// one helper wavefront.  Per sub-chunk c there are two phases:
+//   alpha: every wave writes its share of sub-chunk c+1 into the other LDS
+//          buffer and starts the global loads of c+2; the helper inverts
+//          I + A_c; the strip waves form Q H and K H and R.
+//   beta:  the strip waves form V', the outputs and the new state; all waves
+//          compute the Gram tiles (A and P) of sub-chunk c+1.
+// so the triangular inverse, which is serial, overlaps the state products.
+// All states and accumulations are fp32.  MFMA operands are fp16: the bf16
+// inputs convert to fp16 exactly (in fp16's normal range) and each rounded
+// intermediate (Tm, H, R, V', P) keeps 11 significant bits.  Precondition of
+// this path: inputs and intermediate magnitudes stay below fp16's maximum
+// (65504).  Every MFMA here is the 16x16x32 f16 form except the 16x16 block
+// products of the inverse, which start from a zero accumulator.
 #include "gdn_common.h"
 #include "gdn_internal.h"
 #include "gdn_mfma.h"
@@ -44,16 +56,13 @@ namespace gdn {
 namespace {
 
 constexpr int CH = 64;          // sub-chunk tokens
-constexpr int NT = 256;         // threads per workgroup of the map and output kernels
-constexpr int NW = NT / 64;     // wavefronts per workgroup
+constexpr int LDT = CH + 8;     // row stride (elements) of token-contracted fp16 matrices
+constexpr int LDD = 24;         // row stride of the diagonal inverse blocks
 constexpr int NTC = 256;        // threads per workgroup of the chain kernel
 constexpr int NWC = NTC / 64;
-constexpr int LDT = CH + 8;     // row stride (elements) of token-contracted fp16 matrices
-constexpr int LDA = CH + 4;     // row stride of the fp32 A matrix
 constexpr float kLog2e = 1.4426950408889634f;
 
 std::atomic<int> g_segment_override{0};
-
 
 struct Args {
   const bh* q;
@@ -84,60 +93,94 @@ __device__ __forceinline__ int dir_of_slot(int dirs, int slot) {
 }
 __device__ __forceinline__ int slot_of_dir(int dirs, int dir) { return (dir == 1 && (dirs & 1)) ? 1 : 0; }
 
-// Shared-memory layout of a workgroup.  OUT: the output pass (else the map
-// pass).  Only operands shared by all wavefronts live here; each wavefront's
-// state strips, U, V' and outputs stay in registers.
+// Workgroup geometry for state width D.
+template <int D>
+struct Geo {
+  static constexpr int MD = D / 16;              // 16-wide tiles along d
+  static constexpr int NSW = MD;                 // strip wavefronts
+  static constexpr int HW = NSW;                 // index of the helper wavefront
+  static constexpr int NT = 64 * (NSW + 1);      // threads per workgroup
+  static constexpr int DP = (D + 31) / 32 * 32;  // d padded to whole K = 32 steps
+  static constexpr int NP = DP / 32;
+  static constexpr int LDK = DP + 8;             // row stride of d-contracted fp16 rows
+};
+
+// Shared memory.  Two sub-chunk buffers (Q and K rows, K^T, P, gate factors)
+// alternate between "being computed on" and "being staged"; the inverse and
+// the A matrix are single-buffered (their producer and consumer phases are
+// separated by a barrier).  OUT: output pass (else map pass: no Q, no P).
 template <int D, bool OUT>
 struct Lay {
-  static constexpr int LDK = D + 8;    // row stride of d-contracted matrices
-  static constexpr int KR = CH * LDK * 2;
-  static constexpr int QR = OUT ? CH * LDK * 2 : 0;
+  using G = Geo<D>;
+  static constexpr int QR = OUT ? CH * G::LDK * 2 : 0;
+  static constexpr int KR = CH * G::LDK * 2;
   static constexpr int KT = D * LDT * 2;
-  static constexpr int VT = D * LDT * 2;
-  static constexpr int AF = CH * LDA * 4;
-  static constexpr int SQ = CH * LDT * 2;
-  static constexpr int NSQ = OUT ? 5 : 4;
-  static constexpr int o_kr = 0;
-  static constexpr int o_qr = o_kr + KR;
-  static constexpr int o_kt = o_qr + QR;
-  static constexpr int o_vt = o_kt + KT;
-  static constexpr int o_af = o_vt + VT;
-  static constexpr int o_sq = o_af + AF;
-  static constexpr int o_g2 = o_sq + NSQ * SQ;
-  static constexpr int o_bt = o_g2 + CH * 4;
-  static constexpr int BYTES = o_bt + CH * 4;
+  static constexpr int PP = OUT ? CH * LDT * 2 : 0;
+  static constexpr int GT = 5 * CH * 4;
+  static constexpr int o_qr = 0;
+  static constexpr int o_kr = o_qr + QR;
+  static constexpr int o_kt = o_kr + KR;
+  static constexpr int o_pp = o_kt + KT;
+  static constexpr int o_gt = o_pp + PP;
+  static constexpr int BUF = o_gt + GT;
+  static constexpr int o_tt = 2 * BUF;                 // Tm diag(beta), fp16 rows
+  static constexpr int o_ao = o_tt + CH * LDT * 2;     // off-diagonal blocks of A, fp16 rows
+  static constexpr int o_td = o_ao + CH * LDT * 2;     // diagonal blocks of Tm, fp16 rows
+  static constexpr int o_ad = o_td + CH * LDD * 2;     // diagonal blocks of A, fp32
+  static constexpr int BYTES = o_ad + 4 * 16 * 16 * 4;
   static_assert(BYTES <= 160 * 1024, "workgroup LDS budget exceeded");
-  static_assert(KR % 16 == 0 && KT % 16 == 0 && AF % 16 == 0 && SQ % 16 == 0, "alignment");
+  static_assert(QR % 16 == 0 && KR % 16 == 0 && KT % 16 == 0 && PP % 16 == 0 && BUF % 16 == 0, "alignment");
+};
+
+// One sub-chunk buffer.
+struct Buf {
+  hb *qr, *kr, *kt, *pp;
+  float *g2, *eg, *ce, *dn, *bt;   // cumsum (log2), e^G, c e^G, c e^{G_n - G}, beta
+};
+
+// An LDS base address the compiler must treat as computed here: every LDS
+// address of the loop body is then this base plus an immediate offset, instead
+// of one loop-invariant address register per array and lane pattern (which the
+// compiler would otherwise hoist and keep live for the whole kernel).
+__device__ __forceinline__ char* lds_at(char* smem, uint32_t off) {
+  asm volatile("" : "+v"(off));
+  return smem + off;
+}
+
+template <int D, bool OUT>
+__device__ __forceinline__ Buf buf_at(char* s, int i) {
+  using L = Lay<D, OUT>;
+  char* p = lds_at(s, (uint32_t)(i * L::BUF));
+  Buf b;
+  b.qr = reinterpret_cast<hb*>(p + L::o_qr);
+  b.kr = reinterpret_cast<hb*>(p + L::o_kr);
+  b.kt = reinterpret_cast<hb*>(p + L::o_kt);
+  b.pp = reinterpret_cast<hb*>(p + L::o_pp);
+  float* gt = reinterpret_cast<float*>(p + L::o_gt);
+  b.g2 = gt;
+  b.eg = gt + CH;
+  b.ce = gt + 2 * CH;
+  b.dn = gt + 3 * CH;
+  b.bt = gt + 4 * CH;
+  return b;
+}
+
+// Single-buffered arrays of the inverse.
+struct Inv {
+  hb *tt, *ao, *td;
+  float* ad;
 };
 
 template <int D, bool OUT>
-struct Smem {
+__device__ __forceinline__ Inv inv_at(char* s0) {
   using L = Lay<D, OUT>;
-  hb *kr, *qr, *kt, *vt, *p, *ab, *tbt, *t1, *t2;
-  float *af, *g2, *bt;
-  __device__ explicit Smem(char* s) {
-    kr = reinterpret_cast<hb*>(s + L::o_kr);
-    qr = reinterpret_cast<hb*>(s + L::o_qr);
-    kt = reinterpret_cast<hb*>(s + L::o_kt);
-    vt = reinterpret_cast<hb*>(s + L::o_vt);
-    af = reinterpret_cast<float*>(s + L::o_af);
-    hb* sq = reinterpret_cast<hb*>(s + L::o_sq);
-    ab = sq;
-    tbt = sq + CH * LDT;
-    t1 = sq + 2 * CH * LDT;
-    t2 = sq + 3 * CH * LDT;
-    p = OUT ? sq + 4 * CH * LDT : nullptr;
-    g2 = reinterpret_cast<float*>(s + L::o_g2);
-    bt = reinterpret_cast<float*>(s + L::o_bt);
-  }
-};
-
-// Lower-triangular 16x16-tile pairs (a <= b) of a 4x4 tile grid.
-__device__ __forceinline__ void tri_pair(int t, int& a, int& b) {
-  constexpr int A[10] = {0, 0, 0, 0, 1, 1, 1, 2, 2, 3};
-  constexpr int B[10] = {0, 1, 2, 3, 1, 2, 3, 2, 3, 3};
-  a = A[t];
-  b = B[t];
+  char* s = lds_at(s0, 0u);
+  Inv v;
+  v.tt = reinterpret_cast<hb*>(s + L::o_tt);
+  v.ao = reinterpret_cast<hb*>(s + L::o_ao);
+  v.td = reinterpret_cast<hb*>(s + L::o_td);
+  v.ad = reinterpret_cast<float*>(s + L::o_ad);
+  return v;
 }
 
 __device__ __forceinline__ void store4_h(hb* dst, float a, float b, float c, float d) {
@@ -147,7 +190,7 @@ __device__ __forceinline__ void store4_h(hb* dst, float a, float b, float c, flo
   *reinterpret_cast<uint2*>(dst) = u;
 }
 
-// --- register-operand MFMA helpers -----------------------------------------
+// --- MFMA helpers -------------------------------------------------------------
 // A 16x16 accumulator tile X (lane l: X[4(l/16) + r][l % 16]) converted to
 // fp16 is directly the B operand of a 16x16x16 product contracting over X's
 // rows.  Two such tiles (rows 0-15 and 16-31 of the contraction) form the B
@@ -167,128 +210,96 @@ __device__ __forceinline__ f16x4_t tof16(f32x4 v) {
   h[3] = static_cast<_Float16>(v[3]);
   return h;
 }
+__device__ __forceinline__ f16x4_t zero_h4() { return f16x4_t{0, 0, 0, 0}; }
 __device__ __forceinline__ f32x4 mfma32(f16x8_t x, f16x8_t y, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(x, y, c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4 mfma16(f16x4_t x, f16x4_t y, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16f16(x, y, c, 0, 0, 0);
+__device__ __forceinline__ f32x4 mfma16(f16x4_t x, f16x4_t y) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(x, y, zero4(), 0, 0, 0);
 }
 
-// acc + x * y for a K = 16 step.  With this toolchain a dependent accumulator
-// chain that mixes the 16x16x32 and 16x16x16 MFMA shapes produces wrong sums
-// (measured on gfx950: large errors on a fraction of the elements), while each
-// shape alone and independent accumulators are exact.  So a K = 16 step always
-// starts a fresh accumulator and is added on the VALU; every accumulator chain
-// uses one MFMA shape only.
-__device__ __forceinline__ f32x4 mfma16_add(f16x4_t x, f16x4_t y, f32x4 acc) {
-  return acc + mfma16(x, y, zero4());
-}
-
-// A fragment of k tiles (q, q + 1) in the register-B order, or of tile q alone.
+// A fragment of k tiles (q, q + 1) in the register-B order.
 __device__ __forceinline__ f16x8_t fragA2(const hb* arow, int q, int g) {
   return cat8(ld4(arow + 16 * q + 4 * g), ld4(arow + 16 * q + 16 + 4 * g));
 }
-__device__ __forceinline__ f16x4_t fragA1(const hb* arow, int q, int g) { return ld4(arow + 16 * q + 4 * g); }
-
 __device__ __forceinline__ f16x8_t tof16x8(f32x4 u, f32x4 v) { return cat8(tof16(u), tof16(v)); }
-__device__ __forceinline__ f16x4_t lo4(f16x8_t v) { return __builtin_shufflevector(v, v, 0, 1, 2, 3); }
-
-// acc[j] += A[row(lane), 0:16 n] * B_j for all SPW strips of the wavefront,
-// contracting over NP pairs of fp16 accumulator tiles bp[j][p] = (tile 2p,
-// tile 2p + 1) and, if TAIL, one more tile bt[j].  Each A fragment is read from
-// LDS once and used for every strip.  Strips past the state's width are
-// computed on clamped data and never stored: a wave with fewer real strips
-// would wait at the next barrier anyway, and branch-free code keeps the
-// accumulators in place (no merge copies).
-template <int SPW, int NP, bool TAIL>
-__device__ __forceinline__ void mma_dB(const hb* arow, const f16x8_t (*bp)[NP > 0 ? NP : 1], const f16x4_t* bt,
-                                       int g, f32x4* acc) {
-#pragma unroll
-  for (int p = 0; p < NP; ++p) {
-    const f16x8_t x = fragA2(arow, 2 * p, g);
-#pragma unroll
-    for (int j = 0; j < SPW; ++j) acc[j] = mfma32(x, bp[j][p], acc[j]);
-  }
-  if constexpr (TAIL) {
-    const f16x4_t x = fragA1(arow, 2 * NP, g);
-#pragma unroll
-    for (int j = 0; j < SPW; ++j) acc[j] = mfma16_add(x, bt[j], acc[j]);
-  }
+__device__ __forceinline__ f32x4 ld4f(const float* p) {
+  const float4 v = *reinterpret_cast<const float4*>(p);
+  return f32x4{v.x, v.y, v.z, v.w};
 }
 
-// Same, contracting over the first n (1..4) token tiles held as the pairs
-// vp[j][0] = (tiles 0, 1) and vp[j][1] = (tiles 2, 3).
-template <int SPW>
-__device__ __forceinline__ void mma_tB(const hb* arow, const f16x8_t (*vp)[2], int n, int g, f32x4* acc) {
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    if (2 * p + 1 < n) {
-      const f16x8_t x = fragA2(arow, 2 * p, g);
-#pragma unroll
-      for (int j = 0; j < SPW; ++j) acc[j] = mfma32(x, vp[j][p], acc[j]);
-    } else if (2 * p < n) {
-      const f16x4_t x = fragA1(arow, 2 * p, g);
-#pragma unroll
-      for (int j = 0; j < SPW; ++j) acc[j] = mfma16_add(x, lo4(vp[j][p]), acc[j]);
-    }
-  }
+// Rows of one sub-chunk [t0, t0 + n) in scan order: scan row i is token
+// ta + sgn i.  Element offsets are formed as a wave-uniform part (row base and
+// the row's uniform step) plus one small per-lane offset, so that no per-row
+// 64-bit offsets stay live across the sub-chunk loop.
+struct Sub {
+  long long ta;   // token of scan row 0
+  int sgn;        // +1: forward scan, -1: reversed scan
+  int n;          // rows present
+};
+
+__device__ __forceinline__ Sub make_sub(long long t0, int n, bool rev) {
+  Sub s;
+  s.ta = rev ? t0 + n - 1 : t0;
+  s.sgn = rev ? -1 : 1;
+  s.n = n;
+  return s;
 }
 
-// acc += A[row(lane), 0:16 n] * B[col(lane), 0:16 n]^T with both rows in LDS.
-__device__ __forceinline__ f32x4 mma_lds(const hb* arow, const hb* brow, int n, int g, f32x4 acc) {
-#pragma unroll
-  for (int q = 0; q < 8; q += 2) {
-    if (q + 1 < n)
-      acc = mfma32(ld8(arow + 16 * q + 8 * g), ld8(brow + 16 * q + 8 * g), acc);
-    else if (q < n)
-      acc = mfma16_add(ld4(arow + 16 * q + 4 * g), ld4(brow + 16 * q + 4 * g), acc);
-  }
-  return acc;
+// exp2 of a non-positive argument (results below 2^-126 flush to zero).
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Raw buffer access to a small fp32 block (a state): one per-lane byte offset
+// plus a wave-uniform one, so that a state's 4 MD addresses per lane are not
+// materialised as separate 64-bit pointers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const float* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ float block_load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+__device__ __forceinline__ void block_store(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, float x) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, voff, soff, 0);
 }
 
-// Global token index of scan-local row i of a sub-chunk [t0, t0 + n).
-__device__ __forceinline__ long long token_of(long long t0, int n, bool rev, int i) {
-  return rev ? t0 + n - 1 - i : t0 + i;
-}
-
-// --- per-sub-chunk preparation (shared by all wavefronts) -------------------
-
-// Per-thread staging registers of one sub-chunk: a 4-token x 8-component
-// block of K, V (and Q) and one token's log-gate and beta.  Loading into
-// registers is split from writing LDS so that the next sub-chunk's global
-// loads are in flight while the current one is being computed.
+// --- staging --------------------------------------------------------------------
+// Strip-wave thread j < 2D holds a 4-token x 8-component block of K (token
+// group j % 16, components 8 (j / 16) ..), thread 2D + j the same block of Q
+// (output pass); the helper wave holds one token's log-gate and beta per lane.
+// Loading into registers is split from writing LDS so that the loads of
+// sub-chunk c+2 are in flight while sub-chunk c is computed.
 struct Stage {
-  uint4 k[4], v[4], q[4];
+  uint4 x[4];
   float g, b;
 };
 
-// Issue the global loads of sub-chunk [t0, t0 + n) (rows in scan order,
-// zero-padded to 64 tokens).
 template <int D, bool OUT>
-__device__ __forceinline__ void fetch_subchunk(const Args& a, int b, int h, long long t0, int n, bool rev,
-                                               Stage& st) {
-  constexpr int C8 = D / 8;
+__device__ __forceinline__ void fetch_subchunk(const Args& a, int b, int h, const Sub& sb, Stage& st) {
+  using G = Geo<D>;
   const int tid = threadIdx.x;
-  if (tid < 16 * C8) {
-    const int i4 = tid / C8, c8 = tid % C8;
+  const long long HD = (long long)a.H * D;
+  if (wave_id() < G::NSW) {
+    const bool isq = tid >= 2 * D;
+    if (OUT || !isq) {
+      const int kb = isq ? tid - 2 * D : tid;
+      const int i4 = kb & 15, c8 = kb >> 4;
+      const bh* src = (isq ? a.q : a.k) + ((long long)b * a.T + sb.ta) * HD + (long long)h * D;
+      const int lo = sb.sgn * 4 * i4 * (int)HD + 8 * c8;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 4 * i4 + r;
-      st.k[r] = st.v[r] = st.q[r] = make_uint4(0u, 0u, 0u, 0u);
-      if (i < n) {
-        const size_t off = ((size_t)((size_t)b * a.T + token_of(t0, n, rev, i)) * a.H + h) * D + 8 * c8;
-        st.k[r] = *reinterpret_cast<const uint4*>(a.k + off);
-        st.v[r] = *reinterpret_cast<const uint4*>(a.v + off);
-        if constexpr (OUT) st.q[r] = *reinterpret_cast<const uint4*>(a.q + off);
+      for (int r = 0; r < 4; ++r) {
+        st.x[r] = make_uint4(0u, 0u, 0u, 0u);
+        if (4 * i4 < sb.n - r) st.x[r] = *reinterpret_cast<const uint4*>(src + (long long)(sb.sgn * r) * HD + lo);
       }
     }
-  }
-  st.g = 0.f;
-  st.b = 0.f;
-  if (tid < 64 && tid < n) {
-    const size_t go = ((size_t)b * a.T + token_of(t0, n, rev, tid)) * a.H + h;
-    st.g = a.g[go];
-    st.b = a.beta[go];
+  } else {
+    const int i = tid & 63;
+    st.g = 0.f;
+    st.b = 0.f;
+    if (i < sb.n) {
+      const long long go = ((long long)b * a.T + sb.ta) * a.H + h + (long long)(sb.sgn * i) * a.H;
+      st.g = a.g[go];
+      st.b = a.beta[go];
+    }
   }
 }
 
@@ -297,193 +308,308 @@ __device__ __forceinline__ uint2 pack4(hb x, hb y, hb z, hb w) {
                     static_cast<uint32_t>(z) | (static_cast<uint32_t>(w) << 16));
 }
 
-// Write the staged sub-chunk into LDS as fp16 (K and Q row-major, K and V
-// transposed) and form the scan-order gate cumsum (log2 units) and beta.
+// Write the staged sub-chunk into buffer B: K and Q rows and K^T as fp16, and
+// (helper) the scan-order gate cumsum in log2 units and the per-token factors.
 template <int D, bool OUT>
-__device__ __forceinline__ void stage_subchunk(const Smem<D, OUT>& S, const Stage& st) {
-  using L = Lay<D, OUT>;
-  constexpr int C8 = D / 8;
+__device__ __forceinline__ void stage_subchunk(const Buf& B, const Stage& st, float c) {
+  using G = Geo<D>;
   const int tid = threadIdx.x;
-  if (tid < 16 * C8) {
-    const int i4 = tid / C8, c8 = tid % C8;
-    uint4 kh[4], vh[4];
+  if (wave_id() < G::NSW) {
+    const bool isq = tid >= 2 * D;
+    if (OUT || !isq) {
+      const int kb = isq ? tid - 2 * D : tid;
+      const int i4 = kb & 15, c8 = kb >> 4;
+      uint4 xh[4];
+      hb* rows = isq ? B.qr : B.kr;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      kh[r] = bf16x8_to_f16x8(st.k[r]);
-      vh[r] = bf16x8_to_f16x8(st.v[r]);
-      *reinterpret_cast<uint4*>(S.kr + (4 * i4 + r) * L::LDK + 8 * c8) = kh[r];
-      if constexpr (OUT) *reinterpret_cast<uint4*>(S.qr + (4 * i4 + r) * L::LDK + 8 * c8) = bf16x8_to_f16x8(st.q[r]);
-    }
-    const hb* ke[4] = {reinterpret_cast<const hb*>(&kh[0]), reinterpret_cast<const hb*>(&kh[1]),
-                       reinterpret_cast<const hb*>(&kh[2]), reinterpret_cast<const hb*>(&kh[3])};
-    const hb* ve[4] = {reinterpret_cast<const hb*>(&vh[0]), reinterpret_cast<const hb*>(&vh[1]),
-                       reinterpret_cast<const hb*>(&vh[2]), reinterpret_cast<const hb*>(&vh[3])};
+      for (int r = 0; r < 4; ++r) {
+        xh[r] = bf16x8_to_f16x8(st.x[r]);
+        *reinterpret_cast<uint4*>(rows + (4 * i4 + r) * G::LDK + 8 * c8) = xh[r];
+      }
+      if (!isq) {
+        const hb* e[4] = {reinterpret_cast<const hb*>(&xh[0]), reinterpret_cast<const hb*>(&xh[1]),
+                          reinterpret_cast<const hb*>(&xh[2]), reinterpret_cast<const hb*>(&xh[3])};
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      *reinterpret_cast<uint2*>(S.kt + (8 * c8 + u) * LDT + 4 * i4) = pack4(ke[0][u], ke[1][u], ke[2][u], ke[3][u]);
-      *reinterpret_cast<uint2*>(S.vt + (8 * c8 + u) * LDT + 4 * i4) = pack4(ve[0][u], ve[1][u], ve[2][u], ve[3][u]);
+        for (int u = 0; u < 8; ++u)
+          *reinterpret_cast<uint2*>(B.kt + (8 * c8 + u) * LDT + 4 * i4) = pack4(e[0][u], e[1][u], e[2][u], e[3][u]);
+      }
     }
-  }
-  if (tid < 64) {
+  } else {
+    const int i = tid & 63;
     float s = st.g * kLog2e;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
       const float t = __shfl_up(s, d);
-      if (tid >= d) s += t;
+      if (i >= d) s += t;
     }
-    S.g2[tid] = s;
-    S.bt[tid] = st.b;
+    const float last = __shfl(s, 63);
+    const float e = ex2(s);
+    B.g2[i] = s;
+    B.eg[i] = e;
+    B.ce[i] = c * e;
+    B.dn[i] = c * ex2(last - s);
+    B.bt[i] = st.b;
   }
 }
 
-// Gram products of the staged sub-chunk: the strictly lower gated A (fp32 and
-// fp16) and, for the output pass, the gated causal P = c tril(Q K^T) * E.
+// --- Gram tiles -------------------------------------------------------------------
+// Tile (ta, tb), ta <= tb, of the products of the K rows of block ta with the
+// K (or Q) rows of block tb: lane holds rows y = 16 ta + 4g + r against row
+// x = 16 tb + (lane % 16), i.e. entries [x][y .. y+3] of A or P.
+template <int D>
+__device__ __forceinline__ f32x4 gram_tile(const hb* kr, const hb* xr, int ta, int tb, int cl, int g) {
+  using G = Geo<D>;
+  const hb* arow = kr + (16 * ta + cl) * G::LDK;
+  const hb* brow = xr + (16 * tb + cl) * G::LDK;
+  f32x4 acc = zero4();
+#pragma unroll
+  for (int p = 0; p < G::NP; ++p) acc = mfma32(ld8(arow + 32 * p + 8 * g), ld8(brow + 32 * p + 8 * g), acc);
+  return acc;
+}
+
+// Lower-triangular 16x16-tile pairs (a <= b) of a 4x4 tile grid; the first
+// six are the strictly lower ones.
+__device__ __forceinline__ void tile_pair(int t, int& a, int& b) {
+  constexpr int A[10] = {0, 0, 0, 1, 1, 2, 0, 1, 2, 3};
+  constexpr int B[10] = {1, 2, 3, 2, 3, 3, 0, 1, 2, 3};
+  a = A[t];
+  b = B[t];
+}
+
+// A of sub-chunk B (diagonal blocks fp32 by the helper, off-diagonal blocks
+// fp16 by the strip waves) and, for the output pass, P = c tril(Q K^T) * E.
 template <int D, bool OUT>
-__device__ void gram_stage(const Args& a, const Smem<D, OUT>& S) {
-  using L = Lay<D, OUT>;
-  const int wave = wave_id(), lane = threadIdx.x & 63, g = lane >> 4;
+__device__ void gram_stage(const Args& a, const Buf& B, const Inv& I) {
+  using G = Geo<D>;
+  const int wave = wave_id(), lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
   const float c2 = a.c * a.c;
-  for (int t = wave; t < 10; t += NW) {
+  if (wave == G::HW) {
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      const f32x4 s = gram_tile<D>(B.kr, B.kr, blk, blk, cl, g);
+      const int x = 16 * blk + cl, y0 = 16 * blk + 4 * g;
+      const float gx = B.g2[x], bx = c2 * B.bt[x];
+      const f32x4 gy = ld4f(B.g2 + y0);
+      float4 v;
+      v.x = (x > y0 + 0) ? bx * s[0] * ex2(gx - gy[0]) : 0.f;
+      v.y = (x > y0 + 1) ? bx * s[1] * ex2(gx - gy[1]) : 0.f;
+      v.z = (x > y0 + 2) ? bx * s[2] * ex2(gx - gy[2]) : 0.f;
+      v.w = (x > y0 + 3) ? bx * s[3] * ex2(gx - gy[3]) : 0.f;
+      *reinterpret_cast<float4*>(I.ad + blk * 256 + cl * 16 + 4 * g) = v;
+    }
+    return;
+  }
+  constexpr int NTILE = OUT ? 16 : 6;
+  for (int t = wave; t < NTILE; t += G::NSW) {
+    const bool isp = t >= 6;
     int ta, tb;
-    tri_pair(t, ta, tb);
-    const int x = tb * 16 + (lane & 15);           // A/P row (scan-local token)
-    const int y0 = ta * 16 + 4 * g;                // first of the lane's 4 columns
-    const float gx = S.g2[x], bx = S.bt[x];
-    // lane holds K_{y0+r} . K_x (symmetric Gram) and K_{y0+r} . Q_x
-    const hb* ka = S.kr + (ta * 16 + (lane & 15)) * L::LDK;
-    const f32x4 s = mma_lds(ka, S.kr + x * L::LDK, D / 16, g, zero4());
-    float av[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int y = y0 + r;
-      av[r] = (x > y) ? c2 * bx * s[r] * exp2f(gx - S.g2[y]) : 0.f;
+    tile_pair(isp ? t - 6 : t, ta, tb);
+    const f32x4 s = gram_tile<D>(B.kr, isp ? B.qr : B.kr, ta, tb, cl, g);
+    const int x = 16 * tb + cl, y0 = 16 * ta + 4 * g;
+    const float gx = B.g2[x];
+    const f32x4 gy = ld4f(B.g2 + y0);
+    if (!isp) {
+      const float bx = c2 * B.bt[x];
+      store4_h(I.ao + x * LDT + y0, bx * s[0] * ex2(gx - gy[0]), bx * s[1] * ex2(gx - gy[1]),
+               bx * s[2] * ex2(gx - gy[2]), bx * s[3] * ex2(gx - gy[3]));
+    } else {
+      const float cc = a.c;
+      store4_h(B.pp + x * LDT + y0, (x >= y0 + 0) ? cc * s[0] * ex2(gx - gy[0]) : 0.f,
+               (x >= y0 + 1) ? cc * s[1] * ex2(gx - gy[1]) : 0.f, (x >= y0 + 2) ? cc * s[2] * ex2(gx - gy[2]) : 0.f,
+               (x >= y0 + 3) ? cc * s[3] * ex2(gx - gy[3]) : 0.f);
     }
-    *reinterpret_cast<float4*>(S.af + x * LDA + y0) = make_float4(av[0], av[1], av[2], av[3]);
-    store4_h(S.ab + x * LDT + y0, av[0], av[1], av[2], av[3]);
-    if constexpr (OUT) {
-      const f32x4 z = mma_lds(ka, S.qr + x * L::LDK, D / 16, g, zero4());
-      float pv[4];
+  }
+}
+
+// --- triangular inverse (helper wavefront) ------------------------------------------
+// Tm = (I + A)^-1 of sub-chunk B into I.tt as Tm diag(beta) (fp16 rows).
+// Diagonal 16x16 blocks: lane (block g, row i) solves row i of
+// T_gg (I + A_gg) = I from the last column to the first, in fp32.
+// Off-diagonal blocks, level by level:
+//   T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj,
+// with every T_kj kept in registers in accumulator layout (fp16), so the
+// levels need no LDS round trip.
+__device__ __forceinline__ f16x4_t tinv_block(const Inv& I, const float* bt, int i, int j, f16x8_t p0, bool two,
+                                              f16x8_t p1, int cl, int g) {
+  const hb* arow = I.ao + (16 * i + cl) * LDT + 16 * j;
+  f32x4 m = mfma32(fragA2(arow, 0, g), p0, zero4());
+  if (two) m = mfma32(fragA2(arow, 2, g), p1, m);
+  const f16x4_t mh = tof16(m);
+  const f16x4_t tii = ld4(I.td + (16 * i + cl) * LDD + 4 * g);
+  const f32x4 tc = mfma16(tii, mh);          // T_ii M: lane holds [4g + r][cl]
+  const f32x4 tr = mfma16(mh, tii);          // (T_ii M)^T: lane holds [cl][4g + r]
+  const f32x4 bb = ld4f(bt + 16 * j + 4 * g);
+  store4_h(I.tt + (16 * i + cl) * LDT + 16 * j + 4 * g, -tr[0] * bb[0], -tr[1] * bb[1], -tr[2] * bb[2],
+           -tr[3] * bb[3]);
+  return tof16(-tc);
+}
+
+__device__ void tinv(const Inv& I, const float* bt) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
+  {
+    const float* Ab = I.ad + g * 256;
+    float one = 1.f;
+    asm volatile("" : "+v"(one));   // keep the identity row from being hoisted out of the caller's loop
+    float s[16];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int y = y0 + r;
-        pv[r] = (x >= y) ? a.c * z[r] * exp2f(gx - S.g2[y]) : 0.f;
+    for (int j = 0; j < 16; ++j) s[j] = (j == cl) ? one : 0.f;
+#pragma unroll
+    for (int k = 15; k >= 1; --k) {
+      __builtin_amdgcn_sched_barrier(0);
+      const float tk = s[k];
+#pragma unroll
+      for (int q = 0; 4 * q < k; ++q) {
+        const f32x4 a4 = ld4f(Ab + k * 16 + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * q + e < k) s[4 * q + e] = fmaf(-tk, a4[e], s[4 * q + e]);
       }
-      store4_h(S.p + x * LDT + y0, pv[0], pv[1], pv[2], pv[3]);
+    }
+    float bb[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 v = ld4f(bt + 16 * g + 4 * q);
+      bb[4 * q] = v[0];
+      bb[4 * q + 1] = v[1];
+      bb[4 * q + 2] = v[2];
+      bb[4 * q + 3] = v[3];
+    }
+    hb* tdr = I.td + (16 * g + cl) * LDD;
+    hb* ttr = I.tt + (16 * g + cl) * LDT + 16 * g;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      store4_h(tdr + 4 * q, s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]);
+      store4_h(ttr + 4 * q, s[4 * q] * bb[4 * q], s[4 * q + 1] * bb[4 * q + 1], s[4 * q + 2] * bb[4 * q + 2],
+               s[4 * q + 3] * bb[4 * q + 3]);
+    }
+  }
+  wave_lds_sync();
+  // diagonal blocks 0..2 in accumulator layout (lane: rows 4g + r, column cl)
+  f16x4_t d[3];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) d[j][r] = __builtin_bit_cast(_Float16, I.td[(16 * j + 4 * g + r) * LDD + cl]);
+  }
+  const f16x4_t z = zero_h4();
+  const f16x4_t t10 = tinv_block(I, bt, 1, 0, cat8(d[0], z), false, cat8(z, z), cl, g);
+  const f16x4_t t21 = tinv_block(I, bt, 2, 1, cat8(d[1], z), false, cat8(z, z), cl, g);
+  (void)tinv_block(I, bt, 3, 2, cat8(d[2], z), false, cat8(z, z), cl, g);
+  const f16x4_t t20 = tinv_block(I, bt, 2, 0, cat8(d[0], t10), false, cat8(z, z), cl, g);
+  (void)tinv_block(I, bt, 3, 1, cat8(d[1], t21), false, cat8(z, z), cl, g);
+  (void)tinv_block(I, bt, 3, 0, cat8(d[0], t10), true, cat8(t20, z), cl, g);
+}
+
+// --- strip-wave products ----------------------------------------------------------
+// State strip: X[md] (md = 0 .. MD-1), the 16x16 accumulator tiles of rows
+// 16 md .. 16 md + 15 of the wave's 16 state columns, fp32.
+
+// fp16 B pairs of a state strip (tiles 2p, 2p + 1; a missing last tile is 0).
+template <int D>
+__device__ __forceinline__ void state_pairs(const f32x4 (&X)[Geo<D>::MD], f16x8_t (&Xp)[Geo<D>::NP]) {
+  using G = Geo<D>;
+#pragma unroll
+  for (int p = 0; p < G::NP; ++p)
+    Xp[p] = cat8(tof16(X[2 * p]), 2 * p + 1 < G::MD ? tof16(X[2 * p + 1]) : zero_h4());
+}
+
+// acc[j][mt] = rows (16 mt ..) of `rows` (d-contracted fp16) times strip j.
+template <int D, int SPW>
+__device__ __forceinline__ void rows_times_state(const hb* rows, const f16x8_t (&Xp)[SPW][Geo<D>::NP], int cl, int g,
+                                                 f32x4 (&acc)[SPW][4]) {
+  using G = Geo<D>;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) acc[j][mt] = zero4();
+    const hb* arow = rows + (16 * mt + cl) * G::LDK;
+#pragma unroll
+    for (int p = 0; p < G::NP; ++p) {
+      const f16x8_t a = fragA2(arow, 2 * p, g);
+#pragma unroll
+      for (int j = 0; j < SPW; ++j) acc[j][mt] = mfma32(a, Xp[j][p], acc[j][mt]);
     }
   }
 }
 
-// Diagonal 16x16 blocks of Tm = (I + A)^-1 by forward substitution in fp32
-// (one wavefront: lane = (block, column)).  Writes Tm_ii row-major into the
-// diagonal blocks of ab, column-major into tbt, and the scaled copies
-// t1 = Tm diag(beta), t2 = c Tm diag(beta e^G).
-template <int D, bool OUT>
-__device__ void diag_inverse(const Args& a, const Smem<D, OUT>& S) {
-  const int lane = threadIdx.x & 63;
-  const int blk = lane >> 4, cc = lane & 15;
-  const float* A0 = S.af + (16 * blk) * LDA + 16 * blk;
-  float t[16];
+// out[j][mt] (+)= lower-triangular token matrix M (fp16 rows, zero above the
+// diagonal) times the token-row tiles held as pairs vp[j][0] = (0, 1),
+// vp[j][1] = (2, 3).
+template <int SPW>
+__device__ __forceinline__ void tri_times(const hb* M, const f16x8_t (&vp)[SPW][2], int cl, int g,
+                                          f32x4 (&acc)[SPW][4]) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    float s = (r == cc) ? 1.f : 0.f;
+  for (int mt = 0; mt < 4; ++mt) {
+    __builtin_amdgcn_sched_barrier(0);
+    const hb* arow = M + (16 * mt + cl) * LDT;
 #pragma unroll
-    for (int k = 0; k < r; ++k) s = fmaf(-A0[r * LDA + k], t[k], s);
-    t[r] = s;
-  }
-  const int col = 16 * blk + cc;
-  const float bc = S.bt[col], ec = a.c * bc * exp2f(S.g2[col]);
+    for (int p = 0; 2 * p <= mt; ++p) {
+      const f16x8_t a = fragA2(arow, 2 * p, g);
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int row = 16 * blk + r;
-    S.ab[row * LDT + col] = f2h(t[r]);
-    S.t1[row * LDT + col] = f2h(t[r] * bc);
-    S.t2[row * LDT + col] = f2h(t[r] * ec);
-  }
-#pragma unroll
-  for (int r = 0; r < 16; r += 4) store4_h(S.tbt + col * LDT + 16 * blk + r, t[r], t[r + 1], t[r + 2], t[r + 3]);
-}
-
-// Off-diagonal blocks of Tm, one block column per wavefront (waves 0..2):
-// Tm_{ib,jb} = -Tm_{ib,ib} sum_{kb=jb}^{ib-1} A_{ib,kb} Tm_{kb,jb}.
-template <int D, bool OUT>
-__device__ void offdiag_inverse(const Args& a, const Smem<D, OUT>& S) {
-  const int wave = wave_id(), lane = threadIdx.x & 63, g = lane >> 4;
-  if (wave >= 3) return;
-  const int jb = wave;
-  hb* rt = reinterpret_cast<hb*>(S.af) + wave * 16 * LDT;   // R^T scratch (A is dead now)
-  const int col = 16 * jb + (lane & 15);
-  const float bc = S.bt[col], ec = a.c * bc * exp2f(S.g2[col]);
-  for (int ib = jb + 1; ib < 4; ++ib) {
-    const hb* arow = S.ab + (16 * ib + (lane & 15)) * LDT + 16 * jb;
-    const f32x4 R = mma_lds(arow, S.tbt + col * LDT + 16 * jb, ib - jb, g, zero4());
-    store4_h(rt + (lane & 15) * LDT + 4 * g, R[0], R[1], R[2], R[3]);
-    wave_lds_sync();
-    const f32x4 Dv = mma_lds(S.ab + (16 * ib + (lane & 15)) * LDT + 16 * ib, rt + (lane & 15) * LDT, 1, g,
-                             zero4());
-    const int row0 = 16 * ib + 4 * g;
-    store4_h(S.tbt + col * LDT + row0, -Dv[0], -Dv[1], -Dv[2], -Dv[3]);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      S.t1[(row0 + r) * LDT + col] = f2h(-Dv[r] * bc);
-      S.t2[(row0 + r) * LDT + col] = f2h(-Dv[r] * ec);
+      for (int j = 0; j < SPW; ++j) acc[j][mt] = mfma32(a, vp[j][p], acc[j][mt]);
     }
-    wave_lds_sync();
   }
 }
 
-// -W rows into kr:  W = t2 K, computed as W^T = K^T t2^T so that each lane
-// stores four consecutive d entries of one token row.
-template <int D, bool OUT>
-__device__ void w_stage(const Smem<D, OUT>& S) {
-  using L = Lay<D, OUT>;
-  const int wave = wave_id(), lane = threadIdx.x & 63, g = lane >> 4;
-  for (int t = wave; t < (D / 16) * 4; t += NW) {
-    const int md = t >> 2, nt = t & 3;
-    const f32x4 w = mma_lds(S.kt + (md * 16 + (lane & 15)) * LDT, S.t2 + (nt * 16 + (lane & 15)) * LDT,
-                            nt + 1, g, zero4());
-    store4_h(S.kr + (nt * 16 + (lane & 15)) * L::LDK + md * 16 + 4 * g, -w[0], -w[1], -w[2], -w[3]);
+// X[j] <- dec X[j] + K^T vs[j]  (vs: fp16 pairs of token-row tiles).
+template <int D, int SPW>
+__device__ __forceinline__ void state_update(const hb* kt, const f16x8_t (&vs)[SPW][2], float dec, int cl, int g,
+                                             f32x4 (&X)[SPW][Geo<D>::MD]) {
+  using G = Geo<D>;
+#pragma unroll
+  for (int md = 0; md < G::MD; ++md) {
+    __builtin_amdgcn_sched_barrier(0);
+    const hb* arow = kt + (16 * md + cl) * LDT;
+    const f16x8_t a0 = fragA2(arow, 0, g), a1 = fragA2(arow, 2, g);
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      f32x4 acc = X[j][md] * dec;
+      acc = mfma32(a0, vs[j][0], acc);
+      acc = mfma32(a1, vs[j][1], acc);
+      X[j][md] = acc;
+    }
   }
 }
 
-// Common per-sub-chunk preparation: write the staged sub-chunk to LDS, start
-// fetching the next one (if any), then Gram, Tm and -W.
-template <int D, bool OUT>
-__device__ __forceinline__ void prepare(const Args& a, const Smem<D, OUT>& S, Stage& st, int b, int h,
-                                        bool has_next, long long t0n, int nn, bool rev) {
-  const int wave = wave_id();
-  __syncthreads();
-  stage_subchunk<D, OUT>(S, st);
-  if (has_next) fetch_subchunk<D, OUT>(a, b, h, t0n, nn, rev, st);
-  __syncthreads();
-  gram_stage<D, OUT>(a, S);
-  __syncthreads();
-  if (wave == 0) diag_inverse<D, OUT>(a, S);
-  __syncthreads();
-  offdiag_inverse<D, OUT>(a, S);
-  __syncthreads();
-  w_stage<D, OUT>(S);
+// Value column `col` of the sub-chunk's rows in accumulator layout, kept as
+// raw bf16 pairs (rows 4g + r and 4g + r + 1 of tile mt in one register; zero
+// past n) until used.
+struct Vals {
+  uint32_t w[4][2];
+};
+
+template <int D>
+__device__ __forceinline__ void load_values(const Args& a, int b, int h, const Sub& sb, int col, int g, Vals& V) {
+  const long long HD = (long long)a.H * D;
+  const bh* base = a.v + ((long long)b * a.T + sb.ta) * HD + (long long)h * D;
+  const int lo = sb.sgn * 4 * g * (int)HD + col;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      uint32_t x0 = 0u, x1 = 0u;
+      const int r = 2 * q;
+      if (4 * g < sb.n - 16 * mt - r) x0 = base[(long long)(sb.sgn * (16 * mt + r)) * HD + lo];
+      if (4 * g < sb.n - 16 * mt - r - 1) x1 = base[(long long)(sb.sgn * (16 * mt + r + 1)) * HD + lo];
+      V.w[mt][q] = x0 | (x1 << 16);
+    }
 }
 
-// Per-lane row factors of token tile mt (rows 16 mt + 4 g + r):
-// exp(G_i) and c exp(G_n - G_i).
-__device__ __forceinline__ f32x4 row_decay(const float* g2, int mt, int g) {
-  const float4 v = *reinterpret_cast<const float4*>(g2 + mt * 16 + 4 * g);
-  return f32x4{exp2f(v.x), exp2f(v.y), exp2f(v.z), exp2f(v.w)};
-}
-__device__ __forceinline__ f32x4 row_scale(const float* g2, float glast, float c, int mt, int g) {
-  const float4 v = *reinterpret_cast<const float4*>(g2 + mt * 16 + 4 * g);
-  return f32x4{c * exp2f(glast - v.x), c * exp2f(glast - v.y), c * exp2f(glast - v.z), c * exp2f(glast - v.w)};
+__device__ __forceinline__ f32x4 vals_tile(const Vals& V, int mt) {
+  return f32x4{__uint_as_float(V.w[mt][0] << 16), __uint_as_float(V.w[mt][0] & 0xffff0000u),
+               __uint_as_float(V.w[mt][1] << 16), __uint_as_float(V.w[mt][1] & 0xffff0000u)};
 }
 
 // ---------------------------------------------------------------------------
 // 1. Segment maps.  grid (NS - 1, B * H, ndir).  The state X = [P | Q]
-// (D x 2D) is split into 16-column strips; wavefront w owns strips w, w + NW, ...
+// (D x 2D): strip wave w owns column strip w of P and column strip w of Q.
 template <int D>
-__global__ __launch_bounds__(NT) void seg_map_kernel(Args a) {
+__global__ __launch_bounds__(Geo<D>::NT) void seg_map_kernel(Args a) {
+  using G = Geo<D>;
   using L = Lay<D, false>;
-  constexpr int MD = D / 16, NS_ = 2 * MD, SPW = (NS_ + NW - 1) / NW;
+  constexpr int MD = G::MD, SPW = 2;
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
-  const Smem<D, false> S(smem);
   const int wave = wave_id(), lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
   const int pos = blockIdx.x;                       // scan position of the segment
   const int bh_ = blockIdx.y, b = bh_ / a.H, h = bh_ % a.H;
@@ -493,103 +619,110 @@ __global__ __launch_bounds__(NT) void seg_map_kernel(Args a) {
   const long long s0 = (long long)seg * a.L;
   const long long s1 = (s0 + a.L < a.T) ? s0 + a.L : a.T;
   const int nsub = (int)((s1 - s0 + CH - 1) / CH);
+  const Inv I = inv_at<D, false>(smem);
+  const bool helper = wave == G::HW;
 
-  for (int i = threadIdx.x; i < 4 * CH * LDT / 2; i += NT) reinterpret_cast<uint32_t*>(S.ab)[i] = 0u;
+  for (int i = threadIdx.x; i < L::BYTES / 16; i += G::NT) reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
 
   f32x4 X[SPW][MD];
 #pragma unroll
-  for (int j = 0; j < SPW; ++j) {
-    const int st = wave + NW * j;
+  for (int md = 0; md < MD; ++md)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      X[0][md][r] = (wave == md && 4 * g + r == cl) ? 1.f : 0.f;
+      X[1][md][r] = 0.f;
+    }
+
+  auto piece = [&](int jj) {
+    const int jc = rev ? nsub - 1 - jj : jj;
+    const long long t0 = s0 + (long long)jc * CH;
+    return make_sub(t0, (int)((s1 - t0) < CH ? (s1 - t0) : CH), rev);
+  };
+  Stage st;
+  Vals Vr;
+  {
+    const Sub s0b = piece(0);
+    fetch_subchunk<D, false>(a, b, h, s0b, st);
+    __syncthreads();
+    stage_subchunk<D, false>(buf_at<D, false>(smem, 0), st, a.c);
+    if (!helper) load_values<D>(a, b, h, s0b, 16 * wave + cl, g, Vr);
+    if (nsub > 1) fetch_subchunk<D, false>(a, b, h, piece(1), st);
+    __syncthreads();
+    gram_stage<D, false>(a, buf_at<D, false>(smem, 0), I);
+    __syncthreads();
+  }
+  if (helper) {
+    // helper: gate factors of c+1, inverse of c, diagonal A blocks of c+1
+    for (int c = 0; c < nsub; ++c) {
+      const Buf Bc = buf_at<D, false>(smem, c & 1), Bn = buf_at<D, false>(smem, (c + 1) & 1);
+      const Inv I = inv_at<D, false>(smem);
+      if (c + 1 < nsub) stage_subchunk<D, false>(Bn, st, a.c);
+      if (c + 2 < nsub) fetch_subchunk<D, false>(a, b, h, piece(c + 2), st);
+      tinv(I, Bc.bt);
+      __syncthreads();
+      if (c + 1 < nsub) gram_stage<D, false>(a, Bn, I);
+      __syncthreads();
+    }
+    return;
+  }
+  f32x4 R[SPW][4];
+  for (int c = 0; c < nsub; ++c) {
+    const Buf Bc = buf_at<D, false>(smem, c & 1), Bn = buf_at<D, false>(smem, (c + 1) & 1);
+      const Inv I = inv_at<D, false>(smem);
+    // alpha
+    if (c + 1 < nsub) stage_subchunk<D, false>(Bn, st, a.c);
+    if (c + 2 < nsub) fetch_subchunk<D, false>(a, b, h, piece(c + 2), st);
+    {
+      f16x8_t Xp[SPW][G::NP];
+      state_pairs<D>(X[0], Xp[0]);
+      state_pairs<D>(X[1], Xp[1]);
+      rows_times_state<D, SPW>(Bc.kr, Xp, cl, g, R);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const f32x4 ce = ld4f(Bc.ce + 16 * mt + 4 * g);
+        R[0][mt] = -(ce * R[0][mt]);
+        R[1][mt] = vals_tile(Vr, mt) - ce * R[1][mt];
+      }
+      if (c + 1 < nsub) load_values<D>(a, b, h, piece(c + 1), 16 * wave + cl, g, Vr);
+    }
+    __syncthreads();
+    // beta
+    {
+      f16x8_t Rh[SPW][2];
+#pragma unroll
+      for (int j = 0; j < SPW; ++j) {
+        Rh[j][0] = tof16x8(R[j][0], R[j][1]);
+        Rh[j][1] = tof16x8(R[j][2], R[j][3]);
+      }
+      f32x4 Vn[SPW][4];
+#pragma unroll
+      for (int j = 0; j < SPW; ++j)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) Vn[j][mt] = zero4();
+      tri_times<SPW>(I.tt, Rh, cl, g, Vn);
+      f16x8_t Vs[SPW][2];
+      const f32x4 d0 = ld4f(Bc.dn + 4 * g), d1 = ld4f(Bc.dn + 16 + 4 * g);
+      const f32x4 d2 = ld4f(Bc.dn + 32 + 4 * g), d3 = ld4f(Bc.dn + 48 + 4 * g);
+#pragma unroll
+      for (int j = 0; j < SPW; ++j) {
+        Vs[j][0] = tof16x8(Vn[j][0] * d0, Vn[j][1] * d1);
+        Vs[j][1] = tof16x8(Vn[j][2] * d2, Vn[j][3] * d3);
+      }
+      state_update<D, SPW>(Bc.kt, Vs, Bc.eg[CH - 1], cl, g, X);
+    }
+    if (c + 1 < nsub) gram_stage<D, false>(a, Bn, I);
+    __syncthreads();
+  }
+  // store X = [P | Q] (fp32, row-major [D][2D])
+  const float* Xg = a.maps + ((((size_t)slot * a.B + b) * a.H + h) * (a.NS - 1) + pos) * (size_t)D * (2 * D);
+  const __amdgpu_buffer_rsrc_t xr = block_rsrc(Xg, D * 2 * D * 4);
+  const uint32_t xo = (uint32_t)((4 * g * 2 * D + wave * 16 + cl) * 4);
+#pragma unroll
+  for (int j = 0; j < SPW; ++j)
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) X[j][md][r] = (st == md && 4 * g + r == cl) ? 1.f : 0.f;
-  }
-
-  // sub-chunk jj of the scan: its first original token and size
-  auto piece = [&](int jj, long long& t0, int& n) {
-    const int jc = rev ? nsub - 1 - jj : jj;
-    t0 = s0 + (long long)jc * CH;
-    n = (int)((s1 - t0) < CH ? (s1 - t0) : CH);
-  };
-  Stage st;
-  {
-    long long t0;
-    int n;
-    piece(0, t0, n);
-    fetch_subchunk<D, false>(a, b, h, t0, n, rev, st);
-  }
-  for (int jj = 0; jj < nsub; ++jj) {
-    long long t0, t0n = 0;
-    int n, nn = 0;
-    piece(jj, t0, n);
-    if (jj + 1 < nsub) piece(jj + 1, t0n, nn);
-    prepare<D, false>(a, S, st, b, h, jj + 1 < nsub, t0n, nn, rev);
-    // U strips (values part only)
-    f32x4 V[SPW][4];
-#pragma unroll
-    for (int j = 0; j < SPW; ++j) {
-      const int st = wave + NW * j;
-      const int vs = st < MD ? 0 : (st < NS_ ? st - MD : MD - 1);   // value strip (clamped)
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const f32x4 u = mma_lds(S.t1 + (mt * 16 + cl) * LDT, S.vt + (vs * 16 + cl) * LDT, mt + 1, g, zero4());
-        V[j][mt] = st >= MD ? u : zero4();          // the P part has no values
-      }
-    }
-    __syncthreads();
-    const float glast = S.g2[CH - 1];
-    const float dec = exp2f(glast);
-    // fp16 copy of the state as MFMA B pairs (rows = d)
-    f16x8_t Xp[SPW][MD / 2 > 0 ? MD / 2 : 1];
-    f16x4_t Xq[SPW];
-#pragma unroll
-    for (int j = 0; j < SPW; ++j) {
-#pragma unroll
-      for (int p = 0; p < MD / 2; ++p) Xp[j][p] = tof16x8(X[j][2 * p], X[j][2 * p + 1]);
-      if constexpr (MD & 1) Xq[j] = tof16(X[j][MD - 1]);
-    }
-    // V'aug = [0 | U] - W X   (per token tile mt, all strips at once)
-    f32x4 Vf[SPW][4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      f32x4 acc[SPW];
-#pragma unroll
-      for (int j = 0; j < SPW; ++j) acc[j] = V[j][mt];
-      mma_dB<SPW, MD / 2, (MD & 1) != 0>(S.kr + (mt * 16 + cl) * L::LDK, Xp, Xq, g, acc);
-      const f32x4 sc = row_scale(S.g2, glast, a.c, mt, g);
-#pragma unroll
-      for (int j = 0; j < SPW; ++j) Vf[j][mt] = acc[j] * sc;
-    }
-    f16x8_t Vs[SPW][2];
-#pragma unroll
-    for (int j = 0; j < SPW; ++j) {
-      Vs[j][0] = tof16x8(Vf[j][0], Vf[j][1]);
-      Vs[j][1] = tof16x8(Vf[j][2], Vf[j][3]);
-    }
-    // X <- e^{G_n} X + c K^T diag(e^{G_n - G}) V'aug
-#pragma unroll
-    for (int md = 0; md < MD; ++md) {
-      f32x4 acc[SPW];
-#pragma unroll
-      for (int j = 0; j < SPW; ++j) acc[j] = X[j][md] * dec;
-      mma_tB<SPW>(S.kt + (md * 16 + cl) * LDT, Vs, 4, g, acc);
-#pragma unroll
-      for (int j = 0; j < SPW; ++j) X[j][md] = acc[j];
-    }
-  }
-  // store X = [P | Q] (fp32, row-major [D][2D])
-  float* Xg = a.maps + ((((size_t)slot * a.B + b) * a.H + h) * (a.NS - 1) + pos) * (size_t)D * (2 * D);
-#pragma unroll
-  for (int j = 0; j < SPW; ++j) {
-    const int st = wave + NW * j;
-    if (st < NS_) {
-#pragma unroll
-      for (int md = 0; md < MD; ++md)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Xg[(size_t)(md * 16 + 4 * g + r) * (2 * D) + st * 16 + cl] = X[j][md][r];
-    }
-  }
+      for (int r = 0; r < 4; ++r) block_store(xr, xo, (uint32_t)(((md * 16 + r) * 2 * D + j * D) * 4), X[j][md][r]);
 }
 
 // ---------------------------------------------------------------------------
@@ -703,16 +836,18 @@ __global__ __launch_bounds__(NTC) void seg_chain_kernel(Args a) {
 }
 
 // ---------------------------------------------------------------------------
+
+// ---------------------------------------------------------------------------
 // 3. Outputs.  grid (NS, B * H).  Each workgroup runs its segment for every
 // requested direction (reversed scan first) from the start states of the
 // chain; the reversed scan's outputs are summed into the forward scan's.
-// Wavefront w owns the state's 16-column strips w, w + NW, ...
+// Strip wave w owns state columns 16 w .. 16 w + 15.
 template <int D>
-__global__ __launch_bounds__(NT) void seg_out_kernel(Args a) {
+__global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
+  using G = Geo<D>;
   using L = Lay<D, true>;
-  constexpr int MD = D / 16, SPW = (MD + NW - 1) / NW;
+  constexpr int MD = G::MD, SPW = 1;
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
-  const Smem<D, true> S(smem);
   const int wave = wave_id(), lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
   const int seg = blockIdx.x;
   const int bh_ = blockIdx.y, b = bh_ / a.H, h = bh_ % a.H;
@@ -720,9 +855,15 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(Args a) {
   const long long s1 = (s0 + a.L < a.T) ? s0 + a.L : a.T;
   const int nsub = (int)((s1 - s0 + CH - 1) / CH);
   const size_t sbase = ((size_t)b * a.H + h) * D * D;
+  const Inv I = inv_at<D, true>(smem);
+  const bool helper = wave == G::HW;
+  const int col = 16 * wave + cl;                  // state / value column of a strip lane
+  const long long HD = (long long)a.H * D;
+  const uint32_t so = (uint32_t)((4 * g * D + col) * 4);   // lane byte offset within a state
 
-  for (int i = threadIdx.x; i < 5 * CH * LDT / 2; i += NT) reinterpret_cast<uint32_t*>(S.ab)[i] = 0u;
+  for (int i = threadIdx.x; i < L::BYTES / 16; i += G::NT) reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
 
+#pragma unroll 1
   for (int pass = 0; pass < 2; ++pass) {
     const int dir = pass == 0 ? 1 : 0;                 // reversed scan first
     if (!(a.dirs & (1 << dir))) continue;
@@ -730,133 +871,127 @@ __global__ __launch_bounds__(NT) void seg_out_kernel(Args a) {
     const int mode = a.dirs == 3 ? (rev ? 1 : 2) : 0;   // 1: write partial, 2: add partial
     const int slot = slot_of_dir(a.dirs, dir);
     const int pos = rev ? a.NS - 1 - seg : seg;
-    const float* stp = a.starts + ((((size_t)slot * a.B + b) * a.H + h) * a.NS + pos) * (size_t)D * D;
     f32x4 H[SPW][MD];
-#pragma unroll
-    for (int j = 0; j < SPW; ++j) {
-      const int st = wave + NW * j;
+    if (!helper) {
+      const float* stp = a.starts + ((((size_t)slot * a.B + b) * a.H + h) * a.NS + pos) * (size_t)D * D;
+      const __amdgpu_buffer_rsrc_t hr = block_rsrc(stp, D * D * 4);
 #pragma unroll
       for (int md = 0; md < MD; ++md)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) H[j][md][r] = (st < MD) ? stp[(size_t)(md * 16 + 4 * g + r) * D + st * 16 + cl] : 0.f;
+        for (int r = 0; r < 4; ++r) H[0][md][r] = block_load(hr, so, (uint32_t)((md * 16 + r) * D * 4));
     }
-    auto piece = [&](int jj, long long& t0, int& n) {
+    auto piece = [&](int jj) {
       const int jc = rev ? nsub - 1 - jj : jj;
-      t0 = s0 + (long long)jc * CH;
-      n = (int)((s1 - t0) < CH ? (s1 - t0) : CH);
+      const long long t0 = s0 + (long long)jc * CH;
+      return make_sub(t0, (int)((s1 - t0) < CH ? (s1 - t0) : CH), rev);
     };
     Stage st;
+    Vals Vr;
     {
-      long long t0;
-      int n;
-      piece(0, t0, n);
-      fetch_subchunk<D, true>(a, b, h, t0, n, rev, st);
+      const Sub s0b = piece(0);
+      fetch_subchunk<D, true>(a, b, h, s0b, st);
+      __syncthreads();
+      stage_subchunk<D, true>(buf_at<D, true>(smem, 0), st, a.c);
+      if (!helper) load_values<D>(a, b, h, s0b, col, g, Vr);
+      if (nsub > 1) fetch_subchunk<D, true>(a, b, h, piece(1), st);
+      __syncthreads();
+      gram_stage<D, true>(a, buf_at<D, true>(smem, 0), I);
+      __syncthreads();
     }
-    for (int jj = 0; jj < nsub; ++jj) {
-      long long t0, t0n = 0;
-      int n, nn = 0;
-      piece(jj, t0, n);
-      if (jj + 1 < nsub) piece(jj + 1, t0n, nn);
-      prepare<D, true>(a, S, st, b, h, jj + 1 < nsub, t0n, nn, rev);
-      f32x4 V[SPW][4];
+    if (helper) {
+      // helper: gate factors of c+1, inverse of c, diagonal A blocks of c+1
+      for (int c = 0; c < nsub; ++c) {
+        const Buf Bc = buf_at<D, true>(smem, c & 1), Bn = buf_at<D, true>(smem, (c + 1) & 1);
+      const Inv I = inv_at<D, true>(smem);
+        if (c + 1 < nsub) stage_subchunk<D, true>(Bn, st, a.c);
+        if (c + 2 < nsub) fetch_subchunk<D, true>(a, b, h, piece(c + 2), st);
+        tinv(I, Bc.bt);
+        __syncthreads();
+        if (c + 1 < nsub) gram_stage<D, true>(a, Bn, I);
+        __syncthreads();
+      }
+      continue;
+    }
+    f32x4 QH[SPW][4], R[SPW][4];
+    float pre[4][4];
+    for (int c = 0; c < nsub; ++c) {
+      const Buf Bc = buf_at<D, true>(smem, c & 1), Bn = buf_at<D, true>(smem, (c + 1) & 1);
+      const Inv I = inv_at<D, true>(smem);
+      const Sub sb = piece(c);
+      const int lo = sb.sgn * 4 * g * (int)HD + col;      // per-lane part of output offsets
+      // alpha
+      if (c + 1 < nsub) stage_subchunk<D, true>(Bn, st, a.c);
+      if (c + 2 < nsub) fetch_subchunk<D, true>(a, b, h, piece(c + 2), st);
+      {
+        f16x8_t Hp[SPW][G::NP];
+        state_pairs<D>(H[0], Hp[0]);
+        rows_times_state<D, SPW>(Bc.qr, Hp, cl, g, QH);
+        rows_times_state<D, SPW>(Bc.kr, Hp, cl, g, R);
 #pragma unroll
-      for (int j = 0; j < SPW; ++j) {
-        const int st = wave + NW * j;
-        const int vs = st < MD ? st : MD - 1;      // clamped strip
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          V[j][mt] = mma_lds(S.t1 + (mt * 16 + cl) * LDT, S.vt + (vs * 16 + cl) * LDT, mt + 1, g, zero4());
+        for (int mt = 0; mt < 4; ++mt) R[0][mt] = vals_tile(Vr, mt) - ld4f(Bc.ce + 16 * mt + 4 * g) * R[0][mt];
+        if (c + 1 < nsub) load_values<D>(a, b, h, piece(c + 1), col, g, Vr);
       }
       __syncthreads();
-      const float glast = S.g2[CH - 1];
-      const float dec = exp2f(glast);
-      f16x8_t Hp[SPW][MD / 2 > 0 ? MD / 2 : 1];
-      f16x4_t Hq[SPW];
+      // beta
+      {
+        if (mode == 2) {
+          const float* pb = a.acc + ((long long)b * a.T + sb.ta) * HD + (long long)h * D;
 #pragma unroll
-      for (int j = 0; j < SPW; ++j) {
-#pragma unroll
-        for (int p = 0; p < MD / 2; ++p) Hp[j][p] = tof16x8(H[j][2 * p], H[j][2 * p + 1]);
-        if constexpr (MD & 1) Hq[j] = tof16(H[j][MD - 1]);
-      }
-      // V' = U - W H
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        f32x4 acc[SPW];
-#pragma unroll
-        for (int j = 0; j < SPW; ++j) acc[j] = V[j][mt];
-        mma_dB<SPW, MD / 2, (MD & 1) != 0>(S.kr + (mt * 16 + cl) * L::LDK, Hp, Hq, g, acc);
-#pragma unroll
-        for (int j = 0; j < SPW; ++j) V[j][mt] = acc[j];
-      }
-      f16x8_t Vh[SPW][2], Vs[SPW][2];
-#pragma unroll
-      for (int j = 0; j < SPW; ++j) {
-        Vh[j][0] = tof16x8(V[j][0], V[j][1]);
-        Vh[j][1] = tof16x8(V[j][2], V[j][3]);
-        const f32x4 s0 = row_scale(S.g2, glast, a.c, 0, g), s1 = row_scale(S.g2, glast, a.c, 1, g);
-        const f32x4 s2 = row_scale(S.g2, glast, a.c, 2, g), s3 = row_scale(S.g2, glast, a.c, 3, g);
-        Vs[j][0] = tof16x8(V[j][0] * s0, V[j][1] * s1);
-        Vs[j][1] = tof16x8(V[j][2] * s2, V[j][3] * s3);
-      }
-      // O = diag(e^G) Q H + P V'
-      const long long tstride = rev ? -(long long)a.H * D : (long long)a.H * D;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        f32x4 acc[SPW];
-#pragma unroll
-        for (int j = 0; j < SPW; ++j) acc[j] = zero4();
-        mma_dB<SPW, MD / 2, (MD & 1) != 0>(S.qr + (mt * 16 + cl) * L::LDK, Hp, Hq, g, acc);
-        const f32x4 eg = row_decay(S.g2, mt, g);
-#pragma unroll
-        for (int j = 0; j < SPW; ++j) acc[j] = acc[j] * eg;
-        mma_tB<SPW>(S.p + (mt * 16 + cl) * LDT, Vh, mt + 1, g, acc);
-        const int i0 = mt * 16 + 4 * g;                       // scan-local row of r = 0
-        const size_t e0 = ((size_t)b * a.T + token_of(t0, n, rev, i0)) * a.H * D + (size_t)h * D;
-#pragma unroll
-        for (int j = 0; j < SPW; ++j) {
-          const int st = wave + NW * j;
-          if (st < MD) {
-            const size_t base = e0 + st * 16 + cl;
+          for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              if (i0 + r < n) {
-                const size_t off = base + r * tstride;
-                float val = acc[j][r];
-                if (mode == 1) {
-                  a.acc[off] = val;
-                } else {
-                  if (mode == 2) val += a.acc[off];
-                  if (a.out_bf16) static_cast<uint16_t*>(a.out)[off] = f32_to_bf16_bits(val);
-                  else static_cast<float*>(a.out)[off] = val;
-                }
+              pre[mt][r] = 0.f;
+              if (4 * g < sb.n - 16 * mt - r) pre[mt][r] = pb[(long long)(sb.sgn * (16 * mt + r)) * HD + lo];
+            }
+        }
+        f16x8_t Rh[SPW][2];
+        Rh[0][0] = tof16x8(R[0][0], R[0][1]);
+        Rh[0][1] = tof16x8(R[0][2], R[0][3]);
+        f32x4 Vn[SPW][4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) Vn[0][mt] = zero4();
+        tri_times<SPW>(I.tt, Rh, cl, g, Vn);
+        f16x8_t Vh[SPW][2];
+        Vh[0][0] = tof16x8(Vn[0][0], Vn[0][1]);
+        Vh[0][1] = tof16x8(Vn[0][2], Vn[0][3]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) QH[0][mt] = ld4f(Bc.eg + 16 * mt + 4 * g) * QH[0][mt];
+        tri_times<SPW>(Bc.pp, Vh, cl, g, QH);
+        // outputs of the sub-chunk's first n scan rows
+        const long long ob = ((long long)b * a.T + sb.ta) * HD + (long long)h * D;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if (4 * g < sb.n - 16 * mt - r) {
+              const long long off = ob + (long long)(sb.sgn * (16 * mt + r)) * HD + lo;
+              float val = QH[0][mt][r];
+              if (mode == 1) {
+                a.acc[off] = val;
+              } else {
+                if (mode == 2) val += pre[mt][r];
+                if (a.out_bf16) static_cast<uint16_t*>(a.out)[off] = f32_to_bf16_bits(val);
+                else static_cast<float*>(a.out)[off] = val;
               }
             }
           }
-        }
+        f16x8_t Vs[SPW][2];
+        const f32x4 d0 = ld4f(Bc.dn + 4 * g), d1 = ld4f(Bc.dn + 16 + 4 * g);
+        const f32x4 d2 = ld4f(Bc.dn + 32 + 4 * g), d3 = ld4f(Bc.dn + 48 + 4 * g);
+        Vs[0][0] = tof16x8(Vn[0][0] * d0, Vn[0][1] * d1);
+        Vs[0][1] = tof16x8(Vn[0][2] * d2, Vn[0][3] * d3);
+        state_update<D, SPW>(Bc.kt, Vs, Bc.eg[CH - 1], cl, g, H);
       }
-      // H <- e^{G_n} H + c K^T diag(e^{G_n - G}) V'
-#pragma unroll
-      for (int md = 0; md < MD; ++md) {
-        f32x4 acc[SPW];
-#pragma unroll
-        for (int j = 0; j < SPW; ++j) acc[j] = H[j][md] * dec;
-        mma_tB<SPW>(S.kt + (md * 16 + cl) * LDT, Vs, 4, g, acc);
-#pragma unroll
-        for (int j = 0; j < SPW; ++j) H[j][md] = acc[j];
-      }
+      if (c + 1 < nsub) gram_stage<D, true>(a, Bn, I);
+      __syncthreads();
     }
     // final state: the scan's last segment
     if (a.hT && pos == a.NS - 1 && (dir == 0 || a.dirs == 2)) {
+      const __amdgpu_buffer_rsrc_t hr = block_rsrc(a.hT + sbase, D * D * 4);
 #pragma unroll
-      for (int j = 0; j < SPW; ++j) {
-        const int st = wave + NW * j;
-        if (st < MD) {
+      for (int md = 0; md < MD; ++md)
 #pragma unroll
-          for (int md = 0; md < MD; ++md)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) a.hT[sbase + (size_t)(md * 16 + 4 * g + r) * D + st * 16 + cl] = H[j][md][r];
-        }
-      }
+        for (int r = 0; r < 4; ++r) block_store(hr, so, (uint32_t)((md * 16 + r) * D * 4), H[0][md][r]);
     }
   }
 }
@@ -920,7 +1055,7 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
   const unsigned bhc = (unsigned)(p.B * p.H);
   if (pl.NS > 1) {
     prof_begin(stream, GDN_KERNEL_SEG_MAP);
-    hipLaunchKernelGGL((seg_map_kernel<D>), dim3(pl.NS - 1, bhc, pl.ndir), dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL((seg_map_kernel<D>), dim3(pl.NS - 1, bhc, pl.ndir), dim3(Geo<D>::NT), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     prof_end(stream, GDN_KERNEL_SEG_MAP);
@@ -931,7 +1066,7 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
   if (e != hipSuccess) return e;
   prof_end(stream, GDN_KERNEL_SEG_CHAIN);
   prof_begin(stream, GDN_KERNEL_SEG_OUT);
-  hipLaunchKernelGGL((seg_out_kernel<D>), dim3(pl.NS, bhc, 1), dim3(NT), 0, stream, a);
+  hipLaunchKernelGGL((seg_out_kernel<D>), dim3(pl.NS, bhc, 1), dim3(Geo<D>::NT), 0, stream, a);
   e = hipGetLastError();
   prof_end(stream, GDN_KERNEL_SEG_OUT);
   return e;

@@ -7,14 +7,17 @@ checked against the oracle before and independently of any GPU run:
     and each segment into sub-chunks of c = 64 tokens (the last of each may be
     ragged); a scan direction visits segments, sub-chunks and tokens in its own
     order (ascending for the forward scan, descending for the reversed one);
-  * sub-chunk (WY/UT) form, with G the inclusive within-sub-chunk cumsum of the
+  * sub-chunk form, with G the inclusive within-sub-chunk cumsum of the
     log-gates in scan order and E_ij = exp(G_i - G_j) (only i >= j is used):
         A  = strict_lower(diag(beta) K K^T * E)
-        Tm = (I + A)^-1
-        W  = Tm diag(beta exp(G)) K,     U = Tm diag(beta) V
-        V' = U - W H
+        Tm = (I + A)^-1      (16x16 diagonal blocks by substitution, then
+                              off-diagonal blocks level by level)
+        R  = V - diag(exp(G)) K H          (values minus the decayed prediction)
+        V' = Tm diag(beta) R
         O  = diag(exp(G)) Q H + (tril(Q K^T) * E) V'
         H <- exp(G_n) H + (diag(exp(G_n - G)) K)^T V'
+    (equal to the WY/UT form V' = U - W H with W = Tm diag(beta exp(G)) K and
+    U = Tm diag(beta) V, which `wy` keeps for the tests);
   * segment map (phase 1): the same chain run on X = [P | Q] from [I | 0] with
     values [0 | V] gives H_end = P H_start + Q;
   * segment chain (phase 2): H_{s+1} = P_s H_s + Q_s;
@@ -46,10 +49,41 @@ def wy(K, V, g, beta):
     return G, E, W, U
 
 
+def blocked_inverse(A, blk=16):
+    """(I + A)^-1 for strictly lower A, n a multiple of blk: each diagonal block
+    by row-wise substitution T_ii (I + A_ii) = I, then the off-diagonal blocks
+    T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj, level i - j = 1, 2, ..."""
+    n = A.shape[0]
+    nb = n // blk
+    T = np.zeros_like(A)
+    for b in range(nb):
+        Ab = A[b * blk:(b + 1) * blk, b * blk:(b + 1) * blk]
+        for i in range(blk):
+            s = np.zeros(blk)
+            s[i] = 1.0
+            for k in range(blk - 1, -1, -1):
+                s[:k] -= s[k] * Ab[k, :k]
+            T[b * blk + i, b * blk:(b + 1) * blk] = s
+    S = lambda i: slice(i * blk, (i + 1) * blk)
+    for lev in range(1, nb):
+        for j in range(nb - lev):
+            i = j + lev
+            M = sum(A[S(i), S(k)] @ T[S(k), S(j)] for k in range(j, i))
+            T[S(i), S(j)] = -T[S(i), S(i)] @ M
+    return T
+
+
 def chunk_step(H, Q, K, V, g, beta):
     """One sub-chunk from state H: returns (outputs, new state)."""
-    G, E, W, U = wy(K, V, g, beta)
-    Vn = U - W @ H
+    n = len(g)
+    G = np.cumsum(g)
+    E = np.exp(np.tril(G[:, None] - G[None, :]))
+    A = np.tril((beta[:, None] * (K @ K.T)) * E, -1)
+    pad = (-n) % 16
+    Ap = np.pad(A, ((0, pad), (0, pad)))
+    Tm = blocked_inverse(Ap)[:n, :n]
+    R = V - np.exp(G)[:, None] * (K @ H)
+    Vn = Tm @ (beta[:, None] * R)
     O = np.exp(G)[:, None] * (Q @ H) + (np.tril(Q @ K.T) * E) @ Vn
     Hn = np.exp(G[-1]) * H + (np.exp(G[-1] - G)[:, None] * K).T @ Vn
     return O, Hn

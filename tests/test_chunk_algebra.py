@@ -38,3 +38,22 @@ def test_segment_map_is_affine_state_map():
     for idx in pieces:
         _, H = M.chunk_step(H, np.zeros((len(idx), dk)), K[idx], V[idx], g[idx], b[idx])
     assert np.allclose(P @ H0 + Qm, H, atol=1e-12)
+
+
+def test_blocked_inverse_and_r_form_match_wy_form():
+    """The blocked triangular inverse equals (I + A)^-1, and the R form of V'
+    equals the WY/UT form U - W H."""
+    rng = np.random.default_rng(5)
+    n, d = 64, 24
+    K = rng.standard_normal((n, d))
+    K /= np.linalg.norm(K, axis=1, keepdims=True)
+    V = rng.standard_normal((n, d))
+    g = -rng.uniform(0.001, 0.1, n)
+    beta = 1 / (1 + np.exp(-rng.standard_normal(n)))
+    H = rng.standard_normal((d, d))
+    G, E, W, U = M.wy(K, V, g, beta)
+    A = np.tril((beta[:, None] * (K @ K.T)) * E, -1)
+    Tm = M.blocked_inverse(A)
+    assert np.max(np.abs(Tm - np.linalg.inv(np.eye(n) + A))) < 1e-12
+    R = V - np.exp(G)[:, None] * (K @ H)
+    assert np.max(np.abs(Tm @ (beta[:, None] * R) - (U - W @ H))) < 1e-11
