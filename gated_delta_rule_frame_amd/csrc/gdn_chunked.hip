@@ -234,16 +234,32 @@ __device__ __forceinline__ f32x4 ld4f(const float* p) {
 // 64-bit offsets stay live across the sub-chunk loop.
 struct Sub {
   long long ta;   // token of scan row 0
+  long long t0;   // first token of the sub-chunk in original order
   int sgn;        // +1: forward scan, -1: reversed scan
+  int r0;         // scan row 0 relative to t0 (so scan row i is t0 + r0 + sgn i)
   int n;          // rows present
 };
 
 __device__ __forceinline__ Sub make_sub(long long t0, int n, bool rev) {
   Sub s;
   s.ta = rev ? t0 + n - 1 : t0;
+  s.t0 = t0;
   s.sgn = rev ? -1 : 1;
+  s.r0 = rev ? n - 1 : 0;
   s.n = n;
   return s;
+}
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer over the n rows [t0, t0 + n) of a token-major tensor, starting at
+// one head's first element.  Offsets past the n rows (and the wrapped
+// "negative" offsets of scan rows past n in a reversed scan) are outside the
+// buffer: loads there return 0 and stores are dropped by the hardware range
+// check, so a ragged sub-chunk needs no branches (a branch around a load would
+// make the compiler wait for every outstanding load at the merge).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, long long bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
 // exp2 of a non-positive argument (results below 2^-126 flush to zero).
@@ -263,93 +279,83 @@ __device__ __forceinline__ void block_store(__amdgpu_buffer_rsrc_t r, uint32_t v
 }
 
 // --- staging --------------------------------------------------------------------
-// Strip-wave thread j < 2D holds a 4-token x 8-component block of K (token
-// group j % 16, components 8 (j / 16) ..), thread 2D + j the same block of Q
-// (output pass); the helper wave holds one token's log-gate and beta per lane.
-// Loading into registers is split from writing LDS so that the loads of
-// sub-chunk c+2 are in flight while sub-chunk c is computed.
-struct Stage {
-  uint4 x[4];
+// Strip-wave thread j holds scan rows 2 (j % 32) and 2 (j % 32) + 1, components
+// 8 (j / 32) .. + 7, of K (and of Q in the output pass); the helper wave holds
+// one token's log-gate and beta per lane.  Loading into registers is split from
+// writing LDS so that the loads of sub-chunk c+2 are in flight while sub-chunk
+// c is computed.  Every load is unconditional: rows past n (and sub-chunks past
+// the segment, given as n = 0) read as zeros through the buffer range check.
+struct StageKQ {
+  uint4 k[2], q[2];
+};
+struct StageG {
   float g, b;
 };
 
 template <int D, bool OUT>
-__device__ __forceinline__ void fetch_subchunk(const Args& a, int b, int h, const Sub& sb, Stage& st) {
-  using G = Geo<D>;
-  const int tid = threadIdx.x;
-  const long long HD = (long long)a.H * D;
-  if (wave_id() < G::NSW) {
-    const bool isq = tid >= 2 * D;
-    if (OUT || !isq) {
-      const int kb = isq ? tid - 2 * D : tid;
-      const int i4 = kb & 15, c8 = kb >> 4;
-      const bh* src = (isq ? a.q : a.k) + ((long long)b * a.T + sb.ta) * HD + (long long)h * D;
-      const int lo = sb.sgn * 4 * i4 * (int)HD + 8 * c8;
+__device__ __forceinline__ void fetch_kq(const Args& a, int b, int h, const Sub& sb, StageKQ& st) {
+  const int t = threadIdx.x, i2 = t & 31, c8 = t >> 5;
+  const int HD = a.H * D;
+  const long long e0 = ((long long)b * a.T + sb.t0) * HD + (long long)h * D;
+  const __amdgpu_buffer_rsrc_t rk = rows_rsrc(a.k + e0, (long long)sb.n * HD * 2);
+  const __amdgpu_buffer_rsrc_t rq = rows_rsrc(a.q + e0, OUT ? (long long)sb.n * HD * 2 : 0);
+  const int lr = sb.r0 + sb.sgn * 2 * i2;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        st.x[r] = make_uint4(0u, 0u, 0u, 0u);
-        if (4 * i4 < sb.n - r) st.x[r] = *reinterpret_cast<const uint4*>(src + (long long)(sb.sgn * r) * HD + lo);
-      }
-    }
-  } else {
-    const int i = tid & 63;
-    st.g = 0.f;
-    st.b = 0.f;
-    if (i < sb.n) {
-      const long long go = ((long long)b * a.T + sb.ta) * a.H + h + (long long)(sb.sgn * i) * a.H;
-      st.g = a.g[go];
-      st.b = a.beta[go];
+  for (int r = 0; r < 2; ++r) {
+    const uint32_t off = (uint32_t)((lr + sb.sgn * r) * HD * 2 + 16 * c8);
+    const u32x4_t vk = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+    st.k[r] = make_uint4(vk[0], vk[1], vk[2], vk[3]);
+    if constexpr (OUT) {
+      const u32x4_t vq = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+      st.q[r] = make_uint4(vq[0], vq[1], vq[2], vq[3]);
     }
   }
 }
 
-__device__ __forceinline__ uint2 pack4(hb x, hb y, hb z, hb w) {
-  return make_uint2(static_cast<uint32_t>(x) | (static_cast<uint32_t>(y) << 16),
-                    static_cast<uint32_t>(z) | (static_cast<uint32_t>(w) << 16));
+__device__ __forceinline__ void fetch_gates(const Args& a, int b, int h, const Sub& sb, StageG& st) {
+  const int i = threadIdx.x & 63;
+  const long long go = ((long long)b * a.T + sb.t0) * a.H + h;
+  const uint32_t off = (uint32_t)((sb.r0 + sb.sgn * i) * a.H * 4);
+  st.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rows_rsrc(a.g + go, (long long)sb.n * a.H * 4), off, 0, 0));
+  st.b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rows_rsrc(a.beta + go, (long long)sb.n * a.H * 4), off, 0, 0));
 }
 
-// Write the staged sub-chunk into buffer B: K and Q rows and K^T as fp16, and
-// (helper) the scan-order gate cumsum in log2 units and the per-token factors.
+// Write the staged rows into buffer B: K and Q rows and K^T as fp16.
 template <int D, bool OUT>
-__device__ __forceinline__ void stage_subchunk(const Buf& B, const Stage& st, float c) {
+__device__ __forceinline__ void stage_kq(const Buf& B, const StageKQ& st) {
   using G = Geo<D>;
-  const int tid = threadIdx.x;
-  if (wave_id() < G::NSW) {
-    const bool isq = tid >= 2 * D;
-    if (OUT || !isq) {
-      const int kb = isq ? tid - 2 * D : tid;
-      const int i4 = kb & 15, c8 = kb >> 4;
-      uint4 xh[4];
-      hb* rows = isq ? B.qr : B.kr;
+  const int t = threadIdx.x, i2 = t & 31, c8 = t >> 5;
+  uint4 xk[2];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        xh[r] = bf16x8_to_f16x8(st.x[r]);
-        *reinterpret_cast<uint4*>(rows + (4 * i4 + r) * G::LDK + 8 * c8) = xh[r];
-      }
-      if (!isq) {
-        const hb* e[4] = {reinterpret_cast<const hb*>(&xh[0]), reinterpret_cast<const hb*>(&xh[1]),
-                          reinterpret_cast<const hb*>(&xh[2]), reinterpret_cast<const hb*>(&xh[3])};
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          *reinterpret_cast<uint2*>(B.kt + (8 * c8 + u) * LDT + 4 * i4) = pack4(e[0][u], e[1][u], e[2][u], e[3][u]);
-      }
-    }
-  } else {
-    const int i = tid & 63;
-    float s = st.g * kLog2e;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const float t = __shfl_up(s, d);
-      if (i >= d) s += t;
-    }
-    const float last = __shfl(s, 63);
-    const float e = ex2(s);
-    B.g2[i] = s;
-    B.eg[i] = e;
-    B.ce[i] = c * e;
-    B.dn[i] = c * ex2(last - s);
-    B.bt[i] = st.b;
+  for (int r = 0; r < 2; ++r) {
+    xk[r] = bf16x8_to_f16x8(st.k[r]);
+    *reinterpret_cast<uint4*>(B.kr + (2 * i2 + r) * G::LDK + 8 * c8) = xk[r];
+    if constexpr (OUT) *reinterpret_cast<uint4*>(B.qr + (2 * i2 + r) * G::LDK + 8 * c8) = bf16x8_to_f16x8(st.q[r]);
   }
+  const hb* e0 = reinterpret_cast<const hb*>(&xk[0]);
+  const hb* e1 = reinterpret_cast<const hb*>(&xk[1]);
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    *reinterpret_cast<uint32_t*>(B.kt + (8 * c8 + u) * LDT + 2 * i2) =
+        static_cast<uint32_t>(e0[u]) | (static_cast<uint32_t>(e1[u]) << 16);
+}
+
+// The scan-order gate cumsum in log2 units and the per-token factors (helper).
+__device__ __forceinline__ void stage_gates(const Buf& B, const StageG& st, float c) {
+  const int i = threadIdx.x & 63;
+  float s = st.g * kLog2e;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const float t = __shfl_up(s, d);
+    if (i >= d) s += t;
+  }
+  const float last = __shfl(s, 63);
+  const float e = ex2(s);
+  B.g2[i] = s;
+  B.eg[i] = e;
+  B.ce[i] = c * e;
+  B.dn[i] = c * ex2(last - s);
+  B.bt[i] = st.b;
 }
 
 // --- Gram tiles -------------------------------------------------------------------
@@ -573,32 +579,28 @@ __device__ __forceinline__ void state_update(const hb* kt, const f16x8_t (&vs)[S
 }
 
 // Value column `col` of the sub-chunk's rows in accumulator layout, kept as
-// raw bf16 pairs (rows 4g + r and 4g + r + 1 of tile mt in one register; zero
-// past n) until used.
+// raw bf16 bits (zero past n) until used in the next sub-chunk, so that no
+// instruction near the loads waits for them.
 struct Vals {
-  uint32_t w[4][2];
+  uint32_t w[4][4];
 };
 
 template <int D>
 __device__ __forceinline__ void load_values(const Args& a, int b, int h, const Sub& sb, int col, int g, Vals& V) {
-  const long long HD = (long long)a.H * D;
-  const bh* base = a.v + ((long long)b * a.T + sb.ta) * HD + (long long)h * D;
-  const int lo = sb.sgn * 4 * g * (int)HD + col;
+  const int HD = a.H * D;
+  const bh* base = a.v + ((long long)b * a.T + sb.t0) * HD + (long long)h * D;
+  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(base, (long long)sb.n * HD * 2);
+  const int lp = (sb.r0 + sb.sgn * 4 * g) * HD * 2 + col * 2;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      uint32_t x0 = 0u, x1 = 0u;
-      const int r = 2 * q;
-      if (4 * g < sb.n - 16 * mt - r) x0 = base[(long long)(sb.sgn * (16 * mt + r)) * HD + lo];
-      if (4 * g < sb.n - 16 * mt - r - 1) x1 = base[(long long)(sb.sgn * (16 * mt + r + 1)) * HD + lo];
-      V.w[mt][q] = x0 | (x1 << 16);
-    }
+    for (int r = 0; r < 4; ++r)
+      V.w[mt][r] = __builtin_amdgcn_raw_buffer_load_b16(rs, (uint32_t)(lp + sb.sgn * (16 * mt + r) * HD * 2), 0, 0);
 }
 
 __device__ __forceinline__ f32x4 vals_tile(const Vals& V, int mt) {
-  return f32x4{__uint_as_float(V.w[mt][0] << 16), __uint_as_float(V.w[mt][0] & 0xffff0000u),
-               __uint_as_float(V.w[mt][1] << 16), __uint_as_float(V.w[mt][1] & 0xffff0000u)};
+  return f32x4{__uint_as_float(V.w[mt][0] << 16), __uint_as_float(V.w[mt][1] << 16),
+               __uint_as_float(V.w[mt][2] << 16), __uint_as_float(V.w[mt][3] << 16)};
 }
 
 // ---------------------------------------------------------------------------
@@ -633,20 +635,30 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_map_kernel(Args a) {
       X[1][md][r] = 0.f;
     }
 
-  auto piece = [&](int jj) {
+  auto piece = [&](int jj) {   // sub-chunk jj of the scan; past the segment: empty
     const int jc = rev ? nsub - 1 - jj : jj;
-    const long long t0 = s0 + (long long)jc * CH;
-    return make_sub(t0, (int)((s1 - t0) < CH ? (s1 - t0) : CH), rev);
+    const long long t0 = jj < nsub ? s0 + (long long)jc * CH : s0;
+    return make_sub(t0, jj < nsub ? (int)((s1 - t0) < CH ? (s1 - t0) : CH) : 0, rev);
   };
-  Stage st;
+  StageKQ sk;
+  StageG sg;
   Vals Vr;
   {
-    const Sub s0b = piece(0);
-    fetch_subchunk<D, false>(a, b, h, s0b, st);
+    const Sub s0b = piece(0), s1b = piece(1);
+    if (helper) {
+      fetch_gates(a, b, h, s0b, sg);
+    } else {
+      fetch_kq<D, false>(a, b, h, s0b, sk);
+      load_values<D>(a, b, h, s0b, 16 * wave + cl, g, Vr);
+    }
     __syncthreads();
-    stage_subchunk<D, false>(buf_at<D, false>(smem, 0), st, a.c);
-    if (!helper) load_values<D>(a, b, h, s0b, 16 * wave + cl, g, Vr);
-    if (nsub > 1) fetch_subchunk<D, false>(a, b, h, piece(1), st);
+    if (helper) {
+      stage_gates(buf_at<D, false>(smem, 0), sg, a.c);
+      fetch_gates(a, b, h, s1b, sg);
+    } else {
+      stage_kq<D, false>(buf_at<D, false>(smem, 0), sk);
+      fetch_kq<D, false>(a, b, h, s1b, sk);
+    }
     __syncthreads();
     gram_stage<D, false>(a, buf_at<D, false>(smem, 0), I);
     __syncthreads();
@@ -656,8 +668,8 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_map_kernel(Args a) {
     for (int c = 0; c < nsub; ++c) {
       const Buf Bc = buf_at<D, false>(smem, c & 1), Bn = buf_at<D, false>(smem, (c + 1) & 1);
       const Inv I = inv_at<D, false>(smem);
-      if (c + 1 < nsub) stage_subchunk<D, false>(Bn, st, a.c);
-      if (c + 2 < nsub) fetch_subchunk<D, false>(a, b, h, piece(c + 2), st);
+      stage_gates(Bn, sg, a.c);
+      fetch_gates(a, b, h, piece(c + 2), sg);
       tinv(I, Bc.bt);
       __syncthreads();
       if (c + 1 < nsub) gram_stage<D, false>(a, Bn, I);
@@ -670,8 +682,8 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_map_kernel(Args a) {
     const Buf Bc = buf_at<D, false>(smem, c & 1), Bn = buf_at<D, false>(smem, (c + 1) & 1);
       const Inv I = inv_at<D, false>(smem);
     // alpha
-    if (c + 1 < nsub) stage_subchunk<D, false>(Bn, st, a.c);
-    if (c + 2 < nsub) fetch_subchunk<D, false>(a, b, h, piece(c + 2), st);
+    stage_kq<D, false>(Bn, sk);
+    fetch_kq<D, false>(a, b, h, piece(c + 2), sk);
     {
       f16x8_t Xp[SPW][G::NP];
       state_pairs<D>(X[0], Xp[0]);
@@ -683,7 +695,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_map_kernel(Args a) {
         R[0][mt] = -(ce * R[0][mt]);
         R[1][mt] = vals_tile(Vr, mt) - ce * R[1][mt];
       }
-      if (c + 1 < nsub) load_values<D>(a, b, h, piece(c + 1), 16 * wave + cl, g, Vr);
+      load_values<D>(a, b, h, piece(c + 1), 16 * wave + cl, g, Vr);
     }
     __syncthreads();
     // beta
@@ -880,20 +892,30 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) H[0][md][r] = block_load(hr, so, (uint32_t)((md * 16 + r) * D * 4));
     }
-    auto piece = [&](int jj) {
+    auto piece = [&](int jj) {   // sub-chunk jj of the scan; past the segment: empty
       const int jc = rev ? nsub - 1 - jj : jj;
-      const long long t0 = s0 + (long long)jc * CH;
-      return make_sub(t0, (int)((s1 - t0) < CH ? (s1 - t0) : CH), rev);
+      const long long t0 = jj < nsub ? s0 + (long long)jc * CH : s0;
+      return make_sub(t0, jj < nsub ? (int)((s1 - t0) < CH ? (s1 - t0) : CH) : 0, rev);
     };
-    Stage st;
+    StageKQ sk;
+    StageG sg;
     Vals Vr;
     {
-      const Sub s0b = piece(0);
-      fetch_subchunk<D, true>(a, b, h, s0b, st);
+      const Sub s0b = piece(0), s1b = piece(1);
+      if (helper) {
+        fetch_gates(a, b, h, s0b, sg);
+      } else {
+        fetch_kq<D, true>(a, b, h, s0b, sk);
+        load_values<D>(a, b, h, s0b, col, g, Vr);
+      }
       __syncthreads();
-      stage_subchunk<D, true>(buf_at<D, true>(smem, 0), st, a.c);
-      if (!helper) load_values<D>(a, b, h, s0b, col, g, Vr);
-      if (nsub > 1) fetch_subchunk<D, true>(a, b, h, piece(1), st);
+      if (helper) {
+        stage_gates(buf_at<D, true>(smem, 0), sg, a.c);
+        fetch_gates(a, b, h, s1b, sg);
+      } else {
+        stage_kq<D, true>(buf_at<D, true>(smem, 0), sk);
+        fetch_kq<D, true>(a, b, h, s1b, sk);
+      }
       __syncthreads();
       gram_stage<D, true>(a, buf_at<D, true>(smem, 0), I);
       __syncthreads();
@@ -903,8 +925,8 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
       for (int c = 0; c < nsub; ++c) {
         const Buf Bc = buf_at<D, true>(smem, c & 1), Bn = buf_at<D, true>(smem, (c + 1) & 1);
       const Inv I = inv_at<D, true>(smem);
-        if (c + 1 < nsub) stage_subchunk<D, true>(Bn, st, a.c);
-        if (c + 2 < nsub) fetch_subchunk<D, true>(a, b, h, piece(c + 2), st);
+        stage_gates(Bn, sg, a.c);
+        fetch_gates(a, b, h, piece(c + 2), sg);
         tinv(I, Bc.bt);
         __syncthreads();
         if (c + 1 < nsub) gram_stage<D, true>(a, Bn, I);
@@ -918,10 +940,10 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
       const Buf Bc = buf_at<D, true>(smem, c & 1), Bn = buf_at<D, true>(smem, (c + 1) & 1);
       const Inv I = inv_at<D, true>(smem);
       const Sub sb = piece(c);
-      const int lo = sb.sgn * 4 * g * (int)HD + col;      // per-lane part of output offsets
+      const int lo = (sb.r0 + sb.sgn * 4 * g) * (int)HD + col;   // per-lane element offset from row t0
       // alpha
-      if (c + 1 < nsub) stage_subchunk<D, true>(Bn, st, a.c);
-      if (c + 2 < nsub) fetch_subchunk<D, true>(a, b, h, piece(c + 2), st);
+      stage_kq<D, true>(Bn, sk);
+      fetch_kq<D, true>(a, b, h, piece(c + 2), sk);
       {
         f16x8_t Hp[SPW][G::NP];
         state_pairs<D>(H[0], Hp[0]);
@@ -929,20 +951,20 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
         rows_times_state<D, SPW>(Bc.kr, Hp, cl, g, R);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) R[0][mt] = vals_tile(Vr, mt) - ld4f(Bc.ce + 16 * mt + 4 * g) * R[0][mt];
-        if (c + 1 < nsub) load_values<D>(a, b, h, piece(c + 1), col, g, Vr);
+        load_values<D>(a, b, h, piece(c + 1), col, g, Vr);
       }
       __syncthreads();
       // beta
       {
-        if (mode == 2) {
-          const float* pb = a.acc + ((long long)b * a.T + sb.ta) * HD + (long long)h * D;
+        const long long rowb = ((long long)b * a.T + sb.t0) * HD + (long long)h * D;
+        {   // reversed scan's partial (forward pass of a bidirectional call; else an empty buffer)
+          const __amdgpu_buffer_rsrc_t rs = rows_rsrc(a.acc + rowb, mode == 2 ? (long long)sb.n * HD * 4 : 0);
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              pre[mt][r] = 0.f;
-              if (4 * g < sb.n - 16 * mt - r) pre[mt][r] = pb[(long long)(sb.sgn * (16 * mt + r)) * HD + lo];
-            }
+            for (int r = 0; r < 4; ++r)
+              pre[mt][r] = __builtin_bit_cast(
+                  float, __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)((lo + sb.sgn * (16 * mt + r) * (int)HD) * 4), 0, 0));
         }
         f16x8_t Rh[SPW][2];
         Rh[0][0] = tof16x8(R[0][0], R[0][1]);
@@ -957,30 +979,31 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) QH[0][mt] = ld4f(Bc.eg + 16 * mt + 4 * g) * QH[0][mt];
         tri_times<SPW>(Bc.pp, Vh, cl, g, QH);
-        // outputs of the sub-chunk's first n scan rows
-        const long long ob = ((long long)b * a.T + sb.ta) * HD + (long long)h * D;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            if (4 * g < sb.n - 16 * mt - r) {
-              const long long off = ob + (long long)(sb.sgn * (16 * mt + r)) * HD + lo;
-              float val = QH[0][mt][r];
-              if (mode == 1) {
-                a.acc[off] = val;
-              } else {
-                if (mode == 2) val += pre[mt][r];
-                if (a.out_bf16) static_cast<uint16_t*>(a.out)[off] = f32_to_bf16_bits(val);
-                else static_cast<float*>(a.out)[off] = val;
-              }
-            }
-          }
         f16x8_t Vs[SPW][2];
         const f32x4 d0 = ld4f(Bc.dn + 4 * g), d1 = ld4f(Bc.dn + 16 + 4 * g);
         const f32x4 d2 = ld4f(Bc.dn + 32 + 4 * g), d3 = ld4f(Bc.dn + 48 + 4 * g);
         Vs[0][0] = tof16x8(Vn[0][0] * d0, Vn[0][1] * d1);
         Vs[0][1] = tof16x8(Vn[0][2] * d2, Vn[0][3] * d3);
         state_update<D, SPW>(Bc.kt, Vs, Bc.eg[CH - 1], cl, g, H);
+        // outputs of the sub-chunk's n scan rows (rows past n fall outside the buffer)
+        {
+          const bool half = mode != 1 && a.out_bf16;
+          void* dst = mode == 1 ? static_cast<void*>(a.acc) : a.out;
+          const long long esz = half ? 2 : 4;
+          const __amdgpu_buffer_rsrc_t rs = rows_rsrc(static_cast<char*>(dst) + rowb * esz, (long long)sb.n * HD * esz);
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const uint32_t off = (uint32_t)((lo + sb.sgn * (16 * mt + r) * (int)HD) * esz);
+              float val = QH[0][mt][r];
+              val += pre[mt][r];
+              if (half)
+                __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f32_to_bf16_bits(val), rs, off, 0, 0);
+              else
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), rs, off, 0, 0);
+            }
+        }
       }
       if (c + 1 < nsub) gram_stage<D, true>(a, Bn, I);
       __syncthreads();
