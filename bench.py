@@ -57,17 +57,22 @@ def subchunk_sizes(T, L, c=64):
 
 
 def out_flops(n, d):
-    """Algorithmic flops of the output pass on one sub-chunk of n tokens."""
-    return n * (n - 1) * d + 4 * n * (n + 1) * d + 6 * n * d * d + n ** 3 // 3
+    """Algorithmic flops of the output pass on one sub-chunk of n tokens:
+    strict-lower K K^T, causal Q K^T, the triangular inverse (n^3/3), K H and
+    Q H, Tm diag(beta) R and P V' (triangular), and the state update."""
+    return n * (n - 1) * d + 3 * n * (n + 1) * d + 6 * n * d * d + n ** 3 // 3
 
 
 def map_flops(n, d):
-    """Algorithmic flops of the segment-map pass on one sub-chunk (state [P|Q])."""
+    """Algorithmic flops of the segment-map pass on one sub-chunk (state [P|Q],
+    2d columns): strict-lower K K^T, the inverse, K X, Tm diag(beta) R and the
+    state update."""
     return n * (n - 1) * d + 2 * n * (n + 1) * d + 8 * n * d * d + n ** 3 // 3
 
 
 def executed_flops(T, L, d, bh, ndir):
-    """Per-kernel algorithmic flops of one call of the chunked path."""
+    """Per-launch algorithmic flops of the chunked path's kernels (the output
+    kernel is launched once per scan direction, the others once per call)."""
     segs = subchunk_sizes(T, L)
     per_out = sum(out_flops(n, d) for seg in segs for n in seg)
     # maps are formed for every segment but the last one of each scan
@@ -75,7 +80,7 @@ def executed_flops(T, L, d, bh, ndir):
     per_map_b = sum(map_flops(n, d) for seg in segs[1:] for n in seg)
     maps = per_map_f if ndir == 1 else per_map_f + per_map_b
     chain = (len(segs) - 1) * 2 * d ** 3
-    return {"seg_out_kernel": per_out * bh * ndir, "seg_map_kernel": maps * bh,
+    return {"seg_out_kernel": per_out * bh, "seg_map_kernel": maps * bh,
             "seg_chain_kernel": chain * bh * ndir}
 
 
@@ -224,7 +229,7 @@ def main():
     roof, flops_exec = None, None
     if "seg_out_kernel" in kern and L:
         fl = executed_flops(T, L, dk, B * H, ndir)
-        flops_exec = sum(fl.values())
+        flops_exec = fl["seg_map_kernel"] + fl["seg_chain_kernel"] + fl["seg_out_kernel"] * ndir   # per call
         for k in fl:
             if k in kern:
                 kern[k]["tflops"] = fl[k] / (kern[k]["avg_ms"] / 1e3) / 1e12

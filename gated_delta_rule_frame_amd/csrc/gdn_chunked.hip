@@ -58,6 +58,7 @@ namespace {
 constexpr int CH = 64;          // sub-chunk tokens
 constexpr int LDT = CH + 8;     // row stride (elements) of token-contracted fp16 matrices
 constexpr int LDD = 24;         // row stride of the diagonal inverse blocks
+constexpr int ADB = 260;        // float stride of the fp32 diagonal blocks of A (16 x 16 + pad)
 constexpr int NTC = 256;        // threads per workgroup of the chain kernel
 constexpr int NWC = NTC / 64;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -79,6 +80,8 @@ struct Args {
   long long T;
   int B, H, L, NS;
   int dirs;             // bit 0: forward scan, bit 1: reversed scan
+  int dir;              // output kernel: the scan direction of this launch (1: reversed)
+  int mode;             // output kernel: 0 store outputs, 1 store the partial, 2 add the partial
   int out_bf16;
   float c;              // key scale
 };
@@ -105,10 +108,11 @@ struct Geo {
   static constexpr int LDK = DP + 8;             // row stride of d-contracted fp16 rows
 };
 
-// Shared memory.  Two sub-chunk buffers (Q and K rows, K^T, P, gate factors)
-// alternate between "being computed on" and "being staged"; the inverse and
-// the A matrix are single-buffered (their producer and consumer phases are
-// separated by a barrier).  OUT: output pass (else map pass: no Q, no P).
+// Shared memory.  Two sub-chunk buffers (Q and K rows, K^T, P, the inverse,
+// gate factors) alternate between "being computed on" and "being prepared";
+// the A matrix and the helper's diagonal blocks are single-buffered (their
+// producer and consumer phases are separated by a barrier).  OUT: output pass
+// (else map pass: no Q, no P).
 template <int D, bool OUT>
 struct Lay {
   using G = Geo<D>;
@@ -116,25 +120,26 @@ struct Lay {
   static constexpr int KR = CH * G::LDK * 2;
   static constexpr int KT = D * LDT * 2;
   static constexpr int PP = OUT ? CH * LDT * 2 : 0;
+  static constexpr int TT = CH * LDT * 2;
   static constexpr int GT = 5 * CH * 4;
   static constexpr int o_qr = 0;
   static constexpr int o_kr = o_qr + QR;
   static constexpr int o_kt = o_kr + KR;
   static constexpr int o_pp = o_kt + KT;
-  static constexpr int o_gt = o_pp + PP;
+  static constexpr int o_tt = o_pp + PP;               // Tm diag(beta), fp16 rows
+  static constexpr int o_gt = o_tt + TT;
   static constexpr int BUF = o_gt + GT;
-  static constexpr int o_tt = 2 * BUF;                 // Tm diag(beta), fp16 rows
-  static constexpr int o_ao = o_tt + CH * LDT * 2;     // off-diagonal blocks of A, fp16 rows
+  static constexpr int o_ao = 2 * BUF;                 // off-diagonal blocks of A, fp16 rows
   static constexpr int o_td = o_ao + CH * LDT * 2;     // diagonal blocks of Tm, fp16 rows
   static constexpr int o_ad = o_td + CH * LDD * 2;     // diagonal blocks of A, fp32
-  static constexpr int BYTES = o_ad + 4 * 16 * 16 * 4;
+  static constexpr int BYTES = o_ad + 4 * ADB * 4;
   static_assert(BYTES <= 160 * 1024, "workgroup LDS budget exceeded");
   static_assert(QR % 16 == 0 && KR % 16 == 0 && KT % 16 == 0 && PP % 16 == 0 && BUF % 16 == 0, "alignment");
 };
 
 // One sub-chunk buffer.
 struct Buf {
-  hb *qr, *kr, *kt, *pp;
+  hb *qr, *kr, *kt, *pp, *tt;
   float *g2, *eg, *ce, *dn, *bt;   // cumsum (log2), e^G, c e^G, c e^{G_n - G}, beta
 };
 
@@ -156,6 +161,7 @@ __device__ __forceinline__ Buf buf_at(char* s, int i) {
   b.kr = reinterpret_cast<hb*>(p + L::o_kr);
   b.kt = reinterpret_cast<hb*>(p + L::o_kt);
   b.pp = reinterpret_cast<hb*>(p + L::o_pp);
+  b.tt = reinterpret_cast<hb*>(p + L::o_tt);
   float* gt = reinterpret_cast<float*>(p + L::o_gt);
   b.g2 = gt;
   b.eg = gt + CH;
@@ -167,7 +173,7 @@ __device__ __forceinline__ Buf buf_at(char* s, int i) {
 
 // Single-buffered arrays of the inverse.
 struct Inv {
-  hb *tt, *ao, *td;
+  hb *ao, *td;
   float* ad;
 };
 
@@ -176,7 +182,6 @@ __device__ __forceinline__ Inv inv_at(char* s0) {
   using L = Lay<D, OUT>;
   char* s = lds_at(s0, 0u);
   Inv v;
-  v.tt = reinterpret_cast<hb*>(s + L::o_tt);
   v.ao = reinterpret_cast<hb*>(s + L::o_ao);
   v.td = reinterpret_cast<hb*>(s + L::o_td);
   v.ad = reinterpret_cast<float*>(s + L::o_ad);
@@ -197,8 +202,12 @@ __device__ __forceinline__ void store4_h(hb* dst, float a, float b, float c, flo
 // operand of a 16x16x32 product whose k order is {4g..4g+3, 16+4g..16+4g+3}
 // for lane group g; the A operand is then read from LDS in that same order.
 
-__device__ __forceinline__ f16x4_t ld4(const hb* p) { return *reinterpret_cast<const f16x4_t*>(p); }
-__device__ __forceinline__ f16x8_t ld8(const hb* p) { return *reinterpret_cast<const f16x8_t*>(p); }
+// Fragment halves are read with one ds_read_b64 each.  The loads are volatile
+// only so that the compiler does not pair them into ds_read2_b64: measured on
+// gfx950, a 16-row fragment read as two ds_read_b64 occupies the LDS for 4
+// cycles, the same data as one ds_read2_b64 for 16 (bank conflicts).
+typedef __attribute__((address_space(3))) const volatile f16x4_t lds_f16x4_t;
+__device__ __forceinline__ f16x4_t ld4(const hb* p) { return *(lds_f16x4_t*)(p); }
 __device__ __forceinline__ f16x8_t cat8(f16x4_t x, f16x4_t y) {
   return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
 }
@@ -251,6 +260,9 @@ __device__ __forceinline__ Sub make_sub(long long t0, int n, bool rev) {
 }
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+// Note: with this toolchain __builtin_bit_cast of a vector element
+// (bit_cast<T>(v[i])) yields element 0 for every i; only whole vectors are
+// bit-cast here.
 
 // Raw buffer over the n rows [t0, t0 + n) of a token-major tensor, starting at
 // one head's first element.  Offsets past the n rows (and the wrapped
@@ -340,16 +352,30 @@ __device__ __forceinline__ void stage_kq(const Buf& B, const StageKQ& st) {
         static_cast<uint32_t>(e0[u]) | (static_cast<uint32_t>(e1[u]) << 16);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wavefront with DPP moves: a
+// Hillis-Steele scan inside each row of 16 lanes (shifts 1, 2, 4, 8), then
+// row 0's total into row 1, row 2's into row 3 (broadcast of lane 15 / 47),
+// and the sum of rows 0-1 into rows 2-3 (broadcast of lane 31).
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+  int v = __builtin_bit_cast(int, x);
+#define GDN_DPP_ADD(ctrl, rmask, bz)                                                                   \
+  v = __builtin_bit_cast(int, __builtin_bit_cast(float, v) +                                          \
+                                  __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, ctrl, rmask, 0xf, bz)))
+  GDN_DPP_ADD(0x111, 0xf, true);    // row_shr:1 (lanes without a source read 0)
+  GDN_DPP_ADD(0x112, 0xf, true);    // row_shr:2
+  GDN_DPP_ADD(0x114, 0xf, true);    // row_shr:4
+  GDN_DPP_ADD(0x118, 0xf, true);    // row_shr:8
+  GDN_DPP_ADD(0x142, 0xa, false);   // row_bcast:15 into rows 1 and 3 (other rows add 0)
+  GDN_DPP_ADD(0x143, 0xc, false);   // row_bcast:31 into rows 2 and 3
+#undef GDN_DPP_ADD
+  return __builtin_bit_cast(float, v);
+}
+
 // The scan-order gate cumsum in log2 units and the per-token factors (helper).
 __device__ __forceinline__ void stage_gates(const Buf& B, const StageG& st, float c) {
   const int i = threadIdx.x & 63;
-  float s = st.g * kLog2e;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const float t = __shfl_up(s, d);
-    if (i >= d) s += t;
-  }
-  const float last = __shfl(s, 63);
+  const float s = wave_prefix_sum(st.g * kLog2e);
+  const float last = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), 63));
   const float e = ex2(s);
   B.g2[i] = s;
   B.eg[i] = e;
@@ -357,6 +383,8 @@ __device__ __forceinline__ void stage_gates(const Buf& B, const StageG& st, floa
   B.dn[i] = c * ex2(last - s);
   B.bt[i] = st.b;
 }
+
+__device__ void tinv_diag(const Inv& I, const Buf& B);
 
 // --- Gram tiles -------------------------------------------------------------------
 // Tile (ta, tb), ta <= tb, of the products of the K rows of block ta with the
@@ -368,8 +396,9 @@ __device__ __forceinline__ f32x4 gram_tile(const hb* kr, const hb* xr, int ta, i
   const hb* arow = kr + (16 * ta + cl) * G::LDK;
   const hb* brow = xr + (16 * tb + cl) * G::LDK;
   f32x4 acc = zero4();
+  // both operands in the same (permuted) k order, two 8-byte reads each
 #pragma unroll
-  for (int p = 0; p < G::NP; ++p) acc = mfma32(ld8(arow + 32 * p + 8 * g), ld8(brow + 32 * p + 8 * g), acc);
+  for (int p = 0; p < G::NP; ++p) acc = mfma32(fragA2(arow, 2 * p, g), fragA2(brow, 2 * p, g), acc);
   return acc;
 }
 
@@ -382,14 +411,13 @@ __device__ __forceinline__ void tile_pair(int t, int& a, int& b) {
   b = B[t];
 }
 
-// A of sub-chunk B (diagonal blocks fp32 by the helper, off-diagonal blocks
-// fp16 by the strip waves) and, for the output pass, P = c tril(Q K^T) * E.
-template <int D, bool OUT>
-__device__ void gram_stage(const Args& a, const Buf& B, const Inv& I) {
-  using G = Geo<D>;
-  const int wave = wave_id(), lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
+// Helper: the diagonal 16x16 blocks of A of sub-chunk B (fp32), then their
+// inverses.
+template <int D>
+__device__ void gram_stage_helper(const Args& a, const Buf& B, const Inv& I) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
   const float c2 = a.c * a.c;
-  if (wave == G::HW) {
+  {
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
       const f32x4 s = gram_tile<D>(B.kr, B.kr, blk, blk, cl, g);
@@ -401,10 +429,20 @@ __device__ void gram_stage(const Args& a, const Buf& B, const Inv& I) {
       v.y = (x > y0 + 1) ? bx * s[1] * ex2(gx - gy[1]) : 0.f;
       v.z = (x > y0 + 2) ? bx * s[2] * ex2(gx - gy[2]) : 0.f;
       v.w = (x > y0 + 3) ? bx * s[3] * ex2(gx - gy[3]) : 0.f;
-      *reinterpret_cast<float4*>(I.ad + blk * 256 + cl * 16 + 4 * g) = v;
+      *reinterpret_cast<float4*>(I.ad + blk * ADB + cl * 16 + 4 * g) = v;
     }
-    return;
+    wave_lds_sync();
+    tinv_diag(I, B);
   }
+}
+
+// Strip waves: the off-diagonal blocks of A (fp16) and, for the output pass,
+// P = c tril(Q K^T) * E.
+template <int D, bool OUT>
+__device__ void gram_stage_strips(const Args& a, const Buf& B, const Inv& I) {
+  using G = Geo<D>;
+  const int wave = wave_id(), lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
+  const float c2 = a.c * a.c;
   constexpr int NTILE = OUT ? 16 : 6;
   for (int t = wave; t < NTILE; t += G::NSW) {
     const bool isp = t >= 6;
@@ -428,14 +466,42 @@ __device__ void gram_stage(const Args& a, const Buf& B, const Inv& I) {
 }
 
 // --- triangular inverse (helper wavefront) ------------------------------------------
-// Tm = (I + A)^-1 of sub-chunk B into I.tt as Tm diag(beta) (fp16 rows).
-// Diagonal 16x16 blocks: lane (block g, row i) solves row i of
-// T_gg (I + A_gg) = I from the last column to the first, in fp32.
-// Off-diagonal blocks, level by level:
+// Tm = (I + A)^-1 of sub-chunk B into B.tt as Tm diag(beta) (fp16 rows), in
+// two parts run in different phases:
+// tinv_diag: diagonal 16x16 blocks; lane (block g, row i) solves row i of
+//   T_gg (I + A_gg) = I from the last column to the first, in fp32.
+// tinv_offdiag: off-diagonal blocks, level by level,
 //   T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj,
-// with every T_kj kept in registers in accumulator layout (fp16), so the
-// levels need no LDS round trip.
-__device__ __forceinline__ f16x4_t tinv_block(const Inv& I, const float* bt, int i, int j, f16x8_t p0, bool two,
+//   with every T_kj kept in registers in accumulator layout (fp16), so the
+//   levels need no LDS round trip.
+__device__ void tinv_diag(const Inv& I, const Buf& B) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
+  const float* Ab = I.ad + g * ADB;
+  float s[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) s[j] = (j == cl) ? 1.f : 0.f;
+#pragma unroll
+  for (int k = 15; k >= 1; --k) {
+    const float tk = s[k];
+#pragma unroll
+    for (int q = 0; 4 * q < k; ++q) {
+      const f32x4 a4 = ld4f(Ab + k * 16 + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (4 * q + e < k) s[4 * q + e] = fmaf(-tk, a4[e], s[4 * q + e]);
+    }
+  }
+  hb* tdr = I.td + (16 * g + cl) * LDD;
+  hb* ttr = B.tt + (16 * g + cl) * LDT + 16 * g;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const f32x4 bb = ld4f(B.bt + 16 * g + 4 * q);
+    store4_h(tdr + 4 * q, s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]);
+    store4_h(ttr + 4 * q, s[4 * q] * bb[0], s[4 * q + 1] * bb[1], s[4 * q + 2] * bb[2], s[4 * q + 3] * bb[3]);
+  }
+}
+
+__device__ __forceinline__ f16x4_t tinv_block(const Inv& I, const Buf& B, int i, int j, f16x8_t p0, bool two,
                                               f16x8_t p1, int cl, int g) {
   const hb* arow = I.ao + (16 * i + cl) * LDT + 16 * j;
   f32x4 m = mfma32(fragA2(arow, 0, g), p0, zero4());
@@ -444,52 +510,14 @@ __device__ __forceinline__ f16x4_t tinv_block(const Inv& I, const float* bt, int
   const f16x4_t tii = ld4(I.td + (16 * i + cl) * LDD + 4 * g);
   const f32x4 tc = mfma16(tii, mh);          // T_ii M: lane holds [4g + r][cl]
   const f32x4 tr = mfma16(mh, tii);          // (T_ii M)^T: lane holds [cl][4g + r]
-  const f32x4 bb = ld4f(bt + 16 * j + 4 * g);
-  store4_h(I.tt + (16 * i + cl) * LDT + 16 * j + 4 * g, -tr[0] * bb[0], -tr[1] * bb[1], -tr[2] * bb[2],
+  const f32x4 bb = ld4f(B.bt + 16 * j + 4 * g);
+  store4_h(B.tt + (16 * i + cl) * LDT + 16 * j + 4 * g, -tr[0] * bb[0], -tr[1] * bb[1], -tr[2] * bb[2],
            -tr[3] * bb[3]);
   return tof16(-tc);
 }
 
-__device__ void tinv(const Inv& I, const float* bt) {
+__device__ void tinv_offdiag(const Inv& I, const Buf& B) {
   const int lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
-  {
-    const float* Ab = I.ad + g * 256;
-    float one = 1.f;
-    asm volatile("" : "+v"(one));   // keep the identity row from being hoisted out of the caller's loop
-    float s[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) s[j] = (j == cl) ? one : 0.f;
-#pragma unroll
-    for (int k = 15; k >= 1; --k) {
-      __builtin_amdgcn_sched_barrier(0);
-      const float tk = s[k];
-#pragma unroll
-      for (int q = 0; 4 * q < k; ++q) {
-        const f32x4 a4 = ld4f(Ab + k * 16 + 4 * q);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (4 * q + e < k) s[4 * q + e] = fmaf(-tk, a4[e], s[4 * q + e]);
-      }
-    }
-    float bb[16];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x4 v = ld4f(bt + 16 * g + 4 * q);
-      bb[4 * q] = v[0];
-      bb[4 * q + 1] = v[1];
-      bb[4 * q + 2] = v[2];
-      bb[4 * q + 3] = v[3];
-    }
-    hb* tdr = I.td + (16 * g + cl) * LDD;
-    hb* ttr = I.tt + (16 * g + cl) * LDT + 16 * g;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      store4_h(tdr + 4 * q, s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]);
-      store4_h(ttr + 4 * q, s[4 * q] * bb[4 * q], s[4 * q + 1] * bb[4 * q + 1], s[4 * q + 2] * bb[4 * q + 2],
-               s[4 * q + 3] * bb[4 * q + 3]);
-    }
-  }
-  wave_lds_sync();
   // diagonal blocks 0..2 in accumulator layout (lane: rows 4g + r, column cl)
   f16x4_t d[3];
 #pragma unroll
@@ -498,12 +526,12 @@ __device__ void tinv(const Inv& I, const float* bt) {
     for (int r = 0; r < 4; ++r) d[j][r] = __builtin_bit_cast(_Float16, I.td[(16 * j + 4 * g + r) * LDD + cl]);
   }
   const f16x4_t z = zero_h4();
-  const f16x4_t t10 = tinv_block(I, bt, 1, 0, cat8(d[0], z), false, cat8(z, z), cl, g);
-  const f16x4_t t21 = tinv_block(I, bt, 2, 1, cat8(d[1], z), false, cat8(z, z), cl, g);
-  (void)tinv_block(I, bt, 3, 2, cat8(d[2], z), false, cat8(z, z), cl, g);
-  const f16x4_t t20 = tinv_block(I, bt, 2, 0, cat8(d[0], t10), false, cat8(z, z), cl, g);
-  (void)tinv_block(I, bt, 3, 1, cat8(d[1], t21), false, cat8(z, z), cl, g);
-  (void)tinv_block(I, bt, 3, 0, cat8(d[0], t10), true, cat8(t20, z), cl, g);
+  const f16x4_t t10 = tinv_block(I, B, 1, 0, cat8(d[0], z), false, cat8(z, z), cl, g);
+  const f16x4_t t21 = tinv_block(I, B, 2, 1, cat8(d[1], z), false, cat8(z, z), cl, g);
+  (void)tinv_block(I, B, 3, 2, cat8(d[2], z), false, cat8(z, z), cl, g);
+  const f16x4_t t20 = tinv_block(I, B, 2, 0, cat8(d[0], t10), false, cat8(z, z), cl, g);
+  (void)tinv_block(I, B, 3, 1, cat8(d[1], t21), false, cat8(z, z), cl, g);
+  (void)tinv_block(I, B, 3, 0, cat8(d[0], t10), true, cat8(t20, z), cl, g);
 }
 
 // --- strip-wave products ----------------------------------------------------------
@@ -526,7 +554,6 @@ __device__ __forceinline__ void rows_times_state(const hb* rows, const f16x8_t (
   using G = Geo<D>;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < SPW; ++j) acc[j][mt] = zero4();
     const hb* arow = rows + (16 * mt + cl) * G::LDK;
@@ -547,7 +574,6 @@ __device__ __forceinline__ void tri_times(const hb* M, const f16x8_t (&vp)[SPW][
                                           f32x4 (&acc)[SPW][4]) {
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
-    __builtin_amdgcn_sched_barrier(0);
     const hb* arow = M + (16 * mt + cl) * LDT;
 #pragma unroll
     for (int p = 0; 2 * p <= mt; ++p) {
@@ -558,6 +584,32 @@ __device__ __forceinline__ void tri_times(const hb* M, const f16x8_t (&vp)[SPW][
   }
 }
 
+// Transposed products for the outputs: out[mt] (+)= (rows x strip)^T, i.e.
+// lane (g, cl) receives row 16 mt + cl, strip columns 4g .. 4g + 3 (the state or
+// V' tiles are the A operand, the LDS rows the B operand), so that each lane
+// stores four consecutive columns of one token.
+template <int D>
+__device__ __forceinline__ void state_times_rows_T(const hb* rows, const f16x8_t (&Xp)[Geo<D>::NP], int cl, int g,
+                                                   f32x4 (&acc)[4]) {
+  using G = Geo<D>;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    acc[mt] = zero4();
+    const hb* brow = rows + (16 * mt + cl) * G::LDK;
+#pragma unroll
+    for (int p = 0; p < G::NP; ++p) acc[mt] = mfma32(Xp[p], fragA2(brow, 2 * p, g), acc[mt]);
+  }
+}
+
+__device__ __forceinline__ void tri_times_T(const hb* M, const f16x8_t (&vp)[2], int cl, int g, f32x4 (&acc)[4]) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const hb* brow = M + (16 * mt + cl) * LDT;
+#pragma unroll
+    for (int p = 0; 2 * p <= mt; ++p) acc[mt] = mfma32(vp[p], fragA2(brow, 2 * p, g), acc[mt]);
+  }
+}
+
 // X[j] <- dec X[j] + K^T vs[j]  (vs: fp16 pairs of token-row tiles).
 template <int D, int SPW>
 __device__ __forceinline__ void state_update(const hb* kt, const f16x8_t (&vs)[SPW][2], float dec, int cl, int g,
@@ -565,7 +617,6 @@ __device__ __forceinline__ void state_update(const hb* kt, const f16x8_t (&vs)[S
   using G = Geo<D>;
 #pragma unroll
   for (int md = 0; md < G::MD; ++md) {
-    __builtin_amdgcn_sched_barrier(0);
     const hb* arow = kt + (16 * md + cl) * LDT;
     const f16x8_t a0 = fragA2(arow, 0, g), a1 = fragA2(arow, 2, g);
 #pragma unroll
@@ -660,7 +711,8 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_map_kernel(Args a) {
       fetch_kq<D, false>(a, b, h, s1b, sk);
     }
     __syncthreads();
-    gram_stage<D, false>(a, buf_at<D, false>(smem, 0), I);
+    if (helper) gram_stage_helper<D>(a, buf_at<D, false>(smem, 0), I);
+    else gram_stage_strips<D, false>(a, buf_at<D, false>(smem, 0), I);
     __syncthreads();
   }
   if (helper) {
@@ -670,9 +722,9 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_map_kernel(Args a) {
       const Inv I = inv_at<D, false>(smem);
       stage_gates(Bn, sg, a.c);
       fetch_gates(a, b, h, piece(c + 2), sg);
-      tinv(I, Bc.bt);
+      tinv_offdiag(I, Bc);
       __syncthreads();
-      if (c + 1 < nsub) gram_stage<D, false>(a, Bn, I);
+      if (c + 1 < nsub) gram_stage_helper<D>(a, Bn, I);
       __syncthreads();
     }
     return;
@@ -711,7 +763,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_map_kernel(Args a) {
       for (int j = 0; j < SPW; ++j)
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) Vn[j][mt] = zero4();
-      tri_times<SPW>(I.tt, Rh, cl, g, Vn);
+      tri_times<SPW>(Bc.tt, Rh, cl, g, Vn);
       f16x8_t Vs[SPW][2];
       const f32x4 d0 = ld4f(Bc.dn + 4 * g), d1 = ld4f(Bc.dn + 16 + 4 * g);
       const f32x4 d2 = ld4f(Bc.dn + 32 + 4 * g), d3 = ld4f(Bc.dn + 48 + 4 * g);
@@ -722,7 +774,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_map_kernel(Args a) {
       }
       state_update<D, SPW>(Bc.kt, Vs, Bc.eg[CH - 1], cl, g, X);
     }
-    if (c + 1 < nsub) gram_stage<D, false>(a, Bn, I);
+    if (c + 1 < nsub) gram_stage_strips<D, false>(a, Bn, I);
     __syncthreads();
   }
   // store X = [P | Q] (fp32, row-major [D][2D])
@@ -850,9 +902,10 @@ __global__ __launch_bounds__(NTC) void seg_chain_kernel(Args a) {
 // ---------------------------------------------------------------------------
 
 // ---------------------------------------------------------------------------
-// 3. Outputs.  grid (NS, B * H).  Each workgroup runs its segment for every
-// requested direction (reversed scan first) from the start states of the
-// chain; the reversed scan's outputs are summed into the forward scan's.
+// 3. Outputs.  grid (NS, B * H), one launch per requested direction (the
+// reversed scan first): each workgroup re-runs its segment from the start
+// state of the chain.  In a bidirectional call the reversed scan stores its
+// outputs as a partial that the forward scan's launch adds to its own.
 // Strip wave w owns state columns 16 w .. 16 w + 15.
 template <int D>
 __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
@@ -875,12 +928,10 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
 
   for (int i = threadIdx.x; i < L::BYTES / 16; i += G::NT) reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
 
-#pragma unroll 1
-  for (int pass = 0; pass < 2; ++pass) {
-    const int dir = pass == 0 ? 1 : 0;                 // reversed scan first
-    if (!(a.dirs & (1 << dir))) continue;
+  {
+    const int dir = a.dir;
     const bool rev = dir == 1;
-    const int mode = a.dirs == 3 ? (rev ? 1 : 2) : 0;   // 1: write partial, 2: add partial
+    const int mode = a.mode;
     const int slot = slot_of_dir(a.dirs, dir);
     const int pos = rev ? a.NS - 1 - seg : seg;
     f32x4 H[SPW][MD];
@@ -917,7 +968,8 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
         fetch_kq<D, true>(a, b, h, s1b, sk);
       }
       __syncthreads();
-      gram_stage<D, true>(a, buf_at<D, true>(smem, 0), I);
+      if (helper) gram_stage_helper<D>(a, buf_at<D, true>(smem, 0), I);
+      else gram_stage_strips<D, true>(a, buf_at<D, true>(smem, 0), I);
       __syncthreads();
     }
     if (helper) {
@@ -927,27 +979,40 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
       const Inv I = inv_at<D, true>(smem);
         stage_gates(Bn, sg, a.c);
         fetch_gates(a, b, h, piece(c + 2), sg);
-        tinv(I, Bc.bt);
+        tinv_offdiag(I, Bc);
         __syncthreads();
-        if (c + 1 < nsub) gram_stage<D, true>(a, Bn, I);
+        if (c + 1 < nsub) gram_stage_helper<D>(a, Bn, I);
         __syncthreads();
       }
-      continue;
+      return;
     }
-    f32x4 QH[SPW][4], R[SPW][4];
-    float pre[4][4];
+    f32x4 R[SPW][4];
+    f32x4 pre[4];
     for (int c = 0; c < nsub; ++c) {
       const Buf Bc = buf_at<D, true>(smem, c & 1), Bn = buf_at<D, true>(smem, (c + 1) & 1);
       const Inv I = inv_at<D, true>(smem);
       const Sub sb = piece(c);
-      const int lo = (sb.r0 + sb.sgn * 4 * g) * (int)HD + col;   // per-lane element offset from row t0
-      // alpha
+      // per-lane element offset (from row t0) of the first output row, strip columns 4g ..
+      const int lo = (sb.r0 + sb.sgn * cl) * (int)HD + 16 * wave + 4 * g;
+      const long long rowb = ((long long)b * a.T + sb.t0) * HD + (long long)h * D;
+      // alpha.  The reversed scan's partial (forward pass of a bidirectional
+      // call; else an empty buffer) is loaded first: the load counter drains in
+      // issue order, so loads issued before the prefetches can be waited for
+      // without waiting for the prefetches.
+      {
+        const __amdgpu_buffer_rsrc_t rs = rows_rsrc(a.acc + rowb, mode == 2 ? (long long)sb.n * HD * 4 : 0);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const u32x4_t v =
+              __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)((lo + sb.sgn * 16 * mt * (int)HD) * 4), 0, 0);
+          pre[mt] = __builtin_bit_cast(f32x4, v);   // whole-vector casts only: see the note on vector elements
+        }
+      }
       stage_kq<D, true>(Bn, sk);
       fetch_kq<D, true>(a, b, h, piece(c + 2), sk);
       {
         f16x8_t Hp[SPW][G::NP];
         state_pairs<D>(H[0], Hp[0]);
-        rows_times_state<D, SPW>(Bc.qr, Hp, cl, g, QH);
         rows_times_state<D, SPW>(Bc.kr, Hp, cl, g, R);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) R[0][mt] = vals_tile(Vr, mt) - ld4f(Bc.ce + 16 * mt + 4 * g) * R[0][mt];
@@ -956,15 +1021,11 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
       __syncthreads();
       // beta
       {
-        const long long rowb = ((long long)b * a.T + sb.t0) * HD + (long long)h * D;
-        {   // reversed scan's partial (forward pass of a bidirectional call; else an empty buffer)
-          const __amdgpu_buffer_rsrc_t rs = rows_rsrc(a.acc + rowb, mode == 2 ? (long long)sb.n * HD * 4 : 0);
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              pre[mt][r] = __builtin_bit_cast(
-                  float, __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)((lo + sb.sgn * (16 * mt + r) * (int)HD) * 4), 0, 0));
+        f32x4 O[4];   // outputs, transposed tiles (lane: token 16 mt + cl, columns 4g ..)
+        {
+          f16x8_t Hp[G::NP];
+          state_pairs<D>(H[0], Hp);
+          state_times_rows_T<D>(Bc.qr, Hp, cl, g, O);
         }
         f16x8_t Rh[SPW][2];
         Rh[0][0] = tof16x8(R[0][0], R[0][1]);
@@ -972,13 +1033,13 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
         f32x4 Vn[SPW][4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) Vn[0][mt] = zero4();
-        tri_times<SPW>(I.tt, Rh, cl, g, Vn);
+        tri_times<SPW>(Bc.tt, Rh, cl, g, Vn);
         f16x8_t Vh[SPW][2];
         Vh[0][0] = tof16x8(Vn[0][0], Vn[0][1]);
         Vh[0][1] = tof16x8(Vn[0][2], Vn[0][3]);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) QH[0][mt] = ld4f(Bc.eg + 16 * mt + 4 * g) * QH[0][mt];
-        tri_times<SPW>(Bc.pp, Vh, cl, g, QH);
+        for (int mt = 0; mt < 4; ++mt) O[mt] = Bc.eg[16 * mt + cl] * O[mt];
+        tri_times_T(Bc.pp, Vh[0], cl, g, O);
         f16x8_t Vs[SPW][2];
         const f32x4 d0 = ld4f(Bc.dn + 4 * g), d1 = ld4f(Bc.dn + 16 + 4 * g);
         const f32x4 d2 = ld4f(Bc.dn + 32 + 4 * g), d3 = ld4f(Bc.dn + 48 + 4 * g);
@@ -992,20 +1053,21 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
           const long long esz = half ? 2 : 4;
           const __amdgpu_buffer_rsrc_t rs = rows_rsrc(static_cast<char*>(dst) + rowb * esz, (long long)sb.n * HD * esz);
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const uint32_t off = (uint32_t)((lo + sb.sgn * (16 * mt + r) * (int)HD) * esz);
-              float val = QH[0][mt][r];
-              val += pre[mt][r];
-              if (half)
-                __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f32_to_bf16_bits(val), rs, off, 0, 0);
-              else
-                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), rs, off, 0, 0);
+          for (int mt = 0; mt < 4; ++mt) {
+            const uint32_t off = (uint32_t)((lo + sb.sgn * 16 * mt * (int)HD) * esz);
+            const f32x4 val = O[mt] + pre[mt];
+            if (half) {
+              typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+              const u32x2_t w{f32_to_bf16_bits(val[0]) | ((uint32_t)f32_to_bf16_bits(val[1]) << 16),
+                              f32_to_bf16_bits(val[2]) | ((uint32_t)f32_to_bf16_bits(val[3]) << 16)};
+              __builtin_amdgcn_raw_buffer_store_b64(w, rs, off, 0, 0);
+            } else {
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, val), rs, off, 0, 0);
             }
+          }
         }
       }
-      if (c + 1 < nsub) gram_stage<D, true>(a, Bn, I);
+      if (c + 1 < nsub) gram_stage_strips<D, true>(a, Bn, I);
       __syncthreads();
     }
     // final state: the scan's last segment
@@ -1088,10 +1150,16 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   prof_end(stream, GDN_KERNEL_SEG_CHAIN);
-  prof_begin(stream, GDN_KERNEL_SEG_OUT);
-  hipLaunchKernelGGL((seg_out_kernel<D>), dim3(pl.NS, bhc, 1), dim3(Geo<D>::NT), 0, stream, a);
-  e = hipGetLastError();
-  prof_end(stream, GDN_KERNEL_SEG_OUT);
+  for (int dir = 1; dir >= 0; --dir) {   // reversed scan first
+    if (!(pl.dirs & (1 << dir))) continue;
+    a.dir = dir;
+    a.mode = pl.dirs == 3 ? (dir == 1 ? 1 : 2) : 0;
+    prof_begin(stream, GDN_KERNEL_SEG_OUT);
+    hipLaunchKernelGGL((seg_out_kernel<D>), dim3(pl.NS, bhc, 1), dim3(Geo<D>::NT), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    prof_end(stream, GDN_KERNEL_SEG_OUT);
+  }
   return e;
 }
 
