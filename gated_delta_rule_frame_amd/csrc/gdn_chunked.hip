@@ -59,8 +59,6 @@ constexpr int CH = 64;          // sub-chunk tokens
 constexpr int LDT = CH + 8;     // row stride (elements) of token-contracted fp16 matrices
 constexpr int LDD = 24;         // row stride of the diagonal inverse blocks
 constexpr int ADB = 260;        // float stride of the fp32 diagonal blocks of A (16 x 16 + pad)
-constexpr int NTC = 256;        // threads per workgroup of the chain kernel
-constexpr int NWC = NTC / 64;
 constexpr float kLog2e = 1.4426950408889634f;
 
 std::atomic<int> g_segment_override{0};
@@ -553,17 +551,18 @@ __device__ __forceinline__ void rows_times_state(const hb* rows, const f16x8_t (
                                                  f32x4 (&acc)[SPW][4]) {
   using G = Geo<D>;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int j = 0; j < SPW; ++j) acc[j][mt] = zero4();
-    const hb* arow = rows + (16 * mt + cl) * G::LDK;
+  // k-pair outer, tile inner: consecutive MFMAs update different accumulators
 #pragma unroll
-    for (int p = 0; p < G::NP; ++p) {
-      const f16x8_t a = fragA2(arow, 2 * p, g);
+  for (int p = 0; p < G::NP; ++p)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const f16x8_t a = fragA2(rows + (16 * mt + cl) * G::LDK, 2 * p, g);
 #pragma unroll
       for (int j = 0; j < SPW; ++j) acc[j][mt] = mfma32(a, Xp[j][p], acc[j][mt]);
     }
-  }
 }
 
 // out[j][mt] (+)= lower-triangular token matrix M (fp16 rows, zero above the
@@ -573,15 +572,13 @@ template <int SPW>
 __device__ __forceinline__ void tri_times(const hb* M, const f16x8_t (&vp)[SPW][2], int cl, int g,
                                           f32x4 (&acc)[SPW][4]) {
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const hb* arow = M + (16 * mt + cl) * LDT;
+  for (int p = 0; p < 2; ++p)
 #pragma unroll
-    for (int p = 0; 2 * p <= mt; ++p) {
-      const f16x8_t a = fragA2(arow, 2 * p, g);
+    for (int mt = 2 * p; mt < 4; ++mt) {
+      const f16x8_t a = fragA2(M + (16 * mt + cl) * LDT, 2 * p, g);
 #pragma unroll
       for (int j = 0; j < SPW; ++j) acc[j][mt] = mfma32(a, vp[j][p], acc[j][mt]);
     }
-  }
 }
 
 // Transposed products for the outputs: out[mt] (+)= (rows x strip)^T, i.e.
@@ -593,21 +590,18 @@ __device__ __forceinline__ void state_times_rows_T(const hb* rows, const f16x8_t
                                                    f32x4 (&acc)[4]) {
   using G = Geo<D>;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    acc[mt] = zero4();
-    const hb* brow = rows + (16 * mt + cl) * G::LDK;
+  for (int mt = 0; mt < 4; ++mt) acc[mt] = zero4();
 #pragma unroll
-    for (int p = 0; p < G::NP; ++p) acc[mt] = mfma32(Xp[p], fragA2(brow, 2 * p, g), acc[mt]);
-  }
+  for (int p = 0; p < G::NP; ++p)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma32(Xp[p], fragA2(rows + (16 * mt + cl) * G::LDK, 2 * p, g), acc[mt]);
 }
 
 __device__ __forceinline__ void tri_times_T(const hb* M, const f16x8_t (&vp)[2], int cl, int g, f32x4 (&acc)[4]) {
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const hb* brow = M + (16 * mt + cl) * LDT;
+  for (int p = 0; p < 2; ++p)
 #pragma unroll
-    for (int p = 0; 2 * p <= mt; ++p) acc[mt] = mfma32(vp[p], fragA2(brow, 2 * p, g), acc[mt]);
-  }
+    for (int mt = 2 * p; mt < 4; ++mt) acc[mt] = mfma32(vp[p], fragA2(M + (16 * mt + cl) * LDT, 2 * p, g), acc[mt]);
 }
 
 // X[j] <- dec X[j] + K^T vs[j]  (vs: fp16 pairs of token-row tiles).
@@ -616,17 +610,17 @@ __device__ __forceinline__ void state_update(const hb* kt, const f16x8_t (&vs)[S
                                              f32x4 (&X)[SPW][Geo<D>::MD]) {
   using G = Geo<D>;
 #pragma unroll
-  for (int md = 0; md < G::MD; ++md) {
-    const hb* arow = kt + (16 * md + cl) * LDT;
-    const f16x8_t a0 = fragA2(arow, 0, g), a1 = fragA2(arow, 2, g);
+  for (int md = 0; md < G::MD; ++md)
 #pragma unroll
-    for (int j = 0; j < SPW; ++j) {
-      f32x4 acc = X[j][md] * dec;
-      acc = mfma32(a0, vs[j][0], acc);
-      acc = mfma32(a1, vs[j][1], acc);
-      X[j][md] = acc;
+    for (int j = 0; j < SPW; ++j) X[j][md] = X[j][md] * dec;
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int md = 0; md < G::MD; ++md) {
+      const f16x8_t a = fragA2(kt + (16 * md + cl) * LDT, 2 * q, g);
+#pragma unroll
+      for (int j = 0; j < SPW; ++j) X[j][md] = mfma32(a, vs[j][q], X[j][md]);
     }
-  }
 }
 
 // Value column `col` of the sub-chunk's rows in accumulator layout, kept as
@@ -790,116 +784,151 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_map_kernel(Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// 2. Segment chain.  grid (DV / 16, B * H, ndir).  H_{p+1} = P_p H_p + Q_p on
-// one 16-column tile of the state, fp32 carried in registers; products in
-// split bf16 (x = hi + lo, hi*hi + hi*lo + lo*hi).
+// 2. Segment chain.  grid (B * H, ndir), one workgroup of MD wavefronts per
+// head and direction: H_{p+1} = P_p H_p + Q_p over the segments in scan order,
+// i.e. the prefix composition of the segments' affine maps.  Wavefront w
+// carries state columns 16 w .. 16 w + 15 in fp32 registers.  Each step the
+// map P_p is staged once into LDS as split bf16 (x = hi + lo) and the product
+// is formed as hi*hi + hi*lo + lo*hi with fp32 accumulation (about 16
+// significant bits per operand); the next map is loaded meanwhile.
 template <int D>
-__global__ __launch_bounds__(NTC) void seg_chain_kernel(Args a) {
-  constexpr int DK = D, DV = D;
-  constexpr int MD = DK / 16, LDK = DK + 8, NXC = DK + DV;
-  constexpr int MSLOTS = (MD + NWC - 1) / NWC;
-  __shared__ __attribute__((aligned(16))) bh hhi[16 * LDK];
-  __shared__ __attribute__((aligned(16))) bh hlo[16 * LDK];
-  const int wave = wave_id(), lane = threadIdx.x & 63;
-  const int nv = blockIdx.x;
-  const int bh_ = blockIdx.y, b = bh_ / a.H, h = bh_ % a.H;
-  const int slot = blockIdx.z, dir = dir_of_slot(a.dirs, slot);
-  const float* seed = (dir == 0 || a.dirs == 2) ? a.h0 : nullptr;
-  const int col = nv * 16 + (lane & 15);
-  const size_t sbase = ((size_t)b * a.H + h) * DK * DV;
+struct ChainLay {
+  static constexpr int MD = D / 16;
+  static constexpr int DP = (D + 31) / 32 * 32;
+  static constexpr int NP = DP / 32;
+  static constexpr int LDC = DP + 8;             // row stride (elements) of a staged map
+  static constexpr int MAT = D * LDC * 2;        // one bf16 matrix
+  static constexpr int BYTES = 2 * 2 * MAT;      // (hi, lo) x double buffer
+  static_assert(BYTES <= 160 * 1024, "workgroup LDS budget exceeded");
+};
 
-  f32x4 hs[MSLOTS];
+typedef __attribute__((address_space(3))) const volatile s16x4_t lds_s16x4_t;
+__device__ __forceinline__ bf16x8_t fragB2(const bh* arow, int q, int g) {
+  const s16x4_t x = *(lds_s16x4_t*)(arow + 16 * q + 4 * g);
+  const s16x4_t y = *(lds_s16x4_t*)(arow + 16 * q + 16 + 4 * g);
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// fp32 tile -> (hi, lo) bf16 halves, each as 4 raw values
+__device__ __forceinline__ void split4(f32x4 v, s16x4_t& hi, s16x4_t& lo) {
 #pragma unroll
-  for (int s = 0; s < MSLOTS; ++s) {
-    const int md = wave + NWC * s;
-    const int row0 = md * 16 + 4 * (lane >> 4);
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      hs[s][r] = (md < MD && seed) ? seed[sbase + (size_t)(row0 + r) * DV + col] : 0.f;
-  }
-  float* st = a.starts + (((size_t)slot * a.B + b) * a.H + h) * (size_t)a.NS * DK * DV;
-  for (int p = 0;; ++p) {
-    // record the start state of segment p and publish H for the product
-#pragma unroll
-    for (int s = 0; s < MSLOTS; ++s) {
-      const int md = wave + NWC * s;
-      if (md < MD) {
-        const int row0 = md * 16 + 4 * (lane >> 4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) st[(size_t)p * DK * DV + (size_t)(row0 + r) * DV + col] = hs[s][r];
-        uint2 uh, ul;
-        bh hh[4], hl[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          hh[r] = f2bh(hs[s][r]);
-          hl[r] = f2bh(hs[s][r] - bh2f(hh[r]));
-        }
-        uh.x = hh[0] | ((uint32_t)hh[1] << 16);
-        uh.y = hh[2] | ((uint32_t)hh[3] << 16);
-        ul.x = hl[0] | ((uint32_t)hl[1] << 16);
-        ul.y = hl[2] | ((uint32_t)hl[3] << 16);
-        *reinterpret_cast<uint2*>(hhi + (lane & 15) * LDK + row0) = uh;
-        *reinterpret_cast<uint2*>(hlo + (lane & 15) * LDK + row0) = ul;
-      }
-    }
-    if (p == a.NS - 1) break;
-    __syncthreads();
-    const float* X = a.maps + ((((size_t)slot * a.B + b) * a.H + h) * (a.NS - 1) + p) * (size_t)DK * NXC;
-#pragma unroll
-    for (int s = 0; s < MSLOTS; ++s) {
-      const int md = wave + NWC * s;
-      if (md < MD) {
-        const int row0 = md * 16 + 4 * (lane >> 4);
-        f32x4 acc;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] = X[(size_t)(row0 + r) * NXC + DK + col];
-        const float* prow = X + (size_t)(md * 16 + (lane & 15)) * NXC;
-        const int g = lane >> 4;
-        int k = 0;
-#pragma unroll
-        for (; k + 32 <= DK; k += 32) {
-          const float4 v0 = *reinterpret_cast<const float4*>(prow + k + 8 * g);
-          const float4 v1 = *reinterpret_cast<const float4*>(prow + k + 8 * g + 4);
-          const float pv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-          bf16x8_t ahi, alo;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const __bf16 hi = static_cast<__bf16>(pv[e]);
-            ahi[e] = hi;
-            alo[e] = static_cast<__bf16>(pv[e] - static_cast<float>(hi));
-          }
-          const bf16x8_t bhi = *reinterpret_cast<const bf16x8_t*>(hhi + (lane & 15) * LDK + k + 8 * g);
-          const bf16x8_t blo = *reinterpret_cast<const bf16x8_t*>(hlo + (lane & 15) * LDK + k + 8 * g);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bhi, acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, blo, acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bhi, acc, 0, 0, 0);
-        }
-        if constexpr ((DK % 32) != 0) {
-          const float4 v0 = *reinterpret_cast<const float4*>(prow + k + 4 * g);
-          const float pv[4] = {v0.x, v0.y, v0.z, v0.w};
-          s16x4_t ahi, alo;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const bh hi = f2bh(pv[e]);
-            ahi[e] = (short)hi;
-            alo[e] = (short)f2bh(pv[e] - bh2f(hi));
-          }
-          const s16x4_t bhi = *reinterpret_cast<const s16x4_t*>(hhi + (lane & 15) * LDK + k + 4 * g);
-          const s16x4_t blo = *reinterpret_cast<const s16x4_t*>(hlo + (lane & 15) * LDK + k + 4 * g);
-          // K = 16 tail in its own accumulator (one MFMA shape per chain)
-          f32x4 tail = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, bhi, zero4(), 0, 0, 0);
-          tail = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, blo, tail, 0, 0, 0);
-          tail = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, bhi, tail, 0, 0, 0);
-          acc = acc + tail;
-        }
-        hs[s] = acc;
-      }
-    }
-    __syncthreads();
+  for (int r = 0; r < 4; ++r) {
+    const float x = v[r];
+    const bh h = f2bh(x);
+    hi[r] = (short)h;
+    lo[r] = (short)f2bh(x - bh2f(h));
   }
 }
 
-// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64 * (D / 16)) void seg_chain_kernel(Args a) {
+  using C = ChainLay<D>;
+  constexpr int MD = C::MD, NP = C::NP, LDC = C::LDC, NX = 2 * D, NTH = 64 * MD;
+  __shared__ __attribute__((aligned(16))) char smem[C::BYTES];
+  const int wave = wave_id(), lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
+  const int bh_ = blockIdx.x, b = bh_ / a.H, h = bh_ % a.H;
+  const int slot = blockIdx.y, dir = dir_of_slot(a.dirs, slot);
+  const float* seed = (dir == 0 || a.dirs == 2) ? a.h0 : nullptr;
+  const int col = 16 * wave + cl;
+  const uint32_t so = (uint32_t)((4 * g * D + col) * 4);        // lane offset within a [D][D] state
+  const uint32_t xo = (uint32_t)((4 * g * NX + D + col) * 4);   // lane offset of Q within a [D][2D] map
+  const float* maps = a.maps + (((size_t)slot * a.B + b) * a.H + h) * (size_t)(a.NS > 1 ? a.NS - 1 : 0) * D * NX;
+  float* starts = a.starts + (((size_t)slot * a.B + b) * a.H + h) * (size_t)a.NS * D * D;
+
+  for (int i = threadIdx.x; i < C::BYTES / 16; i += NTH) reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
+
+  f32x4 H[MD];
+  {
+    const __amdgpu_buffer_rsrc_t r = block_rsrc(seed ? seed + ((size_t)b * a.H + h) * D * D : starts, seed ? D * D * 4 : 0);
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) H[md][rr] = block_load(r, so, (uint32_t)((16 * md + rr) * D * 4));
+  }
+  const __amdgpu_buffer_rsrc_t st = block_rsrc(starts, (uint32_t)a.NS * D * D * 4);
+
+  // staging registers of one map: float4 number threadIdx.x + NTH i of P, and
+  // this lane's accumulator-layout tiles of Q
+  float4 pst[MD];
+  f32x4 qst[MD];
+  auto fetch = [&](int p) {
+    const __amdgpu_buffer_rsrc_t r = block_rsrc(maps + (size_t)p * D * NX, D * NX * 4);
+#pragma unroll
+    for (int i = 0; i < MD; ++i) {
+      const int f = threadIdx.x + NTH * i, row = f / (D / 4), c4 = f % (D / 4);
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)((row * NX + 4 * c4) * 4), 0, 0);
+      pst[i] = __builtin_bit_cast(float4, v);
+    }
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) qst[md][rr] = block_load(r, xo, (uint32_t)((16 * md + rr) * NX * 4));
+  };
+  auto stage = [&](int buf) {
+    bh* phi = reinterpret_cast<bh*>(smem + buf * 2 * C::MAT);
+    bh* plo = phi + C::MAT / 2;
+#pragma unroll
+    for (int i = 0; i < MD; ++i) {
+      const int f = threadIdx.x + NTH * i, row = f / (D / 4), c4 = f % (D / 4);
+      s16x4_t hi, lo;
+      split4(f32x4{pst[i].x, pst[i].y, pst[i].z, pst[i].w}, hi, lo);
+      *reinterpret_cast<s16x4_t*>(phi + row * LDC + 4 * c4) = hi;
+      *reinterpret_cast<s16x4_t*>(plo + row * LDC + 4 * c4) = lo;
+    }
+  };
+
+  if (a.NS > 1) {
+    fetch(0);
+    __syncthreads();   // zero fill done
+    stage(0);
+    __syncthreads();
+  }
+  for (int p = 0; p + 1 < a.NS; ++p) {
+    // start state of segment p
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) block_store(st, so, (uint32_t)((p * D + 16 * md + rr) * D * 4), H[md][rr]);
+    s16x4_t hh[2 * NP], hl[2 * NP];
+#pragma unroll
+    for (int t = 0; t < 2 * NP; ++t) {
+      if (t < MD) {
+        split4(H[t], hh[t], hl[t]);
+      } else {
+        hh[t] = s16x4_t{0, 0, 0, 0};
+        hl[t] = s16x4_t{0, 0, 0, 0};
+      }
+    }
+    f32x4 acc[MD];
+#pragma unroll
+    for (int md = 0; md < MD; ++md) acc[md] = qst[md];
+    fetch(p + 2 < a.NS ? p + 1 : p);   // the next map (the last step reloads its own, unused)
+    const bh* phi = reinterpret_cast<const bh*>(smem + (p & 1) * 2 * C::MAT);
+    const bh* plo = phi + C::MAT / 2;
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      const bf16x8_t bhi = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(hh[2 * q], hh[2 * q + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+      const bf16x8_t blo = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(hl[2 * q], hl[2 * q + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int md = 0; md < MD; ++md) {
+        const bf16x8_t ahi = fragB2(phi + (16 * md + cl) * LDC, 2 * q, g);
+        const bf16x8_t alo = fragB2(plo + (16 * md + cl) * LDC, 2 * q, g);
+        acc[md] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bhi, acc[md], 0, 0, 0);
+        acc[md] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, blo, acc[md], 0, 0, 0);
+        acc[md] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bhi, acc[md], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int md = 0; md < MD; ++md) H[md] = acc[md];
+    stage((p + 1) & 1);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int md = 0; md < MD; ++md)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      block_store(st, so, (uint32_t)(((a.NS - 1) * D + 16 * md + rr) * D * 4), H[md][rr]);
+}
 
 // ---------------------------------------------------------------------------
 // 3. Outputs.  grid (NS, B * H), one launch per requested direction (the
@@ -1093,9 +1122,13 @@ Plan make_plan(const Problem& p, int direction) {
   pl.ndir = pl.dirs == 3 ? 2 : 1;
   int L = g_segment_override.load(std::memory_order_relaxed);
   if (L <= 0) {
-    // enough segments for ~2048 output workgroups
+    // The output kernel runs one workgroup per CU (its LDS use), so aim for
+    // five whole rounds of workgroups over the 256 CUs of a gfx950 part:
+    // longer segments mean fewer serial steps in the chain kernel, and whole
+    // rounds avoid a partly idle last round.
+    constexpr long long kRounds = 5, kComputeUnits = 256;
     const long long hb = (long long)p.B * p.H;
-    const long long want = (2048 + hb - 1) / hb;
+    const long long want = (kRounds * kComputeUnits + hb - 1) / hb;
     long long per = (p.T + want - 1) / want;
     L = (int)((per + CH - 1) / CH * CH);
   }
@@ -1146,7 +1179,7 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
     prof_end(stream, GDN_KERNEL_SEG_MAP);
   }
   prof_begin(stream, GDN_KERNEL_SEG_CHAIN);
-  hipLaunchKernelGGL((seg_chain_kernel<D>), dim3(D / 16, bhc, pl.ndir), dim3(NTC), 0, stream, a);
+  hipLaunchKernelGGL((seg_chain_kernel<D>), dim3(bhc, pl.ndir), dim3(64 * (D / 16)), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   prof_end(stream, GDN_KERNEL_SEG_CHAIN);
