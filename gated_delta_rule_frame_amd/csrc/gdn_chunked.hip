@@ -103,10 +103,19 @@ struct Geo {
   static constexpr int NT = 64 * (NSW + 1);      // threads per workgroup
   static constexpr int DP = (D + 31) / 32 * 32;  // d padded to whole K = 32 steps
   static constexpr int NP = DP / 32;
-  static constexpr int LDK = DP + 8;             // row stride of d-contracted fp16 rows
 };
 
-// Shared memory.  Two sub-chunk buffers (Q and K rows, K^T, P, the inverse,
+// K and Q rows (fp16, d-contracted) are 288 bytes apart, and rows whose index
+// has bit 3 set start 16 bytes further in.  In units of 8 bytes the row starts
+// then fall on banks 4 (r % 8) + 2 ((r / 8) % 2) (mod 32), which makes both
+// ways these rows are read conflict-free per half wavefront: 16 consecutive
+// rows x 2 adjacent 8-byte units (fragment reads), and 8 consecutive rows x 4
+// adjacent units (transposing reads of K^T).  Row offsets depend on r % 16 only
+// through the shift, so every read is a per-lane base plus an immediate.
+constexpr int LDK = 144;   // elements
+__device__ __forceinline__ constexpr int krow(int r) { return r * LDK + 8 * ((r >> 3) & 1); }
+
+// Shared memory.  Two sub-chunk buffers (Q and K rows, P, the inverse,
 // gate factors) alternate between "being computed on" and "being prepared";
 // the A matrix and the helper's diagonal blocks are single-buffered (their
 // producer and consumer phases are separated by a barrier).  OUT: output pass
@@ -114,16 +123,15 @@ struct Geo {
 template <int D, bool OUT>
 struct Lay {
   using G = Geo<D>;
-  static constexpr int QR = OUT ? CH * G::LDK * 2 : 0;
-  static constexpr int KR = CH * G::LDK * 2;
-  static constexpr int KT = D * LDT * 2;
+  static_assert(G::DP + 8 <= LDK, "K rows exceed their stride");
+  static constexpr int QR = OUT ? CH * LDK * 2 : 0;
+  static constexpr int KR = CH * LDK * 2;
   static constexpr int PP = OUT ? CH * LDT * 2 : 0;
   static constexpr int TT = CH * LDT * 2;
   static constexpr int GT = 5 * CH * 4;
   static constexpr int o_qr = 0;
   static constexpr int o_kr = o_qr + QR;
-  static constexpr int o_kt = o_kr + KR;
-  static constexpr int o_pp = o_kt + KT;
+  static constexpr int o_pp = o_kr + KR;
   static constexpr int o_tt = o_pp + PP;               // Tm diag(beta), fp16 rows
   static constexpr int o_gt = o_tt + TT;
   static constexpr int BUF = o_gt + GT;
@@ -132,12 +140,12 @@ struct Lay {
   static constexpr int o_ad = o_td + CH * LDD * 2;     // diagonal blocks of A, fp32
   static constexpr int BYTES = o_ad + 4 * ADB * 4;
   static_assert(BYTES <= 160 * 1024, "workgroup LDS budget exceeded");
-  static_assert(QR % 16 == 0 && KR % 16 == 0 && KT % 16 == 0 && PP % 16 == 0 && BUF % 16 == 0, "alignment");
+  static_assert(QR % 16 == 0 && KR % 16 == 0 && PP % 16 == 0 && BUF % 16 == 0, "alignment");
 };
 
 // One sub-chunk buffer.
 struct Buf {
-  hb *qr, *kr, *kt, *pp, *tt;
+  hb *qr, *kr, *pp, *tt;
   float *g2, *eg, *ce, *dn, *bt;   // cumsum (log2), e^G, c e^G, c e^{G_n - G}, beta
 };
 
@@ -157,7 +165,6 @@ __device__ __forceinline__ Buf buf_at(char* s, int i) {
   Buf b;
   b.qr = reinterpret_cast<hb*>(p + L::o_qr);
   b.kr = reinterpret_cast<hb*>(p + L::o_kr);
-  b.kt = reinterpret_cast<hb*>(p + L::o_kt);
   b.pp = reinterpret_cast<hb*>(p + L::o_pp);
   b.tt = reinterpret_cast<hb*>(p + L::o_tt);
   float* gt = reinterpret_cast<float*>(p + L::o_gt);
@@ -225,6 +232,14 @@ __device__ __forceinline__ f32x4 mfma16(f16x4_t x, f16x4_t y) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(x, y, zero4(), 0, 0, 0);
 }
 
+// Transposing read (gfx950): in each group of 16 lanes, lane 4a + e receives
+// element e of the 8-byte units addressed by lanes a, a + 4, a + 8, a + 12 of
+// the group.  Used to read K^T fragments straight from the K rows.
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_tr_t;
+__device__ __forceinline__ f16x4_t ld4_tr(const hb* p) {
+  return __builtin_bit_cast(f16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_tr_t*)(p)));
+}
+
 // A fragment of k tiles (q, q + 1) in the register-B order.
 __device__ __forceinline__ f16x8_t fragA2(const hb* arow, int q, int g) {
   return cat8(ld4(arow + 16 * q + 4 * g), ld4(arow + 16 * q + 16 + 4 * g));
@@ -289,8 +304,9 @@ __device__ __forceinline__ void block_store(__amdgpu_buffer_rsrc_t r, uint32_t v
 }
 
 // --- staging --------------------------------------------------------------------
-// Strip-wave thread j holds scan rows 2 (j % 32) and 2 (j % 32) + 1, components
-// 8 (j / 32) .. + 7, of K (and of Q in the output pass); the helper wave holds
+// Strip-wave thread j holds scan rows 2 (j / (D/8)) and 2 (j / (D/8)) + 1,
+// components 8 (j % (D/8)) .. + 7, of K (and of Q in the output pass), so that
+// a wavefront's loads cover whole rows; the helper wave holds
 // one token's log-gate and beta per lane.  Loading into registers is split from
 // writing LDS so that the loads of sub-chunk c+2 are in flight while sub-chunk
 // c is computed.  Every load is unconditional: rows past n (and sub-chunks past
@@ -304,7 +320,7 @@ struct StageG {
 
 template <int D, bool OUT>
 __device__ __forceinline__ void fetch_kq(const Args& a, int b, int h, const Sub& sb, StageKQ& st) {
-  const int t = threadIdx.x, i2 = t & 31, c8 = t >> 5;
+  const int t = threadIdx.x, i2 = t / (D / 8), c8 = t % (D / 8);
   const int HD = a.H * D;
   const long long e0 = ((long long)b * a.T + sb.t0) * HD + (long long)h * D;
   const __amdgpu_buffer_rsrc_t rk = rows_rsrc(a.k + e0, (long long)sb.n * HD * 2);
@@ -330,24 +346,15 @@ __device__ __forceinline__ void fetch_gates(const Args& a, int b, int h, const S
   st.b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rows_rsrc(a.beta + go, (long long)sb.n * a.H * 4), off, 0, 0));
 }
 
-// Write the staged rows into buffer B: K and Q rows and K^T as fp16.
+// Write the staged rows into buffer B as fp16.
 template <int D, bool OUT>
 __device__ __forceinline__ void stage_kq(const Buf& B, const StageKQ& st) {
-  using G = Geo<D>;
-  const int t = threadIdx.x, i2 = t & 31, c8 = t >> 5;
-  uint4 xk[2];
+  const int t = threadIdx.x, i2 = t / (D / 8), c8 = t % (D / 8);
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
-    xk[r] = bf16x8_to_f16x8(st.k[r]);
-    *reinterpret_cast<uint4*>(B.kr + (2 * i2 + r) * G::LDK + 8 * c8) = xk[r];
-    if constexpr (OUT) *reinterpret_cast<uint4*>(B.qr + (2 * i2 + r) * G::LDK + 8 * c8) = bf16x8_to_f16x8(st.q[r]);
+    *reinterpret_cast<uint4*>(B.kr + krow(2 * i2 + r) + 8 * c8) = bf16x8_to_f16x8(st.k[r]);
+    if constexpr (OUT) *reinterpret_cast<uint4*>(B.qr + krow(2 * i2 + r) + 8 * c8) = bf16x8_to_f16x8(st.q[r]);
   }
-  const hb* e0 = reinterpret_cast<const hb*>(&xk[0]);
-  const hb* e1 = reinterpret_cast<const hb*>(&xk[1]);
-#pragma unroll
-  for (int u = 0; u < 8; ++u)
-    *reinterpret_cast<uint32_t*>(B.kt + (8 * c8 + u) * LDT + 2 * i2) =
-        static_cast<uint32_t>(e0[u]) | (static_cast<uint32_t>(e1[u]) << 16);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wavefront with DPP moves: a
@@ -391,8 +398,8 @@ __device__ void tinv_diag(const Inv& I, const Buf& B);
 template <int D>
 __device__ __forceinline__ f32x4 gram_tile(const hb* kr, const hb* xr, int ta, int tb, int cl, int g) {
   using G = Geo<D>;
-  const hb* arow = kr + (16 * ta + cl) * G::LDK;
-  const hb* brow = xr + (16 * tb + cl) * G::LDK;
+  const hb* arow = kr + krow(16 * ta + cl);
+  const hb* brow = xr + krow(16 * tb + cl);
   f32x4 acc = zero4();
   // both operands in the same (permuted) k order, two 8-byte reads each
 #pragma unroll
@@ -559,7 +566,7 @@ __device__ __forceinline__ void rows_times_state(const hb* rows, const f16x8_t (
   for (int p = 0; p < G::NP; ++p)
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const f16x8_t a = fragA2(rows + (16 * mt + cl) * G::LDK, 2 * p, g);
+      const f16x8_t a = fragA2(rows + krow(16 * mt + cl), 2 * p, g);
 #pragma unroll
       for (int j = 0; j < SPW; ++j) acc[j][mt] = mfma32(a, Xp[j][p], acc[j][mt]);
     }
@@ -594,7 +601,7 @@ __device__ __forceinline__ void state_times_rows_T(const hb* rows, const f16x8_t
 #pragma unroll
   for (int p = 0; p < G::NP; ++p)
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma32(Xp[p], fragA2(rows + (16 * mt + cl) * G::LDK, 2 * p, g), acc[mt]);
+    for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma32(Xp[p], fragA2(rows + krow(16 * mt + cl), 2 * p, g), acc[mt]);
 }
 
 __device__ __forceinline__ void tri_times_T(const hb* M, const f16x8_t (&vp)[2], int cl, int g, f32x4 (&acc)[4]) {
@@ -604,20 +611,25 @@ __device__ __forceinline__ void tri_times_T(const hb* M, const f16x8_t (&vp)[2],
     for (int mt = 2 * p; mt < 4; ++mt) acc[mt] = mfma32(vp[p], fragA2(M + (16 * mt + cl) * LDT, 2 * p, g), acc[mt]);
 }
 
-// X[j] <- dec X[j] + K^T vs[j]  (vs: fp16 pairs of token-row tiles).
+// X[j] <- dec X[j] + K^T vs[j]  (vs: fp16 pairs of token-row tiles).  The K^T
+// fragments are transposing reads of the K rows: lane (g, cl) = (g, a + 4 j)
+// addresses row 16 h + 4 g + j, components 16 md + 4 a .. + 3, so that lane
+// (g, i) receives component 16 md + i of rows 16 h + 4 g .. + 3, which is the
+// register-B token order of vs.
 template <int D, int SPW>
-__device__ __forceinline__ void state_update(const hb* kt, const f16x8_t (&vs)[SPW][2], float dec, int cl, int g,
+__device__ __forceinline__ void state_update(const hb* kr, const f16x8_t (&vs)[SPW][2], float dec, int cl, int g,
                                              f32x4 (&X)[SPW][Geo<D>::MD]) {
   using G = Geo<D>;
 #pragma unroll
   for (int md = 0; md < G::MD; ++md)
 #pragma unroll
     for (int j = 0; j < SPW; ++j) X[j][md] = X[j][md] * dec;
+  const hb* kt = kr + krow(4 * g + (cl >> 2)) + 4 * (cl & 3);
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
     for (int md = 0; md < G::MD; ++md) {
-      const f16x8_t a = fragA2(kt + (16 * md + cl) * LDT, 2 * q, g);
+      const f16x8_t a = cat8(ld4_tr(kt + krow(32 * q) + 16 * md), ld4_tr(kt + krow(32 * q + 16) + 16 * md));
 #pragma unroll
       for (int j = 0; j < SPW; ++j) X[j][md] = mfma32(a, vs[j][q], X[j][md]);
     }
@@ -625,9 +637,12 @@ __device__ __forceinline__ void state_update(const hb* kt, const f16x8_t (&vs)[S
 
 // Value column `col` of the sub-chunk's rows in accumulator layout, kept as
 // raw bf16 bits (zero past n) until used in the next sub-chunk, so that no
-// instruction near the loads waits for them.
+// instruction near the loads waits for them.  They are widened only where they
+// are used: the loop-carried registers are then the load destinations
+// themselves (a widening copy at the loop latch would wait there for every
+// outstanding memory operation).
 struct Vals {
-  uint32_t w[4][4];
+  uint16_t w[4][4];
 };
 
 template <int D>
@@ -644,8 +659,8 @@ __device__ __forceinline__ void load_values(const Args& a, int b, int h, const S
 }
 
 __device__ __forceinline__ f32x4 vals_tile(const Vals& V, int mt) {
-  return f32x4{__uint_as_float(V.w[mt][0] << 16), __uint_as_float(V.w[mt][1] << 16),
-               __uint_as_float(V.w[mt][2] << 16), __uint_as_float(V.w[mt][3] << 16)};
+  return f32x4{__uint_as_float((uint32_t)V.w[mt][0] << 16), __uint_as_float((uint32_t)V.w[mt][1] << 16),
+               __uint_as_float((uint32_t)V.w[mt][2] << 16), __uint_as_float((uint32_t)V.w[mt][3] << 16)};
 }
 
 // ---------------------------------------------------------------------------
@@ -766,7 +781,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_map_kernel(Args a) {
         Vs[j][0] = tof16x8(Vn[j][0] * d0, Vn[j][1] * d1);
         Vs[j][1] = tof16x8(Vn[j][2] * d2, Vn[j][3] * d3);
       }
-      state_update<D, SPW>(Bc.kt, Vs, Bc.eg[CH - 1], cl, g, X);
+      state_update<D, SPW>(Bc.kr, Vs, Bc.eg[CH - 1], cl, g, X);
     }
     if (c + 1 < nsub) gram_stage_strips<D, false>(a, Bn, I);
     __syncthreads();
@@ -1074,7 +1089,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
         const f32x4 d2 = ld4f(Bc.dn + 32 + 4 * g), d3 = ld4f(Bc.dn + 48 + 4 * g);
         Vs[0][0] = tof16x8(Vn[0][0] * d0, Vn[0][1] * d1);
         Vs[0][1] = tof16x8(Vn[0][2] * d2, Vn[0][3] * d3);
-        state_update<D, SPW>(Bc.kt, Vs, Bc.eg[CH - 1], cl, g, H);
+        state_update<D, SPW>(Bc.kr, Vs, Bc.eg[CH - 1], cl, g, H);
         // outputs of the sub-chunk's n scan rows (rows past n fall outside the buffer)
         {
           const bool half = mode != 1 && a.out_bf16;
