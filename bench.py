@@ -71,8 +71,9 @@ def map_flops(n, d):
 
 
 def executed_flops(T, L, d, bh, ndir):
-    """Per-launch algorithmic flops of the chunked path's kernels (the output
-    kernel is launched once per scan direction, the others once per call)."""
+    """Algorithmic flops per call of each of the chunked path's kernels, summed
+    over its launches (a bidirectional call launches each kernel once per scan
+    direction)."""
     segs = subchunk_sizes(T, L)
     per_out = sum(out_flops(n, d) for seg in segs for n in seg)
     # maps are formed for every segment but the last one of each scan
@@ -80,7 +81,7 @@ def executed_flops(T, L, d, bh, ndir):
     per_map_b = sum(map_flops(n, d) for seg in segs[1:] for n in seg)
     maps = per_map_f if ndir == 1 else per_map_f + per_map_b
     chain = (len(segs) - 1) * 2 * d ** 3
-    return {"seg_out_kernel": per_out * bh, "seg_map_kernel": maps * bh,
+    return {"seg_out_kernel": per_out * bh * ndir, "seg_map_kernel": maps * bh,
             "seg_chain_kernel": chain * bh * ndir}
 
 
@@ -229,12 +230,15 @@ def main():
     roof, flops_exec = None, None
     if "seg_out_kernel" in kern and L:
         fl = executed_flops(T, L, dk, B * H, ndir)
-        flops_exec = fl["seg_map_kernel"] + fl["seg_chain_kernel"] + fl["seg_out_kernel"] * ndir   # per call
+        flops_exec = sum(fl.values())   # per call
+        per_launch = {}
         for k in fl:
             if k in kern:
-                kern[k]["tflops"] = fl[k] / (kern[k]["avg_ms"] / 1e3) / 1e12
+                # launches of k per call, from the profile of the timed steps
+                per_launch[k] = fl[k] * args.steps / kern[k]["launches"]
+                kern[k]["tflops"] = per_launch[k] / (kern[k]["avg_ms"] / 1e3) / 1e12
         dom = max(kern, key=lambda k: kern[k]["avg_ms"] * kern[k]["launches"])
-        achieved = fl.get(dom, 0) / (kern[dom]["avg_ms"] / 1e3) / 1e12
+        achieved = per_launch.get(dom, 0) / (kern[dom]["avg_ms"] / 1e3) / 1e12
         traffic = read_traffic(dom, w.name)
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_TFLOPS, "traffic": traffic, "kernel": dom}

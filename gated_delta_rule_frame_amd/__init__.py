@@ -15,7 +15,7 @@ import ctypes
 import os
 
 __all__ = ["forward", "step", "workspace_size", "make_problem", "lib", "GdnError",
-           "set_segment_tokens", "segment_plan", "profile_enable", "profile_reset", "profile_read",
+           "set_segment_tokens", "set_concurrent_scans", "segment_plan", "profile_enable", "profile_reset", "profile_read",
            "FORWARD", "BACKWARD", "BIDIRECTIONAL", "ABI_VERSION", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
@@ -69,6 +69,8 @@ def lib():
         L.gdn_forward.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.gdn_set_segment_tokens.restype = None
         L.gdn_set_segment_tokens.argtypes = [i32]
+        L.gdn_set_concurrent_scans.restype = None
+        L.gdn_set_concurrent_scans.argtypes = [i32]
         L.gdn_profile_enable.restype = i32
         L.gdn_profile_enable.argtypes = [i32]
         L.gdn_profile_reset.restype = i32
@@ -137,6 +139,12 @@ def profile_read() -> dict:
         _check(lib().gdn_profile_read(i, ctypes.byref(n), ctypes.byref(ms)))
         out[name] = (n.value, ms.value)
     return out
+
+
+def set_concurrent_scans(on: bool) -> None:
+    """Let bidirectional calls overlap the two scans on a second stream (default
+    on); see gdn.h."""
+    lib().gdn_set_concurrent_scans(1 if on else 0)
 
 
 def segment_plan(problem: Problem, direction=BIDIRECTIONAL) -> int:

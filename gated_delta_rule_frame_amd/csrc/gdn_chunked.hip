@@ -51,6 +51,7 @@
 #include "gdn_mfma.h"
 
 #include <atomic>
+#include <mutex>
 
 namespace gdn {
 namespace {
@@ -62,6 +63,7 @@ constexpr int ADB = 260;        // float stride of the fp32 diagonal blocks of A
 constexpr float kLog2e = 1.4426950408889634f;
 
 std::atomic<int> g_segment_override{0};
+std::atomic<bool> g_concurrent_scans{true};
 
 struct Args {
   const bh* q;
@@ -73,11 +75,12 @@ struct Args {
   void* out;
   float* acc;           // fp32 partial of the reversed scan (BIDIR)
   float* hT;            // final state or null
-  float* maps;          // [ndir][B][H][NS-1][DK][DK+DV]
+  float* maps;          // [ndir][B][H][NS][DK][DK+DV]
   float* starts;        // [ndir][B][H][NS][DK][DV]
   long long T;
   int B, H, L, NS;
   int dirs;             // bit 0: forward scan, bit 1: reversed scan
+  int slot0;            // map and chain kernels: slot of blockIdx direction index 0
   int dir;              // output kernel: the scan direction of this launch (1: reversed)
   int mode;             // output kernel: 0 store outputs, 1 store the partial, 2 add the partial
   int out_bf16;
@@ -664,18 +667,21 @@ __device__ __forceinline__ f32x4 vals_tile(const Vals& V, int mt) {
 }
 
 // ---------------------------------------------------------------------------
-// 1. Segment maps.  grid (NS - 1, B * H, ndir).  The state X = [P | Q]
+// 1. Segment maps.  grid (segments, B * H, directions).  The state X = [P | Q]
 // (D x 2D): strip wave w owns column strip w of P and column strip w of Q.
-template <int D>
+// QO: Q only (the reversed scan of a bidirectional call, whose P is the
+// transpose of the forward scan's: every token's factor a (I - b k k^T) is
+// symmetric, so the product in reversed order is the transposed product).
+template <int D, bool QO>
 __global__ __launch_bounds__(Geo<D>::NT) void seg_map_kernel(Args a) {
   using G = Geo<D>;
   using L = Lay<D, false>;
-  constexpr int MD = G::MD, SPW = 2;
+  constexpr int MD = G::MD, SPW = QO ? 1 : 2, JQ = SPW - 1;   // JQ: the Q strip
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
   const int wave = wave_id(), lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
   const int pos = blockIdx.x;                       // scan position of the segment
   const int bh_ = blockIdx.y, b = bh_ / a.H, h = bh_ % a.H;
-  const int slot = blockIdx.z, dir = dir_of_slot(a.dirs, slot);
+  const int slot = a.slot0 + (int)blockIdx.z, dir = dir_of_slot(a.dirs, slot);
   const bool rev = dir == 1;
   const int seg = rev ? a.NS - 1 - pos : pos;
   const long long s0 = (long long)seg * a.L;
@@ -691,8 +697,8 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_map_kernel(Args a) {
   for (int md = 0; md < MD; ++md)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      X[0][md][r] = (wave == md && 4 * g + r == cl) ? 1.f : 0.f;
-      X[1][md][r] = 0.f;
+      if constexpr (!QO) X[0][md][r] = (wave == md && 4 * g + r == cl) ? 1.f : 0.f;
+      X[JQ][md][r] = 0.f;
     }
 
   auto piece = [&](int jj) {   // sub-chunk jj of the scan; past the segment: empty
@@ -747,14 +753,14 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_map_kernel(Args a) {
     fetch_kq<D, false>(a, b, h, piece(c + 2), sk);
     {
       f16x8_t Xp[SPW][G::NP];
-      state_pairs<D>(X[0], Xp[0]);
-      state_pairs<D>(X[1], Xp[1]);
+#pragma unroll
+      for (int j = 0; j < SPW; ++j) state_pairs<D>(X[j], Xp[j]);
       rows_times_state<D, SPW>(Bc.kr, Xp, cl, g, R);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const f32x4 ce = ld4f(Bc.ce + 16 * mt + 4 * g);
-        R[0][mt] = -(ce * R[0][mt]);
-        R[1][mt] = vals_tile(Vr, mt) - ce * R[1][mt];
+        if constexpr (!QO) R[0][mt] = -(ce * R[0][mt]);
+        R[JQ][mt] = vals_tile(Vr, mt) - ce * R[JQ][mt];
       }
       load_values<D>(a, b, h, piece(c + 1), 16 * wave + cl, g, Vr);
     }
@@ -786,8 +792,8 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_map_kernel(Args a) {
     if (c + 1 < nsub) gram_stage_strips<D, false>(a, Bn, I);
     __syncthreads();
   }
-  // store X = [P | Q] (fp32, row-major [D][2D])
-  const float* Xg = a.maps + ((((size_t)slot * a.B + b) * a.H + h) * (a.NS - 1) + pos) * (size_t)D * (2 * D);
+  // store X = [P | Q] (fp32, row-major [D][2D]; QO: the Q half)
+  const float* Xg = a.maps + ((((size_t)slot * a.B + b) * a.H + h) * a.NS + pos) * (size_t)D * (2 * D);
   const __amdgpu_buffer_rsrc_t xr = block_rsrc(Xg, D * 2 * D * 4);
   const uint32_t xo = (uint32_t)((4 * g * 2 * D + wave * 16 + cl) * 4);
 #pragma unroll
@@ -795,7 +801,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_map_kernel(Args a) {
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) block_store(xr, xo, (uint32_t)(((md * 16 + r) * 2 * D + j * D) * 4), X[j][md][r]);
+      for (int r = 0; r < 4; ++r) block_store(xr, xo, (uint32_t)(((md * 16 + r) * 2 * D + (j + (QO ? 1 : 0)) * D) * 4), X[j][md][r]);
 }
 
 // ---------------------------------------------------------------------------
@@ -835,19 +841,24 @@ __device__ __forceinline__ void split4(f32x4 v, s16x4_t& hi, s16x4_t& lo) {
   }
 }
 
-template <int D>
+template <int D, bool PT>
 __global__ __launch_bounds__(64 * (D / 16)) void seg_chain_kernel(Args a) {
   using C = ChainLay<D>;
   constexpr int MD = C::MD, NP = C::NP, LDC = C::LDC, NX = 2 * D, NTH = 64 * MD;
   __shared__ __attribute__((aligned(16))) char smem[C::BYTES];
   const int wave = wave_id(), lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
   const int bh_ = blockIdx.x, b = bh_ / a.H, h = bh_ % a.H;
-  const int slot = blockIdx.y, dir = dir_of_slot(a.dirs, slot);
+  const int slot = a.slot0 + (int)blockIdx.y, dir = dir_of_slot(a.dirs, slot);
   const float* seed = (dir == 0 || a.dirs == 2) ? a.h0 : nullptr;
   const int col = 16 * wave + cl;
   const uint32_t so = (uint32_t)((4 * g * D + col) * 4);        // lane offset within a [D][D] state
   const uint32_t xo = (uint32_t)((4 * g * NX + D + col) * 4);   // lane offset of Q within a [D][2D] map
-  const float* maps = a.maps + (((size_t)slot * a.B + b) * a.H + h) * (size_t)(a.NS > 1 ? a.NS - 1 : 0) * D * NX;
+  const float* maps = a.maps + (((size_t)slot * a.B + b) * a.H + h) * (size_t)a.NS * D * NX;
+  // PT: the reversed scan of a bidirectional call, which takes P_p as the
+  // transpose of the forward scan's P of the same segment (its Q half is its
+  // own).
+  constexpr bool ptr = PT;
+  const float* pmaps = ptr ? a.maps + ((size_t)b * a.H + h) * (size_t)a.NS * D * NX : maps;
   float* starts = a.starts + (((size_t)slot * a.B + b) * a.H + h) * (size_t)a.NS * D * D;
 
   for (int i = threadIdx.x; i < C::BYTES / 16; i += NTH) reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
@@ -862,43 +873,60 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_chain_kernel(Args a) {
   }
   const __amdgpu_buffer_rsrc_t st = block_rsrc(starts, (uint32_t)a.NS * D * D * 4);
 
-  // staging registers of one map: float4 number threadIdx.x + NTH i of P, and
-  // this lane's accumulator-layout tiles of Q
-  float4 pst[MD];
-  f32x4 qst[MD];
-  auto fetch = [&](int p) {
-    const __amdgpu_buffer_rsrc_t r = block_rsrc(maps + (size_t)p * D * NX, D * NX * 4);
+  // Maps in flight.  P (float4 number threadIdx.x + NTH i) is fetched two
+  // steps ahead into two register sets used alternately (the loop is unrolled
+  // by two so that no set is ever copied: a copy would wait for its loads);
+  // Q, this lane's accumulator-layout tiles, one step ahead.
+  typedef float4 PRegs[MD];
+  // Thread element f = threadIdx.x + NTH i holds row `row`, columns 4 c4 ..
+  // 4 c4 + 3 of the staged P; transposed, those are one column of four rows
+  // of the stored map (dword loads, coalesced along the column index).
+  auto fetch_p = [&](int p, PRegs& r) {
+    const __amdgpu_buffer_rsrc_t m = block_rsrc(pmaps + (size_t)(ptr ? a.NS - 1 - p : p) * D * NX, D * NX * 4);
 #pragma unroll
     for (int i = 0; i < MD; ++i) {
-      const int f = threadIdx.x + NTH * i, row = f / (D / 4), c4 = f % (D / 4);
-      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)((row * NX + 4 * c4) * 4), 0, 0);
-      pst[i] = __builtin_bit_cast(float4, v);
+      const int f = threadIdx.x + NTH * i;
+      if constexpr (ptr) {
+        const int row = f % D, c4 = f / D;
+        r[i] = make_float4(block_load(m, (uint32_t)(((4 * c4 + 0) * NX + row) * 4), 0),
+                           block_load(m, (uint32_t)(((4 * c4 + 1) * NX + row) * 4), 0),
+                           block_load(m, (uint32_t)(((4 * c4 + 2) * NX + row) * 4), 0),
+                           block_load(m, (uint32_t)(((4 * c4 + 3) * NX + row) * 4), 0));
+      } else {
+        const int row = f / (D / 4), c4 = f % (D / 4);
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(m, (uint32_t)((row * NX + 4 * c4) * 4), 0, 0);
+        r[i] = __builtin_bit_cast(float4, v);
+      }
     }
+  };
+  auto fetch_q = [&](int p, f32x4 (&q)[MD]) {
+    const __amdgpu_buffer_rsrc_t m = block_rsrc(maps + (size_t)p * D * NX, D * NX * 4);
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) qst[md][rr] = block_load(r, xo, (uint32_t)((16 * md + rr) * NX * 4));
+      for (int rr = 0; rr < 4; ++rr) q[md][rr] = block_load(m, xo, (uint32_t)((16 * md + rr) * NX * 4));
   };
-  auto stage = [&](int buf) {
+  auto stage = [&](int buf, const PRegs& r) {
     bh* phi = reinterpret_cast<bh*>(smem + buf * 2 * C::MAT);
     bh* plo = phi + C::MAT / 2;
 #pragma unroll
     for (int i = 0; i < MD; ++i) {
-      const int f = threadIdx.x + NTH * i, row = f / (D / 4), c4 = f % (D / 4);
+      const int f = threadIdx.x + NTH * i;
+      const int row = ptr ? f % D : f / (D / 4), c4 = ptr ? f / D : f % (D / 4);
       s16x4_t hi, lo;
-      split4(f32x4{pst[i].x, pst[i].y, pst[i].z, pst[i].w}, hi, lo);
+      split4(f32x4{r[i].x, r[i].y, r[i].z, r[i].w}, hi, lo);
       *reinterpret_cast<s16x4_t*>(phi + row * LDC + 4 * c4) = hi;
       *reinterpret_cast<s16x4_t*>(plo + row * LDC + 4 * c4) = lo;
     }
   };
 
-  if (a.NS > 1) {
-    fetch(0);
-    __syncthreads();   // zero fill done
-    stage(0);
-    __syncthreads();
-  }
-  for (int p = 0; p + 1 < a.NS; ++p) {
+  const int nsteps = a.NS - 1;
+  auto last = [&](int p) { return p < nsteps ? p : nsteps - 1; };   // clamped map index
+  PRegs ra, rb;
+  f32x4 qn[MD];   // Q of the current step's map, then of the next one
+  // Step p: H_{p+1} = P_p H_p + Q_p with P_p staged in LDS buffer p & 1; `cur`
+  // receives P_{p+2}, and `nxt` holds P_{p+1}, staged at the end of the step.
+  auto step = [&](int p, PRegs& cur, PRegs& nxt) {
     // start state of segment p
 #pragma unroll
     for (int md = 0; md < MD; ++md)
@@ -916,8 +944,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_chain_kernel(Args a) {
     }
     f32x4 acc[MD];
 #pragma unroll
-    for (int md = 0; md < MD; ++md) acc[md] = qst[md];
-    fetch(p + 2 < a.NS ? p + 1 : p);   // the next map (the last step reloads its own, unused)
+    for (int md = 0; md < MD; ++md) acc[md] = qn[md];
+    fetch_q(last(p + 1), qn);
+    fetch_p(last(p + 2), cur);
     const bh* phi = reinterpret_cast<const bh*>(smem + (p & 1) * 2 * C::MAT);
     const bh* plo = phi + C::MAT / 2;
 #pragma unroll
@@ -935,9 +964,24 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_chain_kernel(Args a) {
     }
 #pragma unroll
     for (int md = 0; md < MD; ++md) H[md] = acc[md];
-    stage((p + 1) & 1);
+    stage((p + 1) & 1, nxt);
+    __syncthreads();
+  };
+
+  if (nsteps > 0) {
+    fetch_p(0, ra);
+    fetch_q(0, qn);
+    fetch_p(last(1), rb);
+    __syncthreads();   // zero fill done
+    stage(0, ra);
     __syncthreads();
   }
+  int p = 0;
+  for (; p + 1 < nsteps; p += 2) {
+    step(p, ra, rb);
+    step(p + 1, rb, ra);
+  }
+  if (p < nsteps) step(p, ra, rb);
 #pragma unroll
   for (int md = 0; md < MD; ++md)
 #pragma unroll
@@ -1153,7 +1197,7 @@ Plan make_plan(const Problem& p, int direction) {
   pl.L = L;
   pl.NS = (int)((p.T + L - 1) / L);
   const size_t bhd = (size_t)pl.ndir * p.B * p.H;
-  const size_t maps = bhd * (size_t)(pl.NS - 1) * p.dk * (p.dk + p.dv) * sizeof(float);
+  const size_t maps = bhd * (size_t)pl.NS * p.dk * (p.dk + p.dv) * sizeof(float);
   const size_t starts = bhd * (size_t)pl.NS * p.dk * p.dv * sizeof(float);
   const size_t acc = (pl.dirs == 3 && p.out_bf16) ? (size_t)p.B * p.T * p.H * p.dv * sizeof(float) : 0;
   pl.maps_off = 0;
@@ -1161,6 +1205,34 @@ Plan make_plan(const Problem& p, int direction) {
   pl.acc_off = pl.starts_off + align_up(starts, 256);
   pl.bytes = pl.acc_off + align_up(acc, 256);
   return pl;
+}
+
+// A library-owned stream per device (default priority) with a fork and a join
+// event, for the concurrent part of bidirectional calls.  Created on first use
+// and kept until the process ends.  The mutex makes a call's fork, launches and
+// join one unit with respect to calls from other host threads.
+struct Side {
+  std::mutex mu;
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+
+// The side stream of the current device, or null if it cannot be created (the
+// call then runs everything on its own stream).
+Side* side_stream() {
+  constexpr int kMaxDevices = 64;
+  static Side sides[kMaxDevices];
+  static std::once_flag once[kMaxDevices];
+  static bool ok[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(once[dev], [dev] {
+    Side& s = sides[dev];
+    ok[dev] = hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking) == hipSuccess &&
+              hipEventCreateWithFlags(&s.fork, hipEventDisableTiming) == hipSuccess &&
+              hipEventCreateWithFlags(&s.join, hipEventDisableTiming) == hipSuccess;
+  });
+  return ok[dev] ? &sides[dev] : nullptr;
 }
 
 template <int D>
@@ -1186,29 +1258,80 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
   a.out_bf16 = p.out_bf16 ? 1 : 0;
   a.c = p.key_scale;
   const unsigned bhc = (unsigned)(p.B * p.H);
-  if (pl.NS > 1) {
-    prof_begin(stream, GDN_KERNEL_SEG_MAP);
-    hipLaunchKernelGGL((seg_map_kernel<D>), dim3(pl.NS - 1, bhc, pl.ndir), dim3(Geo<D>::NT), 0, stream, a);
-    hipError_t e = hipGetLastError();
+  const bool both = pl.dirs == 3;
+  // Maps of the scan in `slot`: segments 0 .. NS-2 in scan order, and for the
+  // forward scan of a bidirectional call also the last one (its transpose is
+  // the reversed scan's first P); that reversed scan forms Q only.
+  auto maps_k = [&](int slot, hipStream_t st) -> hipError_t {
+    if (pl.NS < 2) return hipSuccess;
+    a.slot0 = slot;
+    prof_begin(st, GDN_KERNEL_SEG_MAP);
+    if (both && slot == 1)
+      hipLaunchKernelGGL((seg_map_kernel<D, true>), dim3(pl.NS - 1, bhc, 1), dim3(Geo<D>::NT), 0, st, a);
+    else
+      hipLaunchKernelGGL((seg_map_kernel<D, false>), dim3(both ? pl.NS : pl.NS - 1, bhc, 1), dim3(Geo<D>::NT), 0,
+                         st, a);
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    prof_end(stream, GDN_KERNEL_SEG_MAP);
-  }
-  prof_begin(stream, GDN_KERNEL_SEG_CHAIN);
-  hipLaunchKernelGGL((seg_chain_kernel<D>), dim3(bhc, pl.ndir), dim3(64 * (D / 16)), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  prof_end(stream, GDN_KERNEL_SEG_CHAIN);
-  for (int dir = 1; dir >= 0; --dir) {   // reversed scan first
-    if (!(pl.dirs & (1 << dir))) continue;
+    prof_end(st, GDN_KERNEL_SEG_MAP);
+    return hipSuccess;
+  };
+  // Chain of the scan in `slot`.
+  auto chain_k = [&](int slot, hipStream_t st) -> hipError_t {
+    a.slot0 = slot;
+    prof_begin(st, GDN_KERNEL_SEG_CHAIN);
+    if (both && slot == 1)
+      hipLaunchKernelGGL((seg_chain_kernel<D, true>), dim3(bhc, 1), dim3(64 * (D / 16)), 0, st, a);
+    else
+      hipLaunchKernelGGL((seg_chain_kernel<D, false>), dim3(bhc, 1), dim3(64 * (D / 16)), 0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    prof_end(st, GDN_KERNEL_SEG_CHAIN);
+    return hipSuccess;
+  };
+  // Outputs of one scan direction; in a bidirectional call the forward scan
+  // stores its partial and the reversed scan adds it.
+  auto outputs = [&](int dir, hipStream_t st) -> hipError_t {
     a.dir = dir;
-    a.mode = pl.dirs == 3 ? (dir == 1 ? 1 : 2) : 0;
-    prof_begin(stream, GDN_KERNEL_SEG_OUT);
-    hipLaunchKernelGGL((seg_out_kernel<D>), dim3(pl.NS, bhc, 1), dim3(Geo<D>::NT), 0, stream, a);
-    e = hipGetLastError();
+    a.mode = both ? (dir == 0 ? 1 : 2) : 0;
+    prof_begin(st, GDN_KERNEL_SEG_OUT);
+    hipLaunchKernelGGL((seg_out_kernel<D>), dim3(pl.NS, bhc, 1), dim3(Geo<D>::NT), 0, st, a);
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    prof_end(stream, GDN_KERNEL_SEG_OUT);
+    prof_end(st, GDN_KERNEL_SEG_OUT);
+    return hipSuccess;
+  };
+  hipError_t e = hipSuccess;
+  if (!both) {
+    if ((e = maps_k(0, stream)) != hipSuccess) return e;
+    if ((e = chain_k(0, stream)) != hipSuccess) return e;
+    return outputs(pl.dirs == 1 ? 0 : 1, stream);
   }
-  return e;
+  Side* side = g_concurrent_scans.load(std::memory_order_relaxed) ? side_stream() : nullptr;
+  if (!side) {
+    if ((e = maps_k(0, stream)) != hipSuccess) return e;
+    if ((e = maps_k(1, stream)) != hipSuccess) return e;
+    if ((e = chain_k(0, stream)) != hipSuccess) return e;
+    if ((e = chain_k(1, stream)) != hipSuccess) return e;
+    if ((e = outputs(0, stream)) != hipSuccess) return e;
+    return outputs(1, stream);
+  }
+  // Both scans, partly concurrent.  The serial chain kernels occupy one CU per
+  // head, so each runs beside a full-width kernel: the forward maps first
+  // (alone; the reversed chain needs them too), then on the side stream the
+  // reversed maps and chain beside the forward chain and outputs.  The
+  // reversed outputs add the forward partial and so wait for both.
+  std::lock_guard<std::mutex> lk(side->mu);
+  if ((e = maps_k(0, stream)) != hipSuccess) return e;
+  if ((e = hipEventRecord(side->fork, stream)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(side->stream, side->fork, 0)) != hipSuccess) return e;
+  if ((e = maps_k(1, side->stream)) != hipSuccess) return e;
+  if ((e = chain_k(1, side->stream)) != hipSuccess) return e;
+  if ((e = hipEventRecord(side->join, side->stream)) != hipSuccess) return e;
+  if ((e = chain_k(0, stream)) != hipSuccess) return e;
+  if ((e = outputs(0, stream)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(stream, side->join, 0)) != hipSuccess) return e;
+  return outputs(1, stream);
 }
 
 }  // namespace
@@ -1244,5 +1367,6 @@ hipError_t chunked_launch(const Problem& p, int direction, const Tensors& t, voi
 int chunked_segment_tokens(const Problem& p, int direction) { return make_plan(p, direction).L; }
 
 void set_segment_tokens(int tokens) { g_segment_override.store(tokens > 0 ? tokens : 0); }
+void set_concurrent_scans(bool on) { g_concurrent_scans.store(on); }
 
 }  // namespace gdn

@@ -44,6 +44,7 @@ hipError_t chunked_launch(const Problem& p, int direction, const Tensors& t,
                           void* workspace, hipStream_t stream);
 
 void set_segment_tokens(int tokens);
+void set_concurrent_scans(bool on);
 int chunked_segment_tokens(const Problem& p, int direction);
 
 // Kernel timing hooks (gdn_profile.cpp): no-ops unless profiling is enabled.

@@ -39,7 +39,11 @@
  * aligned.
  *
  * Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream)
- * and return after enqueueing.  The library allocates no device memory: the
+ * and return after enqueueing.  `stream` must belong to the current device.
+ * A bidirectional call of the chunked path also runs part of its work on a
+ * stream the library owns on that device (created on first use, default
+ * priority, kept until the process ends), joined back into `stream` with
+ * events before the call's last kernel; see gdn_set_concurrent_scans().  The library allocates no device memory: the
  * caller passes a workspace of at least gdn_workspace_size() bytes.  All
  * arguments are validated on the host before anything is enqueued; on any
  * error nothing is enqueued and a status other than GDN_OK is returned, with
@@ -169,6 +173,13 @@ const char* gdn_kernel_name(int32_t kernel);   /* static text; "" if unknown */
  * not depend on it beyond rounding, but gdn_workspace_size() does, so size
  * the workspace after setting it.  Thread-safe. */
 void gdn_set_segment_tokens(int32_t tokens);
+
+/* Tuning knob of the chunked path: 1 (default) lets a bidirectional call run
+ * the two scans' segment maps and chains partly concurrently on a second,
+ * library-owned stream; 0 runs every kernel on the call's stream, in order
+ * (maps, chain, reversed outputs, forward outputs), e.g. to time kernels one
+ * at a time.  Results are identical.  Process-wide; thread-safe. */
+void gdn_set_concurrent_scans(int32_t on);
 
 /* Tokens per segment the chunked path would use for (problem, direction), or
  * 0 when the call would take the token-recurrent path.  Host only. */

@@ -140,6 +140,29 @@ def test_chunked_matches_recurrent_gpu(algo):
     assert rel_err(b[0], a[0]) <= 2e-2 and rel_err(b[1], a[1]) <= 2e-2
 
 
+def test_concurrent_scans_match_in_order_schedule():
+    """A bidirectional chunked call gives bit-identical results whether the two
+    scans overlap on the library's second stream or run in order on the
+    caller's stream (same kernels, same inputs, no reduction order changes);
+    several segments, so both chains step."""
+    w = SMALL["clip60s"]
+    x = make_inputs(w, 5)
+    G.set_segment_tokens(256)
+    try:
+        G.set_concurrent_scans(False)
+        a = run_gpu(w, x, "bidir", "chunked")
+        G.set_concurrent_scans(True)
+        b = run_gpu(w, x, "bidir", "chunked")
+        c = run_gpu(w, x, "bidir", "chunked")
+    finally:
+        G.set_concurrent_scans(True)
+        G.set_segment_tokens(0)
+    for u, v in ((a, b), (a, c)):
+        assert np.array_equal(u[0], v[0]) and np.array_equal(u[1], v[1])
+    ro, rH = O.bidir(*oracle_args(x)[0], x["h0"])
+    assert rel_err(b[0], ro) <= TOL["bf16"] and rel_err(b[1], rH) <= TOL["bf16"]
+
+
 FULL = [(1, "bidir", [0, 19]), (2, "bidir", [7]), (2, "fwd", [13]), (4, "bidir", [(0, 3), (1, 34)])]
 
 
