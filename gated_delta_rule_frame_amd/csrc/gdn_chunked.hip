@@ -81,6 +81,7 @@ struct Args {
   int B, H, L, NS;
   int dirs;             // bit 0: forward scan, bit 1: reversed scan
   int slot0;            // map and chain kernels: slot of blockIdx direction index 0
+  int heads_rev;        // map and output kernels: visit the (batch, head) pairs in reversed order
   int dir;              // output kernel: the scan direction of this launch (1: reversed)
   int mode;             // output kernel: 0 store outputs, 1 store the partial, 2 add the partial
   int out_bf16;
@@ -106,6 +107,10 @@ struct Geo {
   static constexpr int NT = 64 * (NSW + 1);      // threads per workgroup
   static constexpr int DP = (D + 31) / 32 * 32;  // d padded to whole K = 32 steps
   static constexpr int NP = DP / 32;
+  // Row stride (elements) of the staged V rows: at least D and = 16 (mod 32),
+  // i.e. an odd multiple of 8 words, so that the 8 consecutive rows x 32 bytes
+  // of a transposing read per half wavefront fall on distinct banks.
+  static constexpr int LDV = (D + 15) / 32 * 32 + 16;
 };
 
 // K and Q rows (fp16, d-contracted) are 288 bytes apart, and rows whose index
@@ -118,7 +123,7 @@ struct Geo {
 constexpr int LDK = 144;   // elements
 __device__ __forceinline__ constexpr int krow(int r) { return r * LDK + 8 * ((r >> 3) & 1); }
 
-// Shared memory.  Two sub-chunk buffers (Q and K rows, P, the inverse,
+// Shared memory.  Two sub-chunk buffers (Q, K and V rows, P, the inverse,
 // gate factors) alternate between "being computed on" and "being prepared";
 // the A matrix and the helper's diagonal blocks are single-buffered (their
 // producer and consumer phases are separated by a barrier).  OUT: output pass
@@ -129,12 +134,14 @@ struct Lay {
   static_assert(G::DP + 8 <= LDK, "K rows exceed their stride");
   static constexpr int QR = OUT ? CH * LDK * 2 : 0;
   static constexpr int KR = CH * LDK * 2;
+  static constexpr int VR = CH * G::LDV * 2;
   static constexpr int PP = OUT ? CH * LDT * 2 : 0;
   static constexpr int TT = CH * LDT * 2;
   static constexpr int GT = 5 * CH * 4;
   static constexpr int o_qr = 0;
   static constexpr int o_kr = o_qr + QR;
-  static constexpr int o_pp = o_kr + KR;
+  static constexpr int o_vr = o_kr + KR;               // V rows, raw bf16
+  static constexpr int o_pp = o_vr + VR;
   static constexpr int o_tt = o_pp + PP;               // Tm diag(beta), fp16 rows
   static constexpr int o_gt = o_tt + TT;
   static constexpr int BUF = o_gt + GT;
@@ -143,12 +150,13 @@ struct Lay {
   static constexpr int o_ad = o_td + CH * LDD * 2;     // diagonal blocks of A, fp32
   static constexpr int BYTES = o_ad + 4 * ADB * 4;
   static_assert(BYTES <= 160 * 1024, "workgroup LDS budget exceeded");
-  static_assert(QR % 16 == 0 && KR % 16 == 0 && PP % 16 == 0 && BUF % 16 == 0, "alignment");
+  static_assert(QR % 16 == 0 && KR % 16 == 0 && VR % 16 == 0 && PP % 16 == 0 && BUF % 16 == 0, "alignment");
 };
 
 // One sub-chunk buffer.
 struct Buf {
   hb *qr, *kr, *pp, *tt;
+  bh* vr;
   float *g2, *eg, *ce, *dn, *bt;   // cumsum (log2), e^G, c e^G, c e^{G_n - G}, beta
 };
 
@@ -168,6 +176,7 @@ __device__ __forceinline__ Buf buf_at(char* s, int i) {
   Buf b;
   b.qr = reinterpret_cast<hb*>(p + L::o_qr);
   b.kr = reinterpret_cast<hb*>(p + L::o_kr);
+  b.vr = reinterpret_cast<bh*>(p + L::o_vr);
   b.pp = reinterpret_cast<hb*>(p + L::o_pp);
   b.tt = reinterpret_cast<hb*>(p + L::o_tt);
   float* gt = reinterpret_cast<float*>(p + L::o_gt);
@@ -308,14 +317,14 @@ __device__ __forceinline__ void block_store(__amdgpu_buffer_rsrc_t r, uint32_t v
 
 // --- staging --------------------------------------------------------------------
 // Strip-wave thread j holds scan rows 2 (j / (D/8)) and 2 (j / (D/8)) + 1,
-// components 8 (j % (D/8)) .. + 7, of K (and of Q in the output pass), so that
-// a wavefront's loads cover whole rows; the helper wave holds
+// components 8 (j % (D/8)) .. + 7, of K and V (and of Q in the output pass),
+// so that a wavefront's loads cover whole rows; the helper wave holds
 // one token's log-gate and beta per lane.  Loading into registers is split from
 // writing LDS so that the loads of sub-chunk c+2 are in flight while sub-chunk
 // c is computed.  Every load is unconditional: rows past n (and sub-chunks past
 // the segment, given as n = 0) read as zeros through the buffer range check.
 struct StageKQ {
-  uint4 k[2], q[2];
+  uint4 k[2], v[2], q[2];
 };
 struct StageG {
   float g, b;
@@ -327,6 +336,7 @@ __device__ __forceinline__ void fetch_kq(const Args& a, int b, int h, const Sub&
   const int HD = a.H * D;
   const long long e0 = ((long long)b * a.T + sb.t0) * HD + (long long)h * D;
   const __amdgpu_buffer_rsrc_t rk = rows_rsrc(a.k + e0, (long long)sb.n * HD * 2);
+  const __amdgpu_buffer_rsrc_t rv = rows_rsrc(a.v + e0, (long long)sb.n * HD * 2);
   const __amdgpu_buffer_rsrc_t rq = rows_rsrc(a.q + e0, OUT ? (long long)sb.n * HD * 2 : 0);
   const int lr = sb.r0 + sb.sgn * 2 * i2;
 #pragma unroll
@@ -334,6 +344,8 @@ __device__ __forceinline__ void fetch_kq(const Args& a, int b, int h, const Sub&
     const uint32_t off = (uint32_t)((lr + sb.sgn * r) * HD * 2 + 16 * c8);
     const u32x4_t vk = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
     st.k[r] = make_uint4(vk[0], vk[1], vk[2], vk[3]);
+    const u32x4_t vv = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+    st.v[r] = make_uint4(vv[0], vv[1], vv[2], vv[3]);
     if constexpr (OUT) {
       const u32x4_t vq = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
       st.q[r] = make_uint4(vq[0], vq[1], vq[2], vq[3]);
@@ -349,13 +361,14 @@ __device__ __forceinline__ void fetch_gates(const Args& a, int b, int h, const S
   st.b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rows_rsrc(a.beta + go, (long long)sb.n * a.H * 4), off, 0, 0));
 }
 
-// Write the staged rows into buffer B as fp16.
+// Write the staged rows into buffer B: K and Q as fp16, V as bf16.
 template <int D, bool OUT>
 __device__ __forceinline__ void stage_kq(const Buf& B, const StageKQ& st) {
   const int t = threadIdx.x, i2 = t / (D / 8), c8 = t % (D / 8);
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     *reinterpret_cast<uint4*>(B.kr + krow(2 * i2 + r) + 8 * c8) = bf16x8_to_f16x8(st.k[r]);
+    *reinterpret_cast<uint4*>(B.vr + (2 * i2 + r) * Geo<D>::LDV + 8 * c8) = st.v[r];
     if constexpr (OUT) *reinterpret_cast<uint4*>(B.qr + krow(2 * i2 + r) + 8 * c8) = bf16x8_to_f16x8(st.q[r]);
   }
 }
@@ -638,32 +651,17 @@ __device__ __forceinline__ void state_update(const hb* kr, const f16x8_t (&vs)[S
     }
 }
 
-// Value column `col` of the sub-chunk's rows in accumulator layout, kept as
-// raw bf16 bits (zero past n) until used in the next sub-chunk, so that no
-// instruction near the loads waits for them.  They are widened only where they
-// are used: the loop-carried registers are then the load destinations
-// themselves (a widening copy at the loop latch would wait there for every
-// outstanding memory operation).
-struct Vals {
-  uint16_t w[4][4];
-};
-
+// Value tile mt of strip w in accumulator layout (lane (g, cl): rows
+// 16 mt + 4 g .. + 3, column 16 w + cl), by one transposing read of the staged
+// bf16 V rows: lane (g, a + 4 j) addresses row 16 mt + 4 g + j, columns
+// 16 w + 4 a .. + 3.
 template <int D>
-__device__ __forceinline__ void load_values(const Args& a, int b, int h, const Sub& sb, int col, int g, Vals& V) {
-  const int HD = a.H * D;
-  const bh* base = a.v + ((long long)b * a.T + sb.t0) * HD + (long long)h * D;
-  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(base, (long long)sb.n * HD * 2);
-  const int lp = (sb.r0 + sb.sgn * 4 * g) * HD * 2 + col * 2;
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      V.w[mt][r] = __builtin_amdgcn_raw_buffer_load_b16(rs, (uint32_t)(lp + sb.sgn * (16 * mt + r) * HD * 2), 0, 0);
-}
-
-__device__ __forceinline__ f32x4 vals_tile(const Vals& V, int mt) {
-  return f32x4{__uint_as_float((uint32_t)V.w[mt][0] << 16), __uint_as_float((uint32_t)V.w[mt][1] << 16),
-               __uint_as_float((uint32_t)V.w[mt][2] << 16), __uint_as_float((uint32_t)V.w[mt][3] << 16)};
+__device__ __forceinline__ f32x4 vals_tile(const bh* vr, int mt, int w, int cl, int g) {
+  const f16x4_t x = ld4_tr(vr + (16 * mt + 4 * g + (cl >> 2)) * Geo<D>::LDV + 16 * w + 4 * (cl & 3));
+  const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_shufflevector(x, x, 0, 1));
+  const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_shufflevector(x, x, 2, 3));
+  return f32x4{__uint_as_float(lo << 16), __uint_as_float(lo & 0xffff0000u), __uint_as_float(hi << 16),
+               __uint_as_float(hi & 0xffff0000u)};
 }
 
 // ---------------------------------------------------------------------------
@@ -680,7 +678,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_map_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
   const int wave = wave_id(), lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
   const int pos = blockIdx.x;                       // scan position of the segment
-  const int bh_ = blockIdx.y, b = bh_ / a.H, h = bh_ % a.H;
+  const int bh_ = a.heads_rev ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y, b = bh_ / a.H, h = bh_ % a.H;
   const int slot = a.slot0 + (int)blockIdx.z, dir = dir_of_slot(a.dirs, slot);
   const bool rev = dir == 1;
   const int seg = rev ? a.NS - 1 - pos : pos;
@@ -708,14 +706,12 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_map_kernel(Args a) {
   };
   StageKQ sk;
   StageG sg;
-  Vals Vr;
   {
     const Sub s0b = piece(0), s1b = piece(1);
     if (helper) {
       fetch_gates(a, b, h, s0b, sg);
     } else {
       fetch_kq<D, false>(a, b, h, s0b, sk);
-      load_values<D>(a, b, h, s0b, 16 * wave + cl, g, Vr);
     }
     __syncthreads();
     if (helper) {
@@ -760,9 +756,8 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_map_kernel(Args a) {
       for (int mt = 0; mt < 4; ++mt) {
         const f32x4 ce = ld4f(Bc.ce + 16 * mt + 4 * g);
         if constexpr (!QO) R[0][mt] = -(ce * R[0][mt]);
-        R[JQ][mt] = vals_tile(Vr, mt) - ce * R[JQ][mt];
+        R[JQ][mt] = vals_tile<D>(Bc.vr, mt, wave, cl, g) - ce * R[JQ][mt];
       }
-      load_values<D>(a, b, h, piece(c + 1), 16 * wave + cl, g, Vr);
     }
     __syncthreads();
     // beta
@@ -1003,7 +998,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
   const int wave = wave_id(), lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
   const int seg = blockIdx.x;
-  const int bh_ = blockIdx.y, b = bh_ / a.H, h = bh_ % a.H;
+  const int bh_ = a.heads_rev ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y, b = bh_ / a.H, h = bh_ % a.H;
   const long long s0 = (long long)seg * a.L;
   const long long s1 = (s0 + a.L < a.T) ? s0 + a.L : a.T;
   const int nsub = (int)((s1 - s0 + CH - 1) / CH);
@@ -1038,14 +1033,12 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
     };
     StageKQ sk;
     StageG sg;
-    Vals Vr;
     {
       const Sub s0b = piece(0), s1b = piece(1);
       if (helper) {
         fetch_gates(a, b, h, s0b, sg);
       } else {
         fetch_kq<D, true>(a, b, h, s0b, sk);
-        load_values<D>(a, b, h, s0b, col, g, Vr);
       }
       __syncthreads();
       if (helper) {
@@ -1103,8 +1096,8 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
         state_pairs<D>(H[0], Hp[0]);
         rows_times_state<D, SPW>(Bc.kr, Hp, cl, g, R);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) R[0][mt] = vals_tile(Vr, mt) - ld4f(Bc.ce + 16 * mt + 4 * g) * R[0][mt];
-        load_values<D>(a, b, h, piece(c + 1), col, g, Vr);
+        for (int mt = 0; mt < 4; ++mt)
+          R[0][mt] = vals_tile<D>(Bc.vr, mt, wave, cl, g) - ld4f(Bc.ce + 16 * mt + 4 * g) * R[0][mt];
       }
       __syncthreads();
       // beta
@@ -1262,9 +1255,14 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
   // Maps of the scan in `slot`: segments 0 .. NS-2 in scan order, and for the
   // forward scan of a bidirectional call also the last one (its transpose is
   // the reversed scan's first P); that reversed scan forms Q only.
+  // In a bidirectional call the second map and output launches visit the heads
+  // in reversed order, so that they start on the heads whose inputs (and
+  // partial outputs) the first launch touched last, which the memory-side
+  // cache may still hold.
   auto maps_k = [&](int slot, hipStream_t st) -> hipError_t {
     if (pl.NS < 2) return hipSuccess;
     a.slot0 = slot;
+    a.heads_rev = both && slot == 1;
     prof_begin(st, GDN_KERNEL_SEG_MAP);
     if (both && slot == 1)
       hipLaunchKernelGGL((seg_map_kernel<D, true>), dim3(pl.NS - 1, bhc, 1), dim3(Geo<D>::NT), 0, st, a);
@@ -1294,6 +1292,7 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
   auto outputs = [&](int dir, hipStream_t st) -> hipError_t {
     a.dir = dir;
     a.mode = both ? (dir == 0 ? 1 : 2) : 0;
+    a.heads_rev = both && dir == 1;
     prof_begin(st, GDN_KERNEL_SEG_OUT);
     hipLaunchKernelGGL((seg_out_kernel<D>), dim3(pl.NS, bhc, 1), dim3(Geo<D>::NT), 0, st, a);
     const hipError_t e = hipGetLastError();
