@@ -82,6 +82,7 @@ struct Args {
   int dirs;             // bit 0: forward scan, bit 1: reversed scan
   int slot0;            // map and chain kernels: slot of blockIdx direction index 0
   int heads_rev;        // map and output kernels: visit the (batch, head) pairs in reversed order
+  int npos;             // map and output kernels: segments in the launch (gridDim.x may be larger)
   int dir;              // output kernel: the scan direction of this launch (1: reversed)
   int mode;             // output kernel: 0 store outputs, 1 store the partial, 2 add the partial
   int out_bf16;
@@ -678,6 +679,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_map_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
   const int wave = wave_id(), lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
   const int pos = blockIdx.x;                       // scan position of the segment
+  if (pos >= a.npos) return;                        // padding of the grid (whole workgroup)
   const int bh_ = a.heads_rev ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y, b = bh_ / a.H, h = bh_ % a.H;
   const int slot = a.slot0 + (int)blockIdx.z, dir = dir_of_slot(a.dirs, slot);
   const bool rev = dir == 1;
@@ -998,6 +1000,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
   const int wave = wave_id(), lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
   const int seg = blockIdx.x;
+  if (seg >= a.npos) return;                        // padding of the grid (whole workgroup)
   const int bh_ = a.heads_rev ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y, b = bh_ / a.H, h = bh_ % a.H;
   const long long s0 = (long long)seg * a.L;
   const long long s1 = (s0 + a.L < a.T) ? s0 + a.L : a.T;
@@ -1252,6 +1255,11 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
   a.c = p.key_scale;
   const unsigned bhc = (unsigned)(p.B * p.H);
   const bool both = pl.dirs == 3;
+  // Workgroups are dealt to the 8 XCDs (each with its own L2) in turn.  With
+  // the segment index padded to a multiple of 8, a segment of neighbouring
+  // heads lands on the same XCD, so the cache lines their rows share (a head's
+  // slice of a token row is not line-aligned) are fetched from memory once.
+  auto padded = [](int n) { return (unsigned)((n + 7) / 8 * 8); };
   // Maps of the scan in `slot`: segments 0 .. NS-2 in scan order, and for the
   // forward scan of a bidirectional call also the last one (its transpose is
   // the reversed scan's first P); that reversed scan forms Q only.
@@ -1264,11 +1272,11 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
     a.slot0 = slot;
     a.heads_rev = both && slot == 1;
     prof_begin(st, GDN_KERNEL_SEG_MAP);
+    a.npos = both && slot == 0 ? pl.NS : pl.NS - 1;
     if (both && slot == 1)
-      hipLaunchKernelGGL((seg_map_kernel<D, true>), dim3(pl.NS - 1, bhc, 1), dim3(Geo<D>::NT), 0, st, a);
+      hipLaunchKernelGGL((seg_map_kernel<D, true>), dim3(padded(a.npos), bhc, 1), dim3(Geo<D>::NT), 0, st, a);
     else
-      hipLaunchKernelGGL((seg_map_kernel<D, false>), dim3(both ? pl.NS : pl.NS - 1, bhc, 1), dim3(Geo<D>::NT), 0,
-                         st, a);
+      hipLaunchKernelGGL((seg_map_kernel<D, false>), dim3(padded(a.npos), bhc, 1), dim3(Geo<D>::NT), 0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     prof_end(st, GDN_KERNEL_SEG_MAP);
@@ -1294,7 +1302,8 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
     a.mode = both ? (dir == 0 ? 1 : 2) : 0;
     a.heads_rev = both && dir == 1;
     prof_begin(st, GDN_KERNEL_SEG_OUT);
-    hipLaunchKernelGGL((seg_out_kernel<D>), dim3(pl.NS, bhc, 1), dim3(Geo<D>::NT), 0, st, a);
+    a.npos = pl.NS;
+    hipLaunchKernelGGL((seg_out_kernel<D>), dim3(padded(pl.NS), bhc, 1), dim3(Geo<D>::NT), 0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     prof_end(st, GDN_KERNEL_SEG_OUT);
