@@ -63,11 +63,12 @@ def out_flops(n, d):
     return n * (n - 1) * d + 3 * n * (n + 1) * d + 6 * n * d * d + n ** 3 // 3
 
 
-def map_flops(n, d):
+def map_flops(n, d, q_only=False):
     """Algorithmic flops of the segment-map pass on one sub-chunk (state [P|Q],
-    2d columns): strict-lower K K^T, the inverse, K X, Tm diag(beta) R and the
-    state update."""
-    return n * (n - 1) * d + 2 * n * (n + 1) * d + 8 * n * d * d + n ** 3 // 3
+    2d columns; q_only: Q alone, d columns): strict-lower K K^T, the inverse,
+    K X, Tm diag(beta) R and the state update."""
+    w = 1 if q_only else 2
+    return n * (n - 1) * d + w * n * (n + 1) * d + 4 * w * n * d * d + n ** 3 // 3
 
 
 def executed_flops(T, L, d, bh, ndir):
@@ -76,10 +77,14 @@ def executed_flops(T, L, d, bh, ndir):
     direction)."""
     segs = subchunk_sizes(T, L)
     per_out = sum(out_flops(n, d) for seg in segs for n in seg)
-    # maps are formed for every segment but the last one of each scan
-    per_map_f = sum(map_flops(n, d) for seg in segs[:-1] for n in seg)
-    per_map_b = sum(map_flops(n, d) for seg in segs[1:] for n in seg)
-    maps = per_map_f if ndir == 1 else per_map_f + per_map_b
+    if ndir == 1:
+        # maps of every segment but the last of the scan
+        maps = sum(map_flops(n, d) for seg in segs[:-1] for n in seg)
+    else:
+        # forward maps of every segment (the last one's P, transposed, is the
+        # reversed scan's first), reversed maps (Q only) of all but the first
+        maps = sum(map_flops(n, d) for seg in segs for n in seg)
+        maps += sum(map_flops(n, d, q_only=True) for seg in segs[1:] for n in seg)
     chain = (len(segs) - 1) * 2 * d ** 3
     return {"seg_out_kernel": per_out * bh * ndir, "seg_map_kernel": maps * bh,
             "seg_chain_kernel": chain * bh * ndir}
