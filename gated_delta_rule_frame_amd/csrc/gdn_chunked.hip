@@ -114,39 +114,52 @@ struct Geo {
   static constexpr int LDV = (D + 15) / 32 * 32 + 16;
 };
 
-// K and Q rows (fp16, d-contracted) are 288 bytes apart, and rows whose index
-// has bit 3 set start 16 bytes further in.  In units of 8 bytes the row starts
-// then fall on banks 4 (r % 8) + 2 ((r / 8) % 2) (mod 32), which makes both
-// ways these rows are read conflict-free per half wavefront: 16 consecutive
-// rows x 2 adjacent 8-byte units (fragment reads), and 8 consecutive rows x 4
-// adjacent units (transposing reads of K^T).  Row offsets depend on r % 16 only
-// through the shift, so every read is a per-lane base plus an immediate.
-constexpr int LDK = 144;   // elements
-__device__ __forceinline__ constexpr int krow(int r) { return r * LDK + 8 * ((r >> 3) & 1); }
+// K and Q rows (fp16, d-contracted): row r starts at r LDK + 8 (r / 8)
+// elements, with LDK = D (D = 16 mod 32) or D + 16 (D = 0 mod 32).  In units of
+// 8 bytes, LDK / 4 is then 4 times an odd number, so the starts of 8
+// consecutive rows fall on distinct multiples of 4 banks (mod 32 units), and
+// the 16-byte step every 8 rows puts rows 8..15 of a 16-row block on the
+// remaining even offsets.  Both ways these rows are read are then free of bank
+// conflicts per half wavefront: 16 consecutive rows x 2 adjacent 8-byte units
+// (fragment reads), and 8 consecutive rows x 4 adjacent units (transposing
+// reads of K^T).  krow is additive over a multiple-of-8 row offset, so every
+// read is a per-lane base plus an immediate.
+template <int D>
+struct KRows {
+  static constexpr int LDK = D % 32 == 0 ? D + 16 : D;
+  static constexpr int ELEMS = CH * LDK + 8 * (CH / 8);
+};
+template <int D>
+__device__ __forceinline__ constexpr int krow(int r) { return r * KRows<D>::LDK + 8 * (r >> 3); }
 
-// Shared memory.  Two sub-chunk buffers (Q, K and V rows, P, the inverse,
-// gate factors) alternate between "being computed on" and "being prepared";
-// the A matrix and the helper's diagonal blocks are single-buffered (their
-// producer and consumer phases are separated by a barrier).  OUT: output pass
-// (else map pass: no Q, no P).
+// Shared memory.  Two sub-chunk buffers (Q and K rows, P, the inverse, gate
+// factors) alternate between "being computed on" and "being prepared"; the V
+// rows (read in phase alpha only, so the next ones are written in beta), the A
+// matrix, the helper's diagonal blocks and the output staging rows are
+// single-buffered (their producer and consumer phases are separated by a
+// barrier).  OUT: output pass (else map pass: no Q, no P, no outputs).
 template <int D, bool OUT>
 struct Lay {
   using G = Geo<D>;
-  static_assert(G::DP + 8 <= LDK, "K rows exceed their stride");
-  static constexpr int QR = OUT ? CH * LDK * 2 : 0;
-  static constexpr int KR = CH * LDK * 2;
+  static constexpr int QR = OUT ? (KRows<D>::ELEMS * 2 + 15) / 16 * 16 : 0;
+  static constexpr int KR = (KRows<D>::ELEMS * 2 + 15) / 16 * 16;
   static constexpr int VR = CH * G::LDV * 2;
   static constexpr int PP = OUT ? CH * LDT * 2 : 0;
   static constexpr int TT = CH * LDT * 2;
   static constexpr int GT = 5 * CH * 4;
   static constexpr int o_qr = 0;
   static constexpr int o_kr = o_qr + QR;
-  static constexpr int o_vr = o_kr + KR;               // V rows, raw bf16
-  static constexpr int o_pp = o_vr + VR;
+  static constexpr int o_pp = o_kr + KR;
   static constexpr int o_tt = o_pp + PP;               // Tm diag(beta), fp16 rows
   static constexpr int o_gt = o_tt + TT;
   static constexpr int BUF = o_gt + GT;
-  static constexpr int o_ao = 2 * BUF;                 // off-diagonal blocks of A, fp16 rows
+  static constexpr int o_vr = 2 * BUF;                 // V rows, raw bf16
+  // output staging: 64 rows of D fp32 values, OSL floats apart (D + 4: the
+  // 16-row columns of a tile write fall on distinct banks)
+  static constexpr int OSL = D + 4;
+  static constexpr int OS = OUT ? CH * OSL * 4 : 0;
+  static constexpr int o_os = o_vr + VR;
+  static constexpr int o_ao = o_os + OS;               // off-diagonal blocks of A, fp16 rows
   static constexpr int o_td = o_ao + CH * LDT * 2;     // diagonal blocks of Tm, fp16 rows
   static constexpr int o_ad = o_td + CH * LDD * 2;     // diagonal blocks of A, fp32
   static constexpr int BYTES = o_ad + 4 * ADB * 4;
@@ -177,7 +190,7 @@ __device__ __forceinline__ Buf buf_at(char* s, int i) {
   Buf b;
   b.qr = reinterpret_cast<hb*>(p + L::o_qr);
   b.kr = reinterpret_cast<hb*>(p + L::o_kr);
-  b.vr = reinterpret_cast<bh*>(p + L::o_vr);
+  b.vr = reinterpret_cast<bh*>(lds_at(s, (uint32_t)L::o_vr));
   b.pp = reinterpret_cast<hb*>(p + L::o_pp);
   b.tt = reinterpret_cast<hb*>(p + L::o_tt);
   float* gt = reinterpret_cast<float*>(p + L::o_gt);
@@ -193,6 +206,7 @@ __device__ __forceinline__ Buf buf_at(char* s, int i) {
 struct Inv {
   hb *ao, *td;
   float* ad;
+  float* os;   // output staging rows (output pass)
 };
 
 template <int D, bool OUT>
@@ -203,6 +217,7 @@ __device__ __forceinline__ Inv inv_at(char* s0) {
   v.ao = reinterpret_cast<hb*>(s + L::o_ao);
   v.td = reinterpret_cast<hb*>(s + L::o_td);
   v.ad = reinterpret_cast<float*>(s + L::o_ad);
+  v.os = reinterpret_cast<float*>(s + L::o_os);
   return v;
 }
 
@@ -258,6 +273,14 @@ __device__ __forceinline__ f16x8_t fragA2(const hb* arow, int q, int g) {
   return cat8(ld4(arow + 16 * q + 4 * g), ld4(arow + 16 * q + 16 + 4 * g));
 }
 __device__ __forceinline__ f16x8_t tof16x8(f32x4 u, f32x4 v) { return cat8(tof16(u), tof16(v)); }
+// The same for the d-contracted K and Q rows at k-step p (columns 32 p ..):
+// when D = 16 (mod 32) the last step's upper 16 columns are past the row and
+// read as zero (their partner state rows are zero too).
+template <int D>
+__device__ __forceinline__ f16x8_t fragK(const hb* row, int p, int g) {
+  if (32 * p + 16 < D) return fragA2(row, 2 * p, g);
+  return cat8(ld4(row + 32 * p + 4 * g), zero_h4());
+}
 __device__ __forceinline__ f32x4 ld4f(const float* p) {
   const float4 v = *reinterpret_cast<const float4*>(p);
   return f32x4{v.x, v.y, v.z, v.w};
@@ -318,14 +341,17 @@ __device__ __forceinline__ void block_store(__amdgpu_buffer_rsrc_t r, uint32_t v
 
 // --- staging --------------------------------------------------------------------
 // Strip-wave thread j holds scan rows 2 (j / (D/8)) and 2 (j / (D/8)) + 1,
-// components 8 (j % (D/8)) .. + 7, of K and V (and of Q in the output pass),
-// so that a wavefront's loads cover whole rows; the helper wave holds
+// components 8 (j % (D/8)) .. + 7, of K, V and (output pass) Q, so that a
+// wavefront's loads cover whole rows; the helper wave holds
 // one token's log-gate and beta per lane.  Loading into registers is split from
 // writing LDS so that the loads of sub-chunk c+2 are in flight while sub-chunk
 // c is computed.  Every load is unconditional: rows past n (and sub-chunks past
 // the segment, given as n = 0) read as zeros through the buffer range check.
 struct StageKQ {
-  uint4 k[2], v[2], q[2];
+  uint4 k[2], q[2];
+};
+struct StageV {
+  uint4 v[2];
 };
 struct StageG {
   float g, b;
@@ -337,7 +363,6 @@ __device__ __forceinline__ void fetch_kq(const Args& a, int b, int h, const Sub&
   const int HD = a.H * D;
   const long long e0 = ((long long)b * a.T + sb.t0) * HD + (long long)h * D;
   const __amdgpu_buffer_rsrc_t rk = rows_rsrc(a.k + e0, (long long)sb.n * HD * 2);
-  const __amdgpu_buffer_rsrc_t rv = rows_rsrc(a.v + e0, (long long)sb.n * HD * 2);
   const __amdgpu_buffer_rsrc_t rq = rows_rsrc(a.q + e0, OUT ? (long long)sb.n * HD * 2 : 0);
   const int lr = sb.r0 + sb.sgn * 2 * i2;
 #pragma unroll
@@ -345,8 +370,6 @@ __device__ __forceinline__ void fetch_kq(const Args& a, int b, int h, const Sub&
     const uint32_t off = (uint32_t)((lr + sb.sgn * r) * HD * 2 + 16 * c8);
     const u32x4_t vk = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
     st.k[r] = make_uint4(vk[0], vk[1], vk[2], vk[3]);
-    const u32x4_t vv = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
-    st.v[r] = make_uint4(vv[0], vv[1], vv[2], vv[3]);
     if constexpr (OUT) {
       const u32x4_t vq = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
       st.q[r] = make_uint4(vq[0], vq[1], vq[2], vq[3]);
@@ -362,15 +385,36 @@ __device__ __forceinline__ void fetch_gates(const Args& a, int b, int h, const S
   st.b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rows_rsrc(a.beta + go, (long long)sb.n * a.H * 4), off, 0, 0));
 }
 
-// Write the staged rows into buffer B: K and Q as fp16, V as bf16.
+// V rows in the same thread mapping.
+template <int D>
+__device__ __forceinline__ void fetch_v(const Args& a, int b, int h, const Sub& sb, StageV& st) {
+  const int t = threadIdx.x, i2 = t / (D / 8), c8 = t % (D / 8);
+  const int HD = a.H * D;
+  const long long e0 = ((long long)b * a.T + sb.t0) * HD + (long long)h * D;
+  const __amdgpu_buffer_rsrc_t rv = rows_rsrc(a.v + e0, (long long)sb.n * HD * 2);
+  const int lr = sb.r0 + sb.sgn * 2 * i2;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const uint32_t off = (uint32_t)((lr + sb.sgn * r) * HD * 2 + 16 * c8);
+    const u32x4_t vv = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+    st.v[r] = make_uint4(vv[0], vv[1], vv[2], vv[3]);
+  }
+}
+template <int D>
+__device__ __forceinline__ void stage_v(const Buf& B, const StageV& st) {
+  const int t = threadIdx.x, i2 = t / (D / 8), c8 = t % (D / 8);
+#pragma unroll
+  for (int r = 0; r < 2; ++r) *reinterpret_cast<uint4*>(B.vr + (2 * i2 + r) * Geo<D>::LDV + 8 * c8) = st.v[r];
+}
+
+// Write the staged rows into buffer B: K and Q as fp16.
 template <int D, bool OUT>
 __device__ __forceinline__ void stage_kq(const Buf& B, const StageKQ& st) {
   const int t = threadIdx.x, i2 = t / (D / 8), c8 = t % (D / 8);
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
-    *reinterpret_cast<uint4*>(B.kr + krow(2 * i2 + r) + 8 * c8) = bf16x8_to_f16x8(st.k[r]);
-    *reinterpret_cast<uint4*>(B.vr + (2 * i2 + r) * Geo<D>::LDV + 8 * c8) = st.v[r];
-    if constexpr (OUT) *reinterpret_cast<uint4*>(B.qr + krow(2 * i2 + r) + 8 * c8) = bf16x8_to_f16x8(st.q[r]);
+    *reinterpret_cast<uint4*>(B.kr + krow<D>(2 * i2 + r) + 8 * c8) = bf16x8_to_f16x8(st.k[r]);
+    if constexpr (OUT) *reinterpret_cast<uint4*>(B.qr + krow<D>(2 * i2 + r) + 8 * c8) = bf16x8_to_f16x8(st.q[r]);
   }
 }
 
@@ -415,12 +459,12 @@ __device__ void tinv_diag(const Inv& I, const Buf& B);
 template <int D>
 __device__ __forceinline__ f32x4 gram_tile(const hb* kr, const hb* xr, int ta, int tb, int cl, int g) {
   using G = Geo<D>;
-  const hb* arow = kr + krow(16 * ta + cl);
-  const hb* brow = xr + krow(16 * tb + cl);
+  const hb* arow = kr + krow<D>(16 * ta + cl);
+  const hb* brow = xr + krow<D>(16 * tb + cl);
   f32x4 acc = zero4();
   // both operands in the same (permuted) k order, two 8-byte reads each
 #pragma unroll
-  for (int p = 0; p < G::NP; ++p) acc = mfma32(fragA2(arow, 2 * p, g), fragA2(brow, 2 * p, g), acc);
+  for (int p = 0; p < G::NP; ++p) acc = mfma32(fragK<D>(arow, p, g), fragK<D>(brow, p, g), acc);
   return acc;
 }
 
@@ -583,7 +627,7 @@ __device__ __forceinline__ void rows_times_state(const hb* rows, const f16x8_t (
   for (int p = 0; p < G::NP; ++p)
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const f16x8_t a = fragA2(rows + krow(16 * mt + cl), 2 * p, g);
+      const f16x8_t a = fragK<D>(rows + krow<D>(16 * mt + cl), p, g);
 #pragma unroll
       for (int j = 0; j < SPW; ++j) acc[j][mt] = mfma32(a, Xp[j][p], acc[j][mt]);
     }
@@ -618,7 +662,7 @@ __device__ __forceinline__ void state_times_rows_T(const hb* rows, const f16x8_t
 #pragma unroll
   for (int p = 0; p < G::NP; ++p)
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma32(Xp[p], fragA2(rows + krow(16 * mt + cl), 2 * p, g), acc[mt]);
+    for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma32(Xp[p], fragK<D>(rows + krow<D>(16 * mt + cl), p, g), acc[mt]);
 }
 
 __device__ __forceinline__ void tri_times_T(const hb* M, const f16x8_t (&vp)[2], int cl, int g, f32x4 (&acc)[4]) {
@@ -641,12 +685,12 @@ __device__ __forceinline__ void state_update(const hb* kr, const f16x8_t (&vs)[S
   for (int md = 0; md < G::MD; ++md)
 #pragma unroll
     for (int j = 0; j < SPW; ++j) X[j][md] = X[j][md] * dec;
-  const hb* kt = kr + krow(4 * g + (cl >> 2)) + 4 * (cl & 3);
+  const hb* kt = kr + krow<D>(4 * g + (cl >> 2)) + 4 * (cl & 3);
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
     for (int md = 0; md < G::MD; ++md) {
-      const f16x8_t a = cat8(ld4_tr(kt + krow(32 * q) + 16 * md), ld4_tr(kt + krow(32 * q + 16) + 16 * md));
+      const f16x8_t a = cat8(ld4_tr(kt + krow<D>(32 * q) + 16 * md), ld4_tr(kt + krow<D>(32 * q + 16) + 16 * md));
 #pragma unroll
       for (int j = 0; j < SPW; ++j) X[j][md] = mfma32(a, vs[j][q], X[j][md]);
     }
@@ -707,6 +751,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_map_kernel(Args a) {
     return make_sub(t0, jj < nsub ? (int)((s1 - t0) < CH ? (s1 - t0) : CH) : 0, rev);
   };
   StageKQ sk;
+  StageV sv;
   StageG sg;
   {
     const Sub s0b = piece(0), s1b = piece(1);
@@ -714,6 +759,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_map_kernel(Args a) {
       fetch_gates(a, b, h, s0b, sg);
     } else {
       fetch_kq<D, false>(a, b, h, s0b, sk);
+      fetch_v<D>(a, b, h, s0b, sv);
     }
     __syncthreads();
     if (helper) {
@@ -721,7 +767,9 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_map_kernel(Args a) {
       fetch_gates(a, b, h, s1b, sg);
     } else {
       stage_kq<D, false>(buf_at<D, false>(smem, 0), sk);
+      stage_v<D>(buf_at<D, false>(smem, 0), sv);
       fetch_kq<D, false>(a, b, h, s1b, sk);
+      fetch_v<D>(a, b, h, s1b, sv);
     }
     __syncthreads();
     if (helper) gram_stage_helper<D>(a, buf_at<D, false>(smem, 0), I);
@@ -762,7 +810,9 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_map_kernel(Args a) {
       }
     }
     __syncthreads();
-    // beta
+    // beta: the V rows of c+1 replace those of c (read in alpha only)
+    stage_v<D>(Bc, sv);
+    fetch_v<D>(a, b, h, piece(c + 2), sv);
     {
       f16x8_t Rh[SPW][2];
 #pragma unroll
@@ -1035,6 +1085,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
       return make_sub(t0, jj < nsub ? (int)((s1 - t0) < CH ? (s1 - t0) : CH) : 0, rev);
     };
     StageKQ sk;
+    StageV sv;
     StageG sg;
     {
       const Sub s0b = piece(0), s1b = piece(1);
@@ -1042,6 +1093,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
         fetch_gates(a, b, h, s0b, sg);
       } else {
         fetch_kq<D, true>(a, b, h, s0b, sk);
+        fetch_v<D>(a, b, h, s0b, sv);
       }
       __syncthreads();
       if (helper) {
@@ -1049,7 +1101,9 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
         fetch_gates(a, b, h, s1b, sg);
       } else {
         stage_kq<D, true>(buf_at<D, true>(smem, 0), sk);
+        stage_v<D>(buf_at<D, true>(smem, 0), sv);
         fetch_kq<D, true>(a, b, h, s1b, sk);
+        fetch_v<D>(a, b, h, s1b, sv);
       }
       __syncthreads();
       if (helper) gram_stage_helper<D>(a, buf_at<D, true>(smem, 0), I);
@@ -1070,29 +1124,60 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
       }
       return;
     }
-    f32x4 R[SPW][4];
+    // Outputs.  Sub-chunk c's tiles are written to the staging rows at the end
+    // of beta c and stored from there in alpha c+1 as whole rows (each thread
+    // 4 x 4 consecutive values), so that global stores and partial loads cover
+    // whole cache lines instead of each strip's 64-byte share of a row.  In
+    // mode 2 the partial is added there, loaded in the same row layout one
+    // sub-chunk ahead.
+    constexpr int NTS = 64 * G::NSW, C4 = D / 4;   // strip threads; 4-column groups per row
+    static_assert(CH * C4 == 4 * NTS, "four groups of four values per strip thread");
+    const int t = threadIdx.x;
+    const bool half = mode != 1 && a.out_bf16;
+    const long long esz = half ? 2 : 4;
+    char* const dstb = static_cast<char*>(mode == 1 ? static_cast<void*>(a.acc) : a.out);
     f32x4 pre[4];
+    auto rows_of = [&](int c) { return ((long long)b * a.T + piece(c).t0) * HD + (long long)h * D; };
+    auto load_pre = [&](int c) {
+      const Sub sb = piece(c);
+      const __amdgpu_buffer_rsrc_t rs = rows_rsrc(a.acc + rows_of(c), mode == 2 ? (long long)sb.n * HD * 4 : 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int k = t + NTS * i, row = k / C4, c4 = k % C4;
+        const u32x4_t v =
+            __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(((sb.r0 + sb.sgn * row) * (int)HD + 4 * c4) * 4), 0, 0);
+        pre[i] = __builtin_bit_cast(f32x4, v);   // whole-vector casts only: see the note on vector elements
+      }
+    };
+    auto flush = [&](int c) {   // store the staged outputs of sub-chunk c (rows past n fall outside the buffer)
+      const Sub sb = piece(c);
+      const Inv I = inv_at<D, true>(smem);
+      const __amdgpu_buffer_rsrc_t rs = rows_rsrc(dstb + rows_of(c) * esz, (long long)sb.n * HD * esz);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int k = t + NTS * i, row = k / C4, c4 = k % C4;
+        const f32x4 val = ld4f(I.os + row * L::OSL + 4 * c4) + pre[i];
+        const uint32_t off = (uint32_t)(((sb.r0 + sb.sgn * row) * (int)HD + 4 * c4) * esz);
+        if (half) {
+          typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+          const u32x2_t w{f32_to_bf16_bits(val[0]) | ((uint32_t)f32_to_bf16_bits(val[1]) << 16),
+                          f32_to_bf16_bits(val[2]) | ((uint32_t)f32_to_bf16_bits(val[3]) << 16)};
+          __builtin_amdgcn_raw_buffer_store_b64(w, rs, off, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, val), rs, off, 0, 0);
+        }
+      }
+    };
+    f32x4 R[SPW][4];
     for (int c = 0; c < nsub; ++c) {
       const Buf Bc = buf_at<D, true>(smem, c & 1), Bn = buf_at<D, true>(smem, (c + 1) & 1);
       const Inv I = inv_at<D, true>(smem);
-      const Sub sb = piece(c);
-      // per-lane element offset (from row t0) of the first output row, strip columns 4g ..
-      const int lo = (sb.r0 + sb.sgn * cl) * (int)HD + 16 * wave + 4 * g;
-      const long long rowb = ((long long)b * a.T + sb.t0) * HD + (long long)h * D;
-      // alpha.  The reversed scan's partial (forward pass of a bidirectional
-      // call; else an empty buffer) is loaded first: the load counter drains in
-      // issue order, so loads issued before the prefetches can be waited for
-      // without waiting for the prefetches.
-      {
-        const __amdgpu_buffer_rsrc_t rs = rows_rsrc(a.acc + rowb, mode == 2 ? (long long)sb.n * HD * 4 : 0);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          const u32x4_t v =
-              __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)((lo + sb.sgn * 16 * mt * (int)HD) * 4), 0, 0);
-          pre[mt] = __builtin_bit_cast(f32x4, v);   // whole-vector casts only: see the note on vector elements
-        }
-      }
+      // alpha.  Staging first: it waits for the prefetched rows, which were
+      // issued before the stores and loads below (the load counter drains in
+      // issue order).
       stage_kq<D, true>(Bn, sk);
+      if (c > 0) flush(c - 1);
+      load_pre(c);
       fetch_kq<D, true>(a, b, h, piece(c + 2), sk);
       {
         f16x8_t Hp[SPW][G::NP];
@@ -1103,7 +1188,9 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
           R[0][mt] = vals_tile<D>(Bc.vr, mt, wave, cl, g) - ld4f(Bc.ce + 16 * mt + 4 * g) * R[0][mt];
       }
       __syncthreads();
-      // beta
+      // beta: the V rows of c+1 replace those of c (read in alpha only)
+      stage_v<D>(Bc, sv);
+      fetch_v<D>(a, b, h, piece(c + 2), sv);
       {
         f32x4 O[4];   // outputs, transposed tiles (lane: token 16 mt + cl, columns 4g ..)
         {
@@ -1124,36 +1211,21 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) O[mt] = Bc.eg[16 * mt + cl] * O[mt];
         tri_times_T(Bc.pp, Vh[0], cl, g, O);
+        // staging rows: row 16 mt + cl, columns 16 wave + 4 g ..
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          *reinterpret_cast<f32x4*>(I.os + (16 * mt + cl) * L::OSL + 16 * wave + 4 * g) = O[mt];
         f16x8_t Vs[SPW][2];
         const f32x4 d0 = ld4f(Bc.dn + 4 * g), d1 = ld4f(Bc.dn + 16 + 4 * g);
         const f32x4 d2 = ld4f(Bc.dn + 32 + 4 * g), d3 = ld4f(Bc.dn + 48 + 4 * g);
         Vs[0][0] = tof16x8(Vn[0][0] * d0, Vn[0][1] * d1);
         Vs[0][1] = tof16x8(Vn[0][2] * d2, Vn[0][3] * d3);
         state_update<D, SPW>(Bc.kr, Vs, Bc.eg[CH - 1], cl, g, H);
-        // outputs of the sub-chunk's n scan rows (rows past n fall outside the buffer)
-        {
-          const bool half = mode != 1 && a.out_bf16;
-          void* dst = mode == 1 ? static_cast<void*>(a.acc) : a.out;
-          const long long esz = half ? 2 : 4;
-          const __amdgpu_buffer_rsrc_t rs = rows_rsrc(static_cast<char*>(dst) + rowb * esz, (long long)sb.n * HD * esz);
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt) {
-            const uint32_t off = (uint32_t)((lo + sb.sgn * 16 * mt * (int)HD) * esz);
-            const f32x4 val = O[mt] + pre[mt];
-            if (half) {
-              typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-              const u32x2_t w{f32_to_bf16_bits(val[0]) | ((uint32_t)f32_to_bf16_bits(val[1]) << 16),
-                              f32_to_bf16_bits(val[2]) | ((uint32_t)f32_to_bf16_bits(val[3]) << 16)};
-              __builtin_amdgcn_raw_buffer_store_b64(w, rs, off, 0, 0);
-            } else {
-              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, val), rs, off, 0, 0);
-            }
-          }
-        }
       }
       if (c + 1 < nsub) gram_stage_strips<D, true>(a, Bn, I);
       __syncthreads();
     }
+    if (nsub > 0) flush(nsub - 1);
     // final state: the scan's last segment
     if (a.hT && pos == a.NS - 1 && (dir == 0 || a.dirs == 2)) {
       const __amdgpu_buffer_rsrc_t hr = block_rsrc(a.hT + sbase, D * D * 4);
