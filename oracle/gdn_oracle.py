@@ -41,7 +41,8 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["fwd", "bwd", "bidir", "step", "jacobi", "forward"]
+__all__ = ["fwd", "bwd", "bidir", "step", "jacobi", "jacobi_bwd", "jacobi_bidir", "forward",
+           "jacobi_forward"]
 
 
 def _as64(x):
@@ -144,6 +145,37 @@ def jacobi(q, k, v, log_gate, beta, h0=None, key_scale=1.0, tokens_per_frame=Non
         H = gamma * H + np.swapaxes(Kf, -1, -2) @ (bf[..., None] * resid)
         o[:, sl] = (Qf @ H).transpose(0, 2, 1, 3)
     return o, H
+
+
+def jacobi_bwd(q, k, v, log_gate, beta, h0=None, key_scale=1.0, tokens_per_frame=None):
+    """Reversed-time scan of the frame-level transition.
+
+    [WM-summary] section 3.2, "Bidirectional and Chunk-Causal GDN Variants",
+    applied to the frame-wise update: the reversed scan is the forward scan of
+    the reversed token axis, so frames are visited last to first and a frame's
+    decay is the gate of its last token (the first one the reversed scan
+    meets).  ``h0`` seeds the reversed scan; the state returned is the state
+    after frame 0.
+    """
+    flip = lambda x: np.flip(_as64(x), axis=1)
+    o, H = jacobi(flip(q), flip(k), flip(v), flip(log_gate), flip(beta), h0, key_scale, tokens_per_frame)
+    return np.flip(o, axis=1).copy(), H
+
+
+def jacobi_bidir(q, k, v, log_gate, beta, h0=None, key_scale=1.0, tokens_per_frame=None):
+    """Bidirectional layer with the frame-level transition: the forward scan
+    from ``h0`` plus the reversed scan from zero, outputs summed; the final
+    state is the forward scan's ([WM-summary] section 3.2, "Bidirectional and
+    Chunk-Causal GDN Variants")."""
+    of, Hf = jacobi(q, k, v, log_gate, beta, h0, key_scale, tokens_per_frame)
+    ob, _ = jacobi_bwd(q, k, v, log_gate, beta, None, key_scale, tokens_per_frame)
+    return of + ob, Hf
+
+
+def jacobi_forward(direction, q, k, v, log_gate, beta, h0=None, key_scale=1.0, tokens_per_frame=None):
+    """Dispatch of the frame-level transition by direction name."""
+    fn = {"fwd": jacobi, "bwd": jacobi_bwd, "bidir": jacobi_bidir}[direction]
+    return fn(q, k, v, log_gate, beta, h0, key_scale, tokens_per_frame)
 
 
 def forward(direction, q, k, v, log_gate, beta, h0=None, key_scale=1.0):

@@ -182,6 +182,40 @@ def test_P4_orthonormal_keys_gate_on_first_token_states_agree():
     np.testing.assert_allclose(Hj, H, atol=1e-12)
 
 
+def test_P3b_single_token_frames_reversed_and_bidirectional_jacobi_equal_tokenwise():
+    """One token per frame: the reversed and bidirectional frame-level scans
+    are the token-wise ones (which the explicit-product pins fix)."""
+    w, x = tiny(seed=4)
+    h0 = 0.1 * np.random.default_rng(6).standard_normal(x["h0"].shape)
+    for jf, tf in ((O.jacobi_bwd, O.bwd), (O.jacobi_bidir, O.bidir)):
+        o, H = tf(*args(x), h0)
+        oj, Hj = jf(*args(x), h0, tokens_per_frame=1)
+        assert rel(oj, o) < 1e-12 and rel(Hj, H) < 1e-12
+
+
+def test_P4b_reversed_jacobi_takes_the_gate_of_the_frame_last_token():
+    """Orthonormal keys per frame, gate only on each frame's last token: the
+    reversed frame-level scan and the reversed token-wise scan reach the same
+    state (the reversed scan meets that token first)."""
+    rng = np.random.default_rng(14)
+    F, d = 3, 16
+    K = _orthonormal_frames(F, d, rng)
+    V, Q = rng.standard_normal((F * d, d)), rng.standard_normal((F * d, d))
+    g = np.zeros(F * d)
+    g[d - 1::d] = -rng.uniform(0.1, 0.5, F)
+    beta = rng.uniform(0, 1, F * d)
+    sh = lambda a: a[None, :, None]
+    h0 = rng.standard_normal((1, 1, d, d))
+    _, H = O.bwd(sh(Q), sh(K), sh(V), sh(g), sh(beta), h0)
+    _, Hj = O.jacobi_bwd(sh(Q), sh(K), sh(V), sh(g), sh(beta), h0, tokens_per_frame=d)
+    np.testing.assert_allclose(Hj, H, atol=1e-12)
+    # with the gate on the first token instead, the decays land elsewhere
+    g2 = np.roll(g, -(d - 1))
+    _, Hj2 = O.jacobi_bwd(sh(Q), sh(K), sh(V), sh(g2), sh(beta), h0, tokens_per_frame=d)
+    _, H2 = O.bwd(sh(Q), sh(K), sh(V), sh(g2), sh(beta), h0)
+    assert np.max(np.abs(Hj2 - H2)) > 1e-3
+
+
 def test_P5_same_key_twice_overwrites():
     rng = np.random.default_rng(17)
     d = 8
