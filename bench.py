@@ -90,6 +90,28 @@ def executed_flops(T, L, d, bh, ndir):
             "seg_chain_kernel": chain * bh * ndir}
 
 
+def jacobi_flops(S, F, d, bh, ndir):
+    """Algorithmic flops per call of the frame-level (Jacobi) path, per kernel:
+    per frame c^2 K^T diag(beta) K and c K^T diag(beta) V (4 S d^2), the
+    outputs Q H_end (2 S d^2, one product with the summed state), and one
+    d x d state product per frame and scan in the chain (2 d^3)."""
+    return {"jac_map_kernel": 4 * S * d * d * F * bh, "jac_out_kernel": 2 * S * d * d * F * bh,
+            "seg_chain_kernel": 2 * d ** 3 * F * bh * ndir}
+
+
+def jacobi_bytes(S, F, d, bh, ndir, out_bytes=4):
+    """Algorithmic HBM bytes per call of the frame-level path, per kernel: the
+    map kernel reads K, V (bf16) and beta and writes one [P | Q] map per frame
+    and scan (fp32); the output kernel reads Q and the end states and writes
+    the outputs; the chain reads the maps and writes the states."""
+    T = S * F
+    maps = ndir * F * bh * d * 2 * d * 4
+    states = ndir * (F + 1) * bh * d * d * 4
+    return {"jac_map_kernel": T * bh * (2 * d * 2 + 4) + maps,
+            "jac_out_kernel": T * bh * (2 * d + out_bytes * d) + states,
+            "seg_chain_kernel": maps + states}
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
@@ -135,6 +157,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--segment", type=int, default=0, help="tokens per segment (0 = automatic)")
     ap.add_argument("--parity-head", type=int, default=7)
+    ap.add_argument("--intra", default="sequential", choices=["sequential", "jacobi"],
+                    help="transition inside a frame: token-wise (the layer) or the frame-level form; "
+                         "jacobi runs with the spatial key scale 1/sqrt(tokens per frame)")
     ap.add_argument("--no-parity", action="store_true", help="skip the oracle check and CPU baseline")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after timing, run one device-to-device copy of this many bytes (counter calibration)")
@@ -162,15 +187,18 @@ def main():
         d[n] = torch.from_numpy(x[n]).to(dev)
     h0 = torch.from_numpy(x["h0"]).to(dev) if np.any(x["h0"]) else None
     B, T, H, dk, dv = w.batch, w.tokens, w.heads, w.d_k, w.d_v
+    jac = args.intra == "jacobi"
+    key_scale = w.tokens_per_frame ** -0.5 if jac else 1.0
     prob = G.make_problem(B, H, dk, dv, w.frames, w.tokens_per_frame, G.BF16 if w.qkv_dtype == "bf16" else G.F32,
-                          G.F32, "auto")
+                          G.F32, "auto", key_scale, args.intra)
     ws = torch.empty(max(G.workspace_size(prob, direction), 16), dtype=torch.uint8, device=dev)
     out = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
     hT = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
 
     def step():
         G.forward(d["q"], d["k"], d["v"], d["log_gate"], d["beta"], h0, direction,
-                  tokens_per_frame=w.tokens_per_frame, out=out, final_state=hT, workspace=ws)
+                  tokens_per_frame=w.tokens_per_frame, out=out, final_state=hT, workspace=ws,
+                  key_scale=key_scale, intra=args.intra)
 
     # ---- parity on a sampled head + CPU baseline (the same oracle run)
     parity, cpu_baseline = None, None
@@ -183,7 +211,11 @@ def main():
         a = [x[n][:1, :, hh:hh + 1] for n in ("q", "k", "v", "log_gate", "beta")]
         with threadpool_limits(1):
             t0 = time.perf_counter()
-            ro, rH = O.forward(direction, *a, x["h0"][:1, hh:hh + 1])
+            if jac:
+                ro, rH = O.jacobi_forward(direction, *a, x["h0"][:1, hh:hh + 1], key_scale=key_scale,
+                                          tokens_per_frame=w.tokens_per_frame)
+            else:
+                ro, rH = O.forward(direction, *a, x["h0"][:1, hh:hh + 1])
             cpu_s = time.perf_counter() - t0
         o = out[:1, :, hh:hh + 1].double().cpu().numpy()
         s = hT[:1, hh:hh + 1].double().cpu().numpy()
@@ -233,7 +265,21 @@ def main():
     canon = canonical_flops(w.tokens_per_frame, dk, dv) * B * H * w.frames * ndir
     kern = {k: {"launches": n, "avg_ms": (t / n if n else None)} for k, (n, t) in prof.items() if n}
     roof, flops_exec = None, None
-    if "seg_out_kernel" in kern and L:
+    if jac and kern:
+        F_, S_ = w.frames, w.tokens_per_frame
+        fl = jacobi_flops(S_, F_, dk, B * H, ndir)
+        by = jacobi_bytes(S_, F_, dk, B * H, ndir)
+        flops_exec = sum(fl.values())
+        for k in fl:
+            if k in kern:
+                launches = kern[k]["launches"] / args.steps
+                kern[k]["tflops"] = fl[k] / launches / (kern[k]["avg_ms"] / 1e3) / 1e12
+                kern[k]["gbs"] = by[k] / launches / (kern[k]["avg_ms"] / 1e3) / 1e9
+        dom = max(kern, key=lambda k: kern[k]["avg_ms"] * kern[k]["launches"])
+        achieved = kern[dom].get("gbs", 0.0)
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": read_traffic(dom, w.name + "_jacobi"), "kernel": dom}
+    elif "seg_out_kernel" in kern and L:
         fl = executed_flops(T, L, dk, B * H, ndir)
         flops_exec = sum(fl.values())   # per call
         per_launch = {}
@@ -247,7 +293,7 @@ def main():
         traffic = read_traffic(dom, w.name)
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_TFLOPS, "traffic": traffic, "kernel": dom}
-    credited = min(canon, flops_exec) if flops_exec else canon
+    credited = flops_exec if jac else (min(canon, flops_exec) if flops_exec else canon)
     layer_tflops = credited / (ms / 1e3) / 1e12
 
     line = {
@@ -267,7 +313,8 @@ def main():
             "workload": w.name, "direction": direction, "batch": B, "heads": H, "d_k": dk, "d_v": dv,
             "frames": w.frames, "tokens_per_frame": w.tokens_per_frame, "tokens": T,
             "inputs": f"{w.qkv_dtype} q/k/v, fp32 log-gate/beta/state, fp32 out; fp16 MFMA operands, fp32 accumulation",
-            "segment_tokens": L, "seed": args.seed,
+            "segment_tokens": None if jac else L, "seed": args.seed,
+            "intra": args.intra, "key_scale": key_scale,
         },
         "layer": {"canonical_gflop": canon / 1e9, "executed_gflop": (flops_exec or 0) / 1e9,
                   "credited_tflops": layer_tflops, "pct_peak": 100 * layer_tflops / PEAK_TFLOPS,

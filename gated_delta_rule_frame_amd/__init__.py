@@ -25,6 +25,7 @@ OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = ra
 F32, BF16 = 0, 1
 FORWARD, BACKWARD, BIDIRECTIONAL = 0, 1, 2
 ALGO = {"auto": 0, "chunked": 1, "recurrent": 2}
+INTRA = {"sequential": 0, "jacobi": 1}
 DIRECTION = {"fwd": FORWARD, "bwd": BACKWARD, "bidir": BIDIRECTIONAL,
              FORWARD: FORWARD, BACKWARD: BACKWARD, BIDIRECTIONAL: BIDIRECTIONAL}
 
@@ -41,7 +42,7 @@ class Problem(ctypes.Structure):
                 ("frames", ctypes.c_int32), ("tokens_per_frame", ctypes.c_int32),
                 ("qkv_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("algo", ctypes.c_int32), ("key_scale", ctypes.c_float),
-                ("reserved", ctypes.c_int32 * 5)]
+                ("intra", ctypes.c_int32), ("reserved", ctypes.c_int32 * 4)]
 
 
 _lib = None
@@ -97,7 +98,7 @@ def _check(status):
 
 
 def make_problem(batch, heads, d_k, d_v, frames, tokens_per_frame, qkv_dtype=BF16,
-                 out_dtype=BF16, algo="auto", key_scale=1.0):
+                 out_dtype=BF16, algo="auto", key_scale=1.0, intra="sequential"):
     p = Problem()
     p.abi_version = ABI_VERSION
     p.batch, p.heads, p.d_k, p.d_v = batch, heads, d_k, d_v
@@ -105,6 +106,7 @@ def make_problem(batch, heads, d_k, d_v, frames, tokens_per_frame, qkv_dtype=BF1
     p.qkv_dtype, p.out_dtype = qkv_dtype, out_dtype
     p.algo = ALGO[algo] if isinstance(algo, str) else int(algo)
     p.key_scale = float(key_scale)
+    p.intra = INTRA[intra] if isinstance(intra, str) else int(intra)
     return p
 
 
@@ -119,7 +121,8 @@ def set_segment_tokens(tokens: int) -> None:
     lib().gdn_set_segment_tokens(int(tokens))
 
 
-KERNELS = ("seg_map_kernel", "seg_chain_kernel", "seg_out_kernel", "recurrent_kernel")
+KERNELS = ("seg_map_kernel", "seg_chain_kernel", "seg_out_kernel", "recurrent_kernel", "jac_map_kernel",
+           "jac_out_kernel")
 
 
 def profile_enable(on: bool = True) -> None:
@@ -172,7 +175,8 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _prepare(q, k, v, log_gate, beta, frames, tokens_per_frame, out_dtype, algo, key_scale):
+def _prepare(q, k, v, log_gate, beta, frames, tokens_per_frame, out_dtype, algo, key_scale,
+             intra="sequential"):
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v), ("log_gate", log_gate), ("beta", beta)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda:
@@ -197,7 +201,7 @@ def _prepare(q, k, v, log_gate, beta, frames, tokens_per_frame, out_dtype, algo,
         raise ValueError(f"frames * tokens_per_frame = {frames * tokens_per_frame} != T = {T}")
     odt = torch.float32 if out_dtype is None else out_dtype
     p = make_problem(B, H, dk, dv, frames, tokens_per_frame, _dtype_code(q),
-                     _dtype_code(torch.empty(0, dtype=odt)), algo, key_scale)
+                     _dtype_code(torch.empty(0, dtype=odt)), algo, key_scale, intra)
     return p, (B, T, H, dk, dv), odt
 
 
@@ -222,17 +226,18 @@ def _workspace(problem, direction, workspace, device):
 
 def forward(q, k, v, log_gate, beta, initial_state=None, direction="bidir", *, frames=None,
             tokens_per_frame=None, key_scale=1.0, out_dtype=None, algo="auto",
-            out=None, final_state=None, want_state=True, workspace=None):
+            out=None, final_state=None, want_state=True, workspace=None, intra="sequential"):
     """Whole-sequence layer forward (gdn_forward); returns (out, final_state).
 
     q, k: [B,T,H,d_k]; v: [B,T,H,d_v] (fp32 or bf16, one dtype); log_gate,
     beta: [B,T,H] fp32; initial_state: [B,H,d_k,d_v] fp32 or None (zeros).
     The output is fp32 unless ``out_dtype`` says otherwise (a bf16 output adds
-    a rounding of up to 2^-8 |o| per element).
+    a rounding of up to 2^-8 |o| per element).  ``intra="jacobi"`` selects the
+    frame-level transition (see gdn.h).
     """
     torch = _torch()
     p, (B, T, H, dk, dv), odt = _prepare(q, k, v, log_gate, beta, frames, tokens_per_frame,
-                                         out_dtype, algo, key_scale)
+                                         out_dtype, algo, key_scale, intra)
     d = DIRECTION[direction]
     shape = (B, H, dk, dv)
     initial_state = _state_tensor(initial_state, shape, "initial_state")
@@ -250,14 +255,14 @@ def forward(q, k, v, log_gate, beta, initial_state=None, direction="bidir", *, f
 
 
 def step(q, k, v, log_gate, beta, state_in=None, state_out=None, *, key_scale=1.0,
-         out_dtype=None, algo="auto", out=None, workspace=None):
+         out_dtype=None, algo="auto", out=None, workspace=None, intra="sequential"):
     """One frame of the chunk-causal forward scan (gdn_step); returns (out, state_out).
 
     The inputs hold exactly one frame ([B,S,H,d]); state_out may be state_in.
     """
     torch = _torch()
     p, (B, T, H, dk, dv), odt = _prepare(q, k, v, log_gate, beta, 1, None, out_dtype, algo,
-                                         key_scale)
+                                         key_scale, intra)
     shape = (B, H, dk, dv)
     state_in = _state_tensor(state_in, shape, "state_in")
     if state_out is None:

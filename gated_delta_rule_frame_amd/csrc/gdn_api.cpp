@@ -30,8 +30,10 @@ gdn_status check_problem(const gdn_problem* pr, int direction, gdn::Problem* out
   if (!pr) return fail(GDN_ERR_INVALID_ARGUMENT, "problem is NULL");
   if (pr->abi_version != GDN_ABI_VERSION)
     return fail(GDN_ERR_INVALID_ARGUMENT, "abi_version %d != %d", pr->abi_version, GDN_ABI_VERSION);
-  for (int i = 0; i < 5; ++i)
+  for (int i = 0; i < 4; ++i)
     if (pr->reserved[i] != 0) return fail(GDN_ERR_INVALID_ARGUMENT, "reserved[%d] is not zero", i);
+  if (pr->intra != GDN_INTRA_SEQUENTIAL && pr->intra != GDN_INTRA_JACOBI)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "unknown intra %d", pr->intra);
   if (pr->batch < 1 || pr->heads < 1 || pr->frames < 1 || pr->tokens_per_frame < 1)
     return fail(GDN_ERR_INVALID_ARGUMENT, "batch, heads, frames and tokens_per_frame must be >= 1 "
                 "(got %d, %d, %d, %d)", pr->batch, pr->heads, pr->frames, pr->tokens_per_frame);
@@ -64,12 +66,21 @@ gdn_status check_problem(const gdn_problem* pr, int direction, gdn::Problem* out
   out->qkv_bf16 = pr->qkv_dtype == GDN_BF16;
   out->out_bf16 = pr->out_dtype == GDN_BF16;
   out->key_scale = pr->key_scale;
+  out->jacobi = pr->intra == GDN_INTRA_JACOBI;
   return GDN_OK;
 }
 
-enum class Path { Recurrent, Chunked };
+enum class Path { Recurrent, Chunked, Jacobi };
 
 gdn_status choose_path(const gdn_problem* pr, const gdn::Problem& p, Path* path) {
+  if (p.jacobi) {
+    if (pr->algo == GDN_ALGO_RECURRENT)
+      return fail(GDN_ERR_UNSUPPORTED, "the frame-level transition has no token-recurrent path");
+    const char* why = gdn::jacobi_unsupported_reason(p);
+    if (why) return fail(GDN_ERR_UNSUPPORTED, "frame-level path: %s", why);
+    *path = Path::Jacobi;
+    return GDN_OK;
+  }
   if (pr->algo == GDN_ALGO_RECURRENT) { *path = Path::Recurrent; return GDN_OK; }
   if (pr->algo == GDN_ALGO_AUTO && !p.qkv_bf16) { *path = Path::Recurrent; return GDN_OK; }
   const char* why = gdn::chunked_unsupported_reason(p);
@@ -83,8 +94,9 @@ gdn_status choose_path(const gdn_problem* pr, const gdn::Problem& p, Path* path)
 }
 
 size_t workspace_for(Path path, const gdn::Problem& p, int direction) {
-  return path == Path::Chunked ? gdn::chunked_workspace(p, direction)
-                               : gdn::recurrent_workspace(p, direction);
+  return path == Path::Chunked  ? gdn::chunked_workspace(p, direction)
+         : path == Path::Jacobi ? gdn::jacobi_workspace(p, direction)
+                                : gdn::recurrent_workspace(p, direction);
 }
 
 gdn_status run(const gdn_problem* pr, int direction, const gdn::Tensors& t, void* workspace,
@@ -106,8 +118,9 @@ gdn_status run(const gdn_problem* pr, int direction, const gdn::Tensors& t, void
     return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes needed, %zu given%s", need,
                 workspace_bytes, workspace ? "" : " (NULL)");
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = path == Path::Chunked ? gdn::chunked_launch(p, direction, t, workspace, st)
-                                       : gdn::recurrent_launch(p, direction, t, workspace, st);
+  hipError_t e = path == Path::Chunked  ? gdn::chunked_launch(p, direction, t, workspace, st)
+                 : path == Path::Jacobi ? gdn::jacobi_launch(p, direction, t, workspace, st)
+                                        : gdn::recurrent_launch(p, direction, t, workspace, st);
   if (e != hipSuccess) return fail(GDN_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
   g_last_error.clear();
   return GDN_OK;

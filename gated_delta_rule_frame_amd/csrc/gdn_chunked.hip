@@ -339,6 +339,17 @@ __device__ __forceinline__ void block_store(__amdgpu_buffer_rsrc_t r, uint32_t v
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, voff, soff, 0);
 }
 
+// Segment start states and the Q half of the segment maps are kept transposed
+// in the workspace (element [i][j] at [j][i]): an accumulator tile's four
+// values per lane (rows 4g .. 4g+3 of one column) are then four consecutive
+// floats, one 128-bit access instead of four.
+__device__ __forceinline__ f32x4 tile_load_t(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ void tile_store_t(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, f32x4 x) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x), r, voff, soff, 0);
+}
+
 // --- staging --------------------------------------------------------------------
 // Strip-wave thread j holds scan rows 2 (j / (D/8)) and 2 (j / (D/8)) + 1,
 // components 8 (j % (D/8)) .. + 7, of K, V and (output pass) Q, so that a
@@ -839,16 +850,19 @@ __device__ __forceinline__ void seg_map_body(Args a) {
     if (c + 1 < nsub) gram_stage_strips<D, false>(a, Bn, I);
     __syncthreads();
   }
-  // store X = [P | Q] (fp32, row-major [D][2D]; QO: the Q half)
+  // store X = [P | Q] ([D][2D], P row-major, Q transposed; QO: the Q half)
   const float* Xg = a.maps + ((((size_t)slot * a.B + b) * a.H + h) * a.NS + pos) * (size_t)D * (2 * D);
   const __amdgpu_buffer_rsrc_t xr = block_rsrc(Xg, D * 2 * D * 4);
   const uint32_t xo = (uint32_t)((4 * g * 2 * D + wave * 16 + cl) * 4);
-#pragma unroll
-  for (int j = 0; j < SPW; ++j)
+  if constexpr (!QO) {
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) block_store(xr, xo, (uint32_t)(((md * 16 + r) * 2 * D + (j + (QO ? 1 : 0)) * D) * 4), X[j][md][r]);
+      for (int r = 0; r < 4; ++r) block_store(xr, xo, (uint32_t)((md * 16 + r) * 2 * D * 4), X[0][md][r]);
+  }
+  const uint32_t xq = (uint32_t)(((wave * 16 + cl) * 2 * D + D + 4 * g) * 4);
+#pragma unroll
+  for (int md = 0; md < MD; ++md) tile_store_t(xr, xq, (uint32_t)(md * 16 * 4), X[JQ][md]);
 }
 
 // [P | Q] maps: one workgroup per CU (LDS and registers).
@@ -912,7 +926,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_chain_kernel(Args a) {
   const float* seed = (dir == 0 || a.dirs == 2) ? a.h0 : nullptr;
   const int col = 16 * wave + cl;
   const uint32_t so = (uint32_t)((4 * g * D + col) * 4);        // lane offset within a [D][D] state
-  const uint32_t xo = (uint32_t)((4 * g * NX + D + col) * 4);   // lane offset of Q within a [D][2D] map
+  const uint32_t xq = (uint32_t)((col * NX + D + 4 * g) * 4);   // lane offset of Q^T within a [D][2D] map
+  const uint32_t tso = (uint32_t)((col * D + 4 * g) * 4);       // lane offset within a transposed state
   const float* maps = a.maps + (((size_t)slot * a.B + b) * a.H + h) * (size_t)a.NS * D * NX;
   // PT: the reversed scan of a bidirectional call, which takes P_p as the
   // transpose of the forward scan's P of the same segment (its Q half is its
@@ -933,10 +948,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_chain_kernel(Args a) {
   }
   const __amdgpu_buffer_rsrc_t st = block_rsrc(starts, (uint32_t)a.NS * D * D * 4);
 
-  // Maps in flight.  P (float4 number threadIdx.x + NTH i) is fetched two
-  // steps ahead into two register sets used alternately (the loop is unrolled
-  // by two so that no set is ever copied: a copy would wait for its loads);
-  // Q, this lane's accumulator-layout tiles, one step ahead.
+  // Maps in flight, one step ahead: P (float4 number threadIdx.x + NTH i) and
+  // Q (this lane's accumulator-layout tiles).
   typedef float4 PRegs[MD];
   // Thread element f = threadIdx.x + NTH i holds row `row`, columns 4 c4 ..
   // 4 c4 + 3 of the staged P; transposed, those are one column of four rows
@@ -962,9 +975,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_chain_kernel(Args a) {
   auto fetch_q = [&](int p, f32x4 (&q)[MD]) {
     const __amdgpu_buffer_rsrc_t m = block_rsrc(maps + (size_t)p * D * NX, D * NX * 4);
 #pragma unroll
-    for (int md = 0; md < MD; ++md)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) q[md][rr] = block_load(m, xo, (uint32_t)((16 * md + rr) * NX * 4));
+    for (int md = 0; md < MD; ++md) q[md] = tile_load_t(m, xq, (uint32_t)(16 * md * 4));
   };
   auto stage = [&](int buf, const PRegs& r) {
     bh* phi = reinterpret_cast<bh*>(smem + buf * 2 * C::MAT);
@@ -982,16 +993,14 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_chain_kernel(Args a) {
 
   const int nsteps = a.NS - 1;
   auto last = [&](int p) { return p < nsteps ? p : nsteps - 1; };   // clamped map index
-  PRegs ra, rb;
+  PRegs pr;       // P of the next step's map
   f32x4 qn[MD];   // Q of the current step's map, then of the next one
-  // Step p: H_{p+1} = P_p H_p + Q_p with P_p staged in LDS buffer p & 1; `cur`
-  // receives P_{p+2}, and `nxt` holds P_{p+1}, staged at the end of the step.
-  auto step = [&](int p, PRegs& cur, PRegs& nxt) {
+  // Step p: H_{p+1} = P_p H_p + Q_p with P_p staged in LDS buffer p & 1;
+  // P_{p+1} is fetched meanwhile and staged at the end of the step.
+  auto step = [&](int p) {
     // start state of segment p
 #pragma unroll
-    for (int md = 0; md < MD; ++md)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) block_store(st, so, (uint32_t)((p * D + 16 * md + rr) * D * 4), H[md][rr]);
+    for (int md = 0; md < MD; ++md) tile_store_t(st, tso, (uint32_t)((p * D * D + 16 * md) * 4), H[md]);
     s16x4_t hh[2 * NP], hl[2 * NP];
 #pragma unroll
     for (int t = 0; t < 2 * NP; ++t) {
@@ -1006,47 +1015,57 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_chain_kernel(Args a) {
 #pragma unroll
     for (int md = 0; md < MD; ++md) acc[md] = qn[md];
     fetch_q(last(p + 1), qn);
-    fetch_p(last(p + 2), cur);
+    fetch_p(last(p + 1), pr);
     const bh* phi = reinterpret_cast<const bh*>(smem + (p & 1) * 2 * C::MAT);
     const bh* plo = phi + C::MAT / 2;
 #pragma unroll
     for (int q = 0; q < NP; ++q) {
       const bf16x8_t bhi = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(hh[2 * q], hh[2 * q + 1], 0, 1, 2, 3, 4, 5, 6, 7));
       const bf16x8_t blo = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(hl[2 * q], hl[2 * q + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+      // Tiles in groups of up to 4, each of the three products over the whole
+      // group before the next: consecutive MFMAs update different
+      // accumulators (three dependent ones in a row each wait for the last).
+      constexpr int GRP = 4;
 #pragma unroll
-      for (int md = 0; md < MD; ++md) {
-        const bf16x8_t ahi = fragB2(phi + (16 * md + cl) * LDC, 2 * q, g);
-        const bf16x8_t alo = fragB2(plo + (16 * md + cl) * LDC, 2 * q, g);
-        acc[md] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bhi, acc[md], 0, 0, 0);
-        acc[md] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, blo, acc[md], 0, 0, 0);
-        acc[md] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bhi, acc[md], 0, 0, 0);
+      for (int m0 = 0; m0 < MD; m0 += GRP) {
+        bf16x8_t ahi[GRP], alo[GRP];
+#pragma unroll
+        for (int i = 0; i < GRP; ++i)
+          if (m0 + i < MD) {
+            ahi[i] = fragB2(phi + (16 * (m0 + i) + cl) * LDC, 2 * q, g);
+            alo[i] = fragB2(plo + (16 * (m0 + i) + cl) * LDC, 2 * q, g);
+          }
+#pragma unroll
+        for (int i = 0; i < GRP; ++i)
+          if (m0 + i < MD) acc[m0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[i], bhi, acc[m0 + i], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < GRP; ++i)
+          if (m0 + i < MD) acc[m0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[i], blo, acc[m0 + i], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < GRP; ++i)
+          if (m0 + i < MD) acc[m0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[i], bhi, acc[m0 + i], 0, 0, 0);
       }
     }
 #pragma unroll
     for (int md = 0; md < MD; ++md) H[md] = acc[md];
-    stage((p + 1) & 1, nxt);
+    stage((p + 1) & 1, pr);
     __syncthreads();
   };
 
   if (nsteps > 0) {
-    fetch_p(0, ra);
+    fetch_p(0, pr);
     fetch_q(0, qn);
-    fetch_p(last(1), rb);
     __syncthreads();   // zero fill done
-    stage(0, ra);
+    stage(0, pr);
     __syncthreads();
   }
-  int p = 0;
-  for (; p + 1 < nsteps; p += 2) {
-    step(p, ra, rb);
-    step(p + 1, rb, ra);
-  }
-  if (p < nsteps) step(p, ra, rb);
+  // Drain the prologue's loads here, once: otherwise the wait the compiler
+  // needs for the seed state on the loop's entry path is placed at the loop
+  // header and executed every step, where it waits for the prefetched maps.
+  __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+  for (int p = 0; p < nsteps; ++p) step(p);
 #pragma unroll
-  for (int md = 0; md < MD; ++md)
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
-      block_store(st, so, (uint32_t)(((a.NS - 1) * D + 16 * md + rr) * D * 4), H[md][rr]);
+  for (int md = 0; md < MD; ++md) tile_store_t(st, tso, (uint32_t)(((a.NS - 1) * D * D + 16 * md) * 4), H[md]);
 }
 
 // ---------------------------------------------------------------------------
@@ -1087,10 +1106,9 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
     if (!helper) {
       const float* stp = a.starts + ((((size_t)slot * a.B + b) * a.H + h) * a.NS + pos) * (size_t)D * D;
       const __amdgpu_buffer_rsrc_t hr = block_rsrc(stp, D * D * 4);
+      const uint32_t tso = (uint32_t)((col * D + 4 * g) * 4);   // starts are transposed
 #pragma unroll
-      for (int md = 0; md < MD; ++md)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) H[0][md][r] = block_load(hr, so, (uint32_t)((md * 16 + r) * D * 4));
+      for (int md = 0; md < MD; ++md) H[0][md] = tile_load_t(hr, tso, (uint32_t)(md * 16 * 4));
     }
     auto piece = [&](int jj) {   // sub-chunk jj of the scan; past the segment: empty
       const int jc = rev ? nsub - 1 - jj : jj;
@@ -1251,6 +1269,255 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
 }
 
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// 4. Frame-level (Jacobi) transition.  [WM-summary] section 3.2, frame-wise
+// update: every token of a frame reads the frame's end state, and the frame
+// maps the state as H_end = gamma (I - c^2 K^T diag(beta) K) H + c K^T diag(beta) V
+// (one decay per frame: the gate of the frame's first token in the scan
+// order).  The per-frame maps are independent, the chain composes them over
+// the frames (the same kernel as above, with one "segment" per frame), and the
+// outputs of a frame are one product Q H_end; in a bidirectional call
+// O = Q (H_end^fwd + H_end^rev), the output being linear in the state.
+
+// Rows of one 64-token piece in the staging thread mapping (two rows and 8
+// components per thread): K, V and per-row beta.
+struct JacStage {
+  uint4 k[2], v[2];
+  float b[2];
+};
+
+template <int D>
+__device__ __forceinline__ void jac_fetch(const Args& a, int b, int h, long long t0, int n, JacStage& st) {
+  const int t = threadIdx.x, i2 = t / (D / 8), c8 = t % (D / 8);
+  const int HD = a.H * D;
+  const long long e0 = ((long long)b * a.T + t0) * HD + (long long)h * D;
+  const __amdgpu_buffer_rsrc_t rk = rows_rsrc(a.k + e0, (long long)n * HD * 2);
+  const __amdgpu_buffer_rsrc_t rv = rows_rsrc(a.v + e0, (long long)n * HD * 2);
+  const __amdgpu_buffer_rsrc_t rb = rows_rsrc(a.beta + ((long long)b * a.T + t0) * a.H + h, (long long)n * a.H * 4);
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int row = 2 * i2 + r;
+    const uint32_t off = (uint32_t)(row * HD * 2 + 16 * c8);
+    st.k[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+    st.v[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+    st.b[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, (uint32_t)(row * a.H * 4), 0, 0));
+  }
+}
+
+// Eight bf16 values times s, as fp16.
+__device__ __forceinline__ uint4 scaled_f16x8(uint4 x, float s) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __uint_as_float(w[i] << 16) * s, hi = __uint_as_float(w[i] & 0xffff0000u) * s;
+    o[i] = static_cast<uint32_t>(f2h(lo)) | (static_cast<uint32_t>(f2h(hi)) << 16);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// LDS of the map kernel: two buffers of K, c^2 beta K and c beta V rows (fp16,
+// the K-row layout above).
+template <int D>
+struct JacLay {
+  static constexpr int MAT = (KRows<D>::ELEMS * 2 + 15) / 16 * 16;
+  static constexpr int BUF = 3 * MAT;
+  static constexpr int BYTES = 2 * BUF;
+  static_assert(BYTES <= 160 * 1024, "workgroup LDS budget exceeded");
+};
+
+// grid (F, B * H), D/16 wavefronts: wave w accumulates column strip w of
+// M = c^2 K^T diag(beta) K and of N = c K^T diag(beta) V over the frame's
+// tokens, 64 at a time; both MFMA operands are transposing reads of the staged
+// rows (contraction over tokens, in the register-B token order).
+template <int D>
+__global__ __launch_bounds__(64 * (D / 16)) void jac_map_kernel(Args a) {
+  using J = JacLay<D>;
+  constexpr int MD = D / 16;
+  __shared__ __attribute__((aligned(16))) char smem[J::BYTES];
+  const int wave = wave_id(), lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
+  const int f = blockIdx.x, bh_ = blockIdx.y, b = bh_ / a.H, h = bh_ % a.H;
+  const int S = a.L, F = a.NS - 1;
+  const long long tf = (long long)f * S;
+  const int np = (S + CH - 1) / CH;
+  const float c = a.c;
+  for (int i = threadIdx.x; i < J::BYTES / 16; i += 64 * MD) reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
+  auto piece_n = [&](int p) { return p < np ? (S - CH * p < CH ? S - CH * p : CH) : 0; };
+  auto stage = [&](int buf, const JacStage& st) {
+    hb* kr = reinterpret_cast<hb*>(lds_at(smem, (uint32_t)(buf * J::BUF)));
+    hb* bk = kr + J::MAT / 2;
+    hb* bv = bk + J::MAT / 2;
+    const int t = threadIdx.x, i2 = t / (D / 8), c8 = t % (D / 8);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int o = krow<D>(2 * i2 + r) + 8 * c8;
+      *reinterpret_cast<uint4*>(kr + o) = bf16x8_to_f16x8(st.k[r]);
+      *reinterpret_cast<uint4*>(bk + o) = scaled_f16x8(st.k[r], c * c * st.b[r]);
+      *reinterpret_cast<uint4*>(bv + o) = scaled_f16x8(st.v[r], c * st.b[r]);
+    }
+  };
+  f32x4 acc[MD][2];
+#pragma unroll
+  for (int md = 0; md < MD; ++md) acc[md][0] = acc[md][1] = zero4();
+  JacStage st;
+  jac_fetch<D>(a, b, h, tf, piece_n(0), st);
+  __syncthreads();   // zero fill done
+  stage(0, st);
+  jac_fetch<D>(a, b, h, tf + CH, piece_n(1), st);
+  __syncthreads();
+  // lane (g, a + 4 j) addresses row 4 g + j, columns 4 a .. of a 16-column block
+  const int toff = krow<D>(4 * g + (cl >> 2)) + 4 * (cl & 3);
+  for (int p = 0; p < np; ++p) {
+    const hb* kr = reinterpret_cast<const hb*>(lds_at(smem, (uint32_t)((p & 1) * J::BUF))) + toff;
+    const hb* bk = kr + J::MAT / 2;
+    const hb* bv = bk + J::MAT / 2;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int r0 = krow<D>(32 * q), r1 = krow<D>(32 * q + 16);
+      const f16x8_t xm = cat8(ld4_tr(bk + r0 + 16 * wave), ld4_tr(bk + r1 + 16 * wave));
+      const f16x8_t xn = cat8(ld4_tr(bv + r0 + 16 * wave), ld4_tr(bv + r1 + 16 * wave));
+#pragma unroll
+      for (int md = 0; md < MD; ++md) {
+        const f16x8_t at = cat8(ld4_tr(kr + r0 + 16 * md), ld4_tr(kr + r1 + 16 * md));
+        acc[md][0] = mfma32(at, xm, acc[md][0]);
+        acc[md][1] = mfma32(at, xn, acc[md][1]);
+      }
+    }
+    if (p + 1 < np) stage((p + 1) & 1, st);
+    jac_fetch<D>(a, b, h, tf + (long long)CH * (p + 2), piece_n(p + 2), st);
+    __syncthreads();
+  }
+  // maps: forward scan (position f, decay of the frame's first token) and
+  // reversed scan (position F-1-f, decay of its last token)
+  const int col = 16 * wave + cl;
+  const uint32_t xo = (uint32_t)((4 * g * 2 * D + col) * 4);
+  const float* gg = a.g + ((long long)b * a.T + tf) * a.H + h;
+#pragma unroll
+  for (int dir = 0; dir < 2; ++dir) {
+    if (!(a.dirs & (1 << dir))) continue;
+    const int slot = slot_of_dir(a.dirs, dir);
+    const int pos = dir == 0 ? f : F - 1 - f;
+    const float gam = expf(gg[(long long)(dir == 0 ? 0 : S - 1) * a.H]);
+    const float* Xg = a.maps + ((((size_t)slot * a.B + b) * a.H + h) * a.NS + pos) * (size_t)D * (2 * D);
+    const __amdgpu_buffer_rsrc_t xr = block_rsrc(Xg, D * 2 * D * 4);
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * md + 4 * g + r;   // the lane offset xo holds the 4 g rows
+        block_store(xr, xo, (uint32_t)((16 * md + r) * 2 * D * 4), gam * ((row == col ? 1.f : 0.f) - acc[md][0][r]));
+      }
+    const uint32_t xq = (uint32_t)((col * 2 * D + D + 4 * g) * 4);   // Q^T
+#pragma unroll
+    for (int md = 0; md < MD; ++md) tile_store_t(xr, xq, (uint32_t)(md * 16 * 4), acc[md][1]);
+  }
+}
+
+// Outputs: grid (F, B * H), D/16 wavefronts; wave w owns output columns
+// 16 w .. 16 w + 15.  The frame's end state (summed over the scans present) is
+// split into fp16 hi + lo parts (about 22 significant bits) and each 64-row
+// piece of Q is multiplied by both.
+template <int D>
+__global__ __launch_bounds__(64 * (D / 16)) void jac_out_kernel(Args a) {
+  using G = Geo<D>;
+  constexpr int MD = D / 16;
+  constexpr int MAT = (KRows<D>::ELEMS * 2 + 15) / 16 * 16;
+  __shared__ __attribute__((aligned(16))) char smem[2 * MAT];
+  const int wave = wave_id(), lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
+  const int f = blockIdx.x, bh_ = blockIdx.y, b = bh_ / a.H, h = bh_ % a.H;
+  const int S = a.L, F = a.NS - 1;
+  const long long tf = (long long)f * S;
+  const int np = (S + CH - 1) / CH;
+  const int col = 16 * wave + cl;
+  const uint32_t so = (uint32_t)((4 * g * D + col) * 4);
+  const uint32_t tso = (uint32_t)((col * D + 4 * g) * 4);   // starts are transposed
+  const long long HD = (long long)a.H * D;
+  for (int i = threadIdx.x; i < 2 * MAT / 16; i += 64 * MD) reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
+  f32x4 Hs[MD];
+#pragma unroll
+  for (int md = 0; md < MD; ++md) Hs[md] = zero4();
+#pragma unroll
+  for (int dir = 0; dir < 2; ++dir) {
+    if (!(a.dirs & (1 << dir))) continue;
+    const int slot = slot_of_dir(a.dirs, dir);
+    const int pos_end = dir == 0 ? f + 1 : F - f;
+    const float* sp = a.starts + ((((size_t)slot * a.B + b) * a.H + h) * a.NS + pos_end) * (size_t)D * D;
+    const __amdgpu_buffer_rsrc_t hr = block_rsrc(sp, D * D * 4);
+#pragma unroll
+    for (int md = 0; md < MD; ++md) Hs[md] += tile_load_t(hr, tso, (uint32_t)(md * 16 * 4));
+  }
+  // final state of the scan reported (forward when present), from its last position
+  if (f == 0 && a.hT) {
+    const float* sp = a.starts + (((size_t)b * a.H + h) * a.NS + F) * (size_t)D * D;
+    const __amdgpu_buffer_rsrc_t hr = block_rsrc(sp, D * D * 4);
+    const __amdgpu_buffer_rsrc_t tr = block_rsrc(a.hT + ((size_t)b * a.H + h) * D * D, D * D * 4);
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+      const f32x4 v = tile_load_t(hr, tso, (uint32_t)(md * 16 * 4));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) block_store(tr, so, (uint32_t)((md * 16 + r) * D * 4), v[r]);
+    }
+  }
+  f32x4 Hl[MD];
+#pragma unroll
+  for (int md = 0; md < MD; ++md) {
+    const f16x4_t hi = tof16(Hs[md]);
+    Hl[md] = Hs[md] - f32x4{(float)hi[0], (float)hi[1], (float)hi[2], (float)hi[3]};
+  }
+  f16x8_t Ph[G::NP], Pl[G::NP];
+  state_pairs<D>(Hs, Ph);
+  state_pairs<D>(Hl, Pl);
+  // Q rows: thread (i2, c8) holds rows 2 i2, 2 i2 + 1, components 8 c8 ..
+  const int t = threadIdx.x, i2 = t / (D / 8), c8 = t % (D / 8);
+  auto piece_n = [&](int p) { return p < np ? (S - CH * p < CH ? S - CH * p : CH) : 0; };
+  auto fetch = [&](int p, uint4 (&qv)[2]) {
+    const __amdgpu_buffer_rsrc_t rq = rows_rsrc(a.q + ((long long)b * a.T + tf + CH * p) * HD + (long long)h * D,
+                                                (long long)piece_n(p) * HD * 2);
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      qv[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rq, (uint32_t)((2 * i2 + r) * HD * 2 + 16 * c8), 0, 0));
+  };
+  auto stage = [&](int buf, const uint4 (&qv)[2]) {
+    hb* qr = reinterpret_cast<hb*>(lds_at(smem, (uint32_t)(buf * MAT)));
+#pragma unroll
+    for (int r = 0; r < 2; ++r) *reinterpret_cast<uint4*>(qr + krow<D>(2 * i2 + r) + 8 * c8) = bf16x8_to_f16x8(qv[r]);
+  };
+  uint4 qv[2];
+  fetch(0, qv);
+  __syncthreads();   // zero fill done
+  stage(0, qv);
+  fetch(1, qv);
+  __syncthreads();
+  const bool half = a.out_bf16;
+  const long long esz = half ? 2 : 4;
+  for (int p = 0; p < np; ++p) {
+    const hb* qr = reinterpret_cast<const hb*>(lds_at(smem, (uint32_t)((p & 1) * MAT)));
+    f32x4 O[4], Ol[4];
+    state_times_rows_T<D>(qr, Ph, cl, g, O);
+    state_times_rows_T<D>(qr, Pl, cl, g, Ol);
+    const long long rowb = ((long long)b * a.T + tf + CH * p) * HD + (long long)h * D;
+    const __amdgpu_buffer_rsrc_t rs =
+        rows_rsrc(static_cast<char*>(a.out) + rowb * esz, (long long)piece_n(p) * HD * esz);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const f32x4 val = O[mt] + Ol[mt];
+      const uint32_t off = (uint32_t)(((16 * mt + cl) * (int)HD + 16 * wave + 4 * g) * esz);
+      if (half) {
+        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+        const u32x2_t w{f32_to_bf16_bits(val[0]) | ((uint32_t)f32_to_bf16_bits(val[1]) << 16),
+                        f32_to_bf16_bits(val[2]) | ((uint32_t)f32_to_bf16_bits(val[3]) << 16)};
+        __builtin_amdgcn_raw_buffer_store_b64(w, rs, off, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, val), rs, off, 0, 0);
+      }
+    }
+    if (p + 1 < np) stage((p + 1) & 1, qv);
+    fetch(p + 2, qv);
+    __syncthreads();
+  }
+}
+
 struct Plan {
   int L, NS, ndir, dirs;
   size_t maps_off, starts_off, acc_off, bytes;
@@ -1458,6 +1725,88 @@ hipError_t chunked_launch(const Problem& p, int direction, const Tensors& t, voi
 }
 
 int chunked_segment_tokens(const Problem& p, int direction) { return make_plan(p, direction).L; }
+
+// --- frame-level (Jacobi) path ----------------------------------------------
+namespace {
+struct JacPlan {
+  int ndir, dirs;
+  size_t maps_off, starts_off, bytes;
+};
+JacPlan jac_plan(const Problem& p, int direction) {
+  JacPlan pl{};
+  pl.dirs = direction == GDN_FORWARD ? 1 : direction == GDN_BACKWARD ? 2 : 3;
+  pl.ndir = pl.dirs == 3 ? 2 : 1;
+  const size_t per = (size_t)pl.ndir * p.B * p.H * (size_t)(p.F + 1);
+  pl.maps_off = 0;
+  pl.starts_off = align_up(per * p.dk * (p.dk + p.dv) * sizeof(float), 256);
+  pl.bytes = pl.starts_off + align_up(per * p.dk * p.dv * sizeof(float), 256);
+  return pl;
+}
+
+template <int D>
+hipError_t jac_launch_d(const Problem& p, const JacPlan& pl, const Tensors& t, char* ws, hipStream_t stream) {
+  Args a{};
+  a.q = static_cast<const bh*>(t.q);
+  a.k = static_cast<const bh*>(t.k);
+  a.v = static_cast<const bh*>(t.v);
+  a.g = t.g;
+  a.beta = t.beta;
+  a.h0 = t.h0;
+  a.out = t.out;
+  a.hT = t.hT;
+  a.maps = reinterpret_cast<float*>(ws + pl.maps_off);
+  a.starts = reinterpret_cast<float*>(ws + pl.starts_off);
+  a.T = p.T;
+  a.B = p.B;
+  a.H = p.H;
+  a.L = p.S;          // one frame per "segment"
+  a.NS = p.F + 1;     // chain positions: the start of every frame and the end state
+  a.dirs = pl.dirs;
+  a.out_bf16 = p.out_bf16 ? 1 : 0;
+  a.c = p.key_scale;
+  const unsigned bhc = (unsigned)(p.B * p.H);
+  hipError_t e;
+  prof_begin(stream, GDN_KERNEL_JAC_MAP);
+  hipLaunchKernelGGL((jac_map_kernel<D>), dim3(p.F, bhc), dim3(64 * (D / 16)), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  prof_end(stream, GDN_KERNEL_JAC_MAP);
+  a.slot0 = 0;
+  prof_begin(stream, GDN_KERNEL_SEG_CHAIN);
+  hipLaunchKernelGGL((seg_chain_kernel<D, false>), dim3(bhc, pl.ndir), dim3(64 * (D / 16)), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  prof_end(stream, GDN_KERNEL_SEG_CHAIN);
+  prof_begin(stream, GDN_KERNEL_JAC_OUT);
+  hipLaunchKernelGGL((jac_out_kernel<D>), dim3(p.F, bhc), dim3(64 * (D / 16)), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  prof_end(stream, GDN_KERNEL_JAC_OUT);
+  return hipSuccess;
+}
+}  // namespace
+
+const char* jacobi_unsupported_reason(const Problem& p) {
+  if (!p.qkv_bf16) return "q, k and v must be bf16";
+  if (p.dk != p.dv) return "d_k must equal d_v";
+  if (p.dk > 112) return "d_k = d_v must be at most 112";
+  if (p.B * (long long)p.H > 65535) return "batch * heads must be at most 65535";
+  return nullptr;
+}
+
+size_t jacobi_workspace(const Problem& p, int direction) { return jac_plan(p, direction).bytes; }
+
+hipError_t jacobi_launch(const Problem& p, int direction, const Tensors& t, void* workspace, hipStream_t stream) {
+  const JacPlan pl = jac_plan(p, direction);
+  char* ws = static_cast<char*>(workspace);
+  switch (p.dk) {
+    case 16: return jac_launch_d<16>(p, pl, t, ws, stream);
+    case 32: return jac_launch_d<32>(p, pl, t, ws, stream);
+    case 48: return jac_launch_d<48>(p, pl, t, ws, stream);
+    case 64: return jac_launch_d<64>(p, pl, t, ws, stream);
+    case 80: return jac_launch_d<80>(p, pl, t, ws, stream);
+    case 96: return jac_launch_d<96>(p, pl, t, ws, stream);
+    case 112: return jac_launch_d<112>(p, pl, t, ws, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 void set_segment_tokens(int tokens) { g_segment_override.store(tokens > 0 ? tokens : 0); }
 void set_concurrent_scans(bool on) { g_concurrent_scans.store(on); }

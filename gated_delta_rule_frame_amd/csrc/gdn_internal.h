@@ -17,6 +17,7 @@ struct Problem {
   bool qkv_bf16;       // q/k/v element type (else fp32)
   bool out_bf16;       // out element type (else fp32)
   float key_scale;
+  bool jacobi;         // frame-level transition (GDN_INTRA_JACOBI)
 };
 
 // Device pointers of one call.
@@ -42,6 +43,12 @@ const char* chunked_unsupported_reason(const Problem& p);
 size_t chunked_workspace(const Problem& p, int direction);
 hipError_t chunked_launch(const Problem& p, int direction, const Tensors& t,
                           void* workspace, hipStream_t stream);
+
+// Frame-level (Jacobi) transition (gdn_chunked.hip).
+const char* jacobi_unsupported_reason(const Problem& p);
+size_t jacobi_workspace(const Problem& p, int direction);
+hipError_t jacobi_launch(const Problem& p, int direction, const Tensors& t,
+                         void* workspace, hipStream_t stream);
 
 void set_segment_tokens(int tokens);
 void set_concurrent_scans(bool on);

@@ -81,6 +81,17 @@ enum { GDN_FORWARD = 0, GDN_BACKWARD = 1, GDN_BIDIRECTIONAL = 2 };    /* directi
  * products).  RECURRENT forces the token-sequential kernel (any dtype). */
 enum { GDN_ALGO_AUTO = 0, GDN_ALGO_CHUNKED = 1, GDN_ALGO_RECURRENT = 2 };
 
+/* Transition inside a frame.  SEQUENTIAL: the token-wise rule applied to every
+ * token in order ("SANA-WM ... Hybrid Linear Diffusion Transformer" summary,
+ * section 3.2, token-wise update).  JACOBI: the same page's frame-wise update,
+ * in which every token of a frame reads the frame's end state:
+ *   H_end = gamma (I - c^2 K^T diag(beta) K) H + c K^T diag(beta) V,  O = Q H_end
+ * (stored orientation, c = key_scale) with one decay per frame, gamma =
+ * exp(log_gate) of the frame's first token in the scan's order (the last
+ * token of the frame for the reversed scan).  JACOBI runs on the chunked
+ * machinery only: bf16 q/k/v, d_k = d_v <= 112, algo AUTO or CHUNKED. */
+enum { GDN_INTRA_SEQUENTIAL = 0, GDN_INTRA_JACOBI = 1 };
+
 typedef struct gdn_problem {
   int32_t abi_version;        /* must equal GDN_ABI_VERSION */
   int32_t batch;              /* B >= 1 */
@@ -93,7 +104,8 @@ typedef struct gdn_problem {
   int32_t out_dtype;          /* GDN_F32 or GDN_BF16 */
   int32_t algo;               /* GDN_ALGO_* */
   float key_scale;            /* keys are multiplied by this on load (finite) */
-  int32_t reserved[5];        /* must be zero */
+  int32_t intra;              /* GDN_INTRA_* (0 = SEQUENTIAL) */
+  int32_t reserved[4];        /* must be zero */
 } gdn_problem;
 
 /* Version of this ABI (GDN_ABI_VERSION of the built library). */
@@ -161,7 +173,9 @@ enum {
   GDN_KERNEL_SEG_CHAIN = 1,   /* chunked path: serial chain of segment maps */
   GDN_KERNEL_SEG_OUT = 2,     /* chunked path: outputs and final state */
   GDN_KERNEL_RECURRENT = 3,   /* token-sequential path */
-  GDN_KERNEL_COUNT = 4
+  GDN_KERNEL_JAC_MAP = 4,     /* frame-level path: per-frame maps */
+  GDN_KERNEL_JAC_OUT = 5,     /* frame-level path: outputs and final state */
+  GDN_KERNEL_COUNT = 6
 };
 gdn_status gdn_profile_enable(int32_t on);
 gdn_status gdn_profile_reset(void);

@@ -115,3 +115,25 @@ def test_step_requires_one_frame_and_state_out():
     assert L.gdn_step(ctypes.byref(p), *args, None, None, vp(FAKE), None, 0, None) \
         == G.ERR_INVALID_ARGUMENT
     assert "state_out" in L.gdn_last_error_message().decode()
+
+
+def test_frame_level_transition_validation_and_workspace():
+    """intra must be SEQUENTIAL or JACOBI; JACOBI needs bf16 q/k/v, d_k = d_v
+    <= 112 and no token-recurrent algorithm; its workspace holds maps and
+    states for every frame boundary of each scan."""
+    p = prob()
+    p.intra = 2
+    with pytest.raises(G.GdnError) as e:
+        G.workspace_size(p, "bidir")
+    assert e.value.status == G.ERR_INVALID_ARGUMENT
+    for kw in (dict(qkv_dtype=G.F32), dict(d_v=32), dict(d_k=128, d_v=128), dict(algo="recurrent")):
+        p = prob(intra="jacobi", **kw)
+        with pytest.raises(G.GdnError) as e:
+            G.workspace_size(p, "fwd")
+        assert e.value.status == G.ERR_UNSUPPORTED, kw
+    p = prob(intra="jacobi")      # B = 1, H = 2, d = 64, F = 3
+    maps = 2 * 1 * 2 * 4 * 64 * 128 * 4
+    states = 2 * 1 * 2 * 4 * 64 * 64 * 4
+    assert G.workspace_size(p, "bidir") == maps + states
+    assert G.workspace_size(p, "fwd") == (maps + states) // 2
+    assert call_forward(p, ws=FAKE, ws_bytes=maps + states - 1) == G.ERR_WORKSPACE_TOO_SMALL

@@ -163,6 +163,73 @@ def test_concurrent_scans_match_in_order_schedule():
     assert rel_err(b[0], ro) <= TOL["bf16"] and rel_err(b[1], rH) <= TOL["bf16"]
 
 
+# ---------------------------------------------------------------- frame-level (Jacobi) transition
+
+JAC = {
+    "clip60s": WORKLOADS[2].resized(frames=3, heads=3),
+    "ragged": WORKLOADS[1].resized(frames=4, tokens_per_frame=201, heads=2),
+    "batched": WORKLOADS[4].resized(frames=3, heads=3),     # d = 64, initial state
+    "short": WORKLOADS[4].resized(frames=2, tokens_per_frame=5, heads=2, h0_sigma=0.3),
+}
+
+
+def run_jacobi(w, x, direction, out_dtype=None):
+    d = to_device(x, w.qkv_dtype)
+    h0 = d["h0"] if np.any(x["h0"]) else None
+    out, hT = G.forward(d["q"], d["k"], d["v"], d["log_gate"], d["beta"], h0, direction,
+                        tokens_per_frame=w.tokens_per_frame, key_scale=w.tokens_per_frame ** -0.5,
+                        intra="jacobi", out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return to_numpy(out), to_numpy(hT)
+
+
+@pytest.mark.parametrize("name", list(JAC))
+@pytest.mark.parametrize("direction", ["fwd", "bwd", "bidir"])
+def test_jacobi_bf16(name, direction):
+    """The frame-level transition against the oracle's (key scale 1/sqrt(S),
+    the pages' spatial scale for unit-norm keys)."""
+    w = JAC[name]
+    x = make_inputs(w, 7)
+    o, hT = run_jacobi(w, x, direction)
+    a, h0 = oracle_args(x)
+    ro, rH = O.jacobi_forward(direction, *a, h0, key_scale=w.tokens_per_frame ** -0.5,
+                              tokens_per_frame=w.tokens_per_frame)
+    eo, eh = rel_err(o, ro), rel_err(hT, rH)
+    print(f"[parity] {w.name} jacobi {direction}: out {eo:.3e} state {eh:.3e}", flush=True)
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"], (eo, eh)
+
+
+def test_jacobi_step_chain_matches_forward():
+    """gdn_step with the frame-level transition, frame after frame with the
+    state carried in place, equals the whole-sequence forward scan."""
+    w = JAC["clip60s"].resized(h0_sigma=0.1)
+    x = make_inputs(w, 8)
+    d = to_device(x, w.qkv_dtype)
+    S, c = w.tokens_per_frame, w.tokens_per_frame ** -0.5
+    state = d["h0"].clone()
+    outs = []
+    for f in range(w.frames):
+        sl = slice(f * S, (f + 1) * S)
+        o, _ = G.step(*(d[n][:, sl].contiguous() for n in ("q", "k", "v", "log_gate", "beta")),
+                      state, state, key_scale=c, intra="jacobi")
+        outs.append(o)
+    o = to_numpy(torch.cat(outs, dim=1))
+    ro, rH = O.jacobi(*oracle_args(x)[0], x["h0"], key_scale=c, tokens_per_frame=S)
+    assert rel_err(o, ro) <= TOL["bf16"] and rel_err(to_numpy(state), rH) <= TOL["bf16"]
+    fo, fH = run_jacobi(w, x, "fwd")
+    assert np.array_equal(o, fo) and np.array_equal(to_numpy(state), fH)
+
+
+def test_jacobi_bf16_output():
+    w = JAC["batched"]
+    x = make_inputs(w, 9)
+    o, hT = run_jacobi(w, x, "bidir", out_dtype=torch.bfloat16)
+    ro, rH = O.jacobi_bidir(*oracle_args(x)[0], x["h0"], key_scale=w.tokens_per_frame ** -0.5,
+                            tokens_per_frame=w.tokens_per_frame)
+    bound = TOL["bf16"] + 2.0 ** -8 * np.max(np.abs(ro)) / np.sqrt(np.mean(ro * ro))
+    assert rel_err(o, ro) <= bound and rel_err(hT, rH) <= TOL["bf16"]
+
+
 FULL = [(1, "bidir", [0, 19]), (2, "bidir", [7]), (2, "fwd", [13]), (4, "bidir", [(0, 3), (1, 34)])]
 
 
