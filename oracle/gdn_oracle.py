@@ -42,7 +42,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["fwd", "bwd", "bidir", "step", "jacobi", "jacobi_bwd", "jacobi_bidir", "forward",
-           "jacobi_forward"]
+           "jacobi_forward", "chunk_causal", "chunk_bounds"]
 
 
 def _as64(x):
@@ -102,6 +102,42 @@ def bidir(q, k, v, log_gate, beta, h0=None, key_scale=1.0):
     of, Hf = fwd(q, k, v, log_gate, beta, h0, key_scale)
     ob, _ = bwd(q, k, v, log_gate, beta, None, key_scale)
     return of + ob, Hf
+
+
+def chunk_bounds(frames, first_chunk_frames, chunk_frames):
+    """Frame ranges [f0, f1) of the chunks: the first holds
+    ``first_chunk_frames`` frames, every later one ``chunk_frames`` (the last
+    may hold fewer)."""
+    out, f0 = [], 0
+    n = first_chunk_frames
+    while f0 < frames:
+        f1 = min(frames, f0 + n)
+        out.append((f0, f1))
+        f0, n = f1, chunk_frames
+    return out
+
+
+def chunk_causal(q, k, v, log_gate, beta, h0=None, key_scale=1.0, tokens_per_frame=None,
+                 first_chunk_frames=1, chunk_frames=1):
+    """Chunk-causal layer: a global forward scan from ``h0`` plus, for every
+    chunk of frames, a reversed scan over that chunk alone from a zero state;
+    outputs summed, final state the forward scan's.
+
+    [WM-summary] section 3.2, "Bidirectional and Chunk-Causal GDN Variants":
+    in chunk-causal mode the forward scan stays global while the reversed
+    scan is confined to the current chunk.  Chunk sizes (in latent frames)
+    follow the streaming release: a first chunk, then equal chunks.
+    """
+    T = np.asarray(q).shape[1]
+    S = T if tokens_per_frame is None else int(tokens_per_frame)
+    if T % S:
+        raise ValueError("token count is not a whole number of frames")
+    o, H = fwd(q, k, v, log_gate, beta, h0, key_scale)
+    for f0, f1 in chunk_bounds(T // S, first_chunk_frames, chunk_frames):
+        sl = slice(f0 * S, f1 * S)
+        ob, _ = bwd(*(np.asarray(x)[:, sl] for x in (q, k, v, log_gate, beta)), None, key_scale)
+        o[:, sl] += ob
+    return o, H
 
 
 def step(q, k, v, log_gate, beta, state_in, key_scale=1.0):

@@ -216,6 +216,47 @@ def test_P4b_reversed_jacobi_takes_the_gate_of_the_frame_last_token():
     assert np.max(np.abs(Hj2 - H2)) > 1e-3
 
 
+def test_P6_chunk_causal_single_chunk_is_bidirectional_and_per_token_chunks_add_the_token_term():
+    """One chunk spanning the sequence is the bidirectional layer; chunks of
+    one single-token frame add to the forward output exactly each token's
+    own reversed-scan term, the read of v beta k^T with q."""
+    w, x = tiny(seed=5)
+    h0 = 0.1 * np.random.default_rng(7).standard_normal(x["h0"].shape)
+    o, H = O.chunk_causal(*args(x), h0, tokens_per_frame=TINY.tokens_per_frame,
+                          first_chunk_frames=TINY.frames, chunk_frames=TINY.frames)
+    ob, Hb = O.bidir(*args(x), h0)
+    assert rel(o, ob) < 1e-12 and rel(H, Hb) < 1e-12
+    q, k, v, g, b = args(x)
+    o1, _ = O.chunk_causal(q, k, v, g, b, h0, tokens_per_frame=1)
+    of, _ = O.fwd(q, k, v, g, b, h0)
+    # a one-token reversed scan from zero: H = beta k v^T, o = H^T q = beta (q.k) v
+    q64, k64, v64, b64 = (np.asarray(t, dtype=np.float64) for t in (q, k, v, b))
+    own = (b64 * np.einsum("bthi,bthi->bth", q64, k64))[..., None] * v64
+    assert rel(o1, of + own) < 1e-12
+
+
+def test_P7_chunk_causal_outputs_do_not_depend_on_later_chunks():
+    """Causality at chunk granularity: changing the inputs of the last chunk
+    leaves every earlier chunk's outputs unchanged, and changes the last
+    chunk's."""
+    w, x = tiny(seed=6, frames=5, tokens_per_frame=4)
+    S = 4
+    kw = dict(tokens_per_frame=S, first_chunk_frames=2, chunk_frames=2)   # chunks 2, 2, 1
+    o, _ = O.chunk_causal(*args(x), **kw)
+    y = {n: np.array(x[n], copy=True) for n in x}
+    y["v"][:, 4 * S:] += 1.0
+    y["k"][:, 4 * S:] *= -1.0
+    o2, _ = O.chunk_causal(*args(y), **kw)
+    assert np.array_equal(o[:, :4 * S], o2[:, :4 * S])
+    assert np.max(np.abs(o[:, 4 * S:] - o2[:, 4 * S:])) > 1e-3
+    # the bidirectional layer is not causal: the same change reaches the first chunk
+    ob, _ = O.bidir(*args(x))
+    ob2, _ = O.bidir(*args(y))
+    assert np.max(np.abs(ob[:, :2 * S] - ob2[:, :2 * S])) > 1e-6
+    assert O.chunk_bounds(5, 2, 2) == [(0, 2), (2, 4), (4, 5)]
+    assert O.chunk_bounds(121, 4, 3)[:3] == [(0, 4), (4, 7), (7, 10)] and O.chunk_bounds(121, 4, 3)[-1] == (118, 121)
+
+
 def test_P5_same_key_twice_overwrites():
     rng = np.random.default_rng(17)
     d = 8
