@@ -90,6 +90,21 @@ def executed_flops(T, L, d, bh, ndir):
             "seg_chain_kernel": chain * bh * ndir}
 
 
+def chunk_causal_flops(T, S, L, d, bh, first, every):
+    """Per-call flops of the chunk-causal layer on the chunked path: the
+    forward scan's maps, chain and outputs, and the reversed scan's outputs
+    over each chunk of frames (its segments are the chunks: no maps, no
+    chain)."""
+    fl = executed_flops(T, L, d, bh, 1)
+    bounds, t0, n = [], 0, first * S
+    while t0 < T:
+        bounds.append((t0, min(T, t0 + n)))
+        t0, n = t0 + n, every * S
+    rev = sum(out_flops(min(64, e - a), d) for s0, s1 in bounds for a in range(s0, s1, 64) for e in [s1])
+    fl["seg_out_kernel"] += rev * bh
+    return fl
+
+
 def jacobi_flops(S, F, d, bh, ndir):
     """Algorithmic flops per call of the frame-level (Jacobi) path, per kernel:
     per frame c^2 K^T diag(beta) K and c K^T diag(beta) V (4 S d^2), the
@@ -153,7 +168,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="clip60s_121x880_h20d112")
-    ap.add_argument("--direction", default=None, choices=["fwd", "bwd", "bidir"])
+    ap.add_argument("--direction", default=None, choices=["fwd", "bwd", "bidir", "chunk_causal"])
+    ap.add_argument("--chunks", default="4,3",
+                    help="chunk_causal: frames of the first chunk and of every later chunk")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--segment", type=int, default=0, help="tokens per segment (0 = automatic)")
     ap.add_argument("--parity-head", type=int, default=7)
@@ -189,8 +206,10 @@ def main():
     B, T, H, dk, dv = w.batch, w.tokens, w.heads, w.d_k, w.d_v
     jac = args.intra == "jacobi"
     key_scale = w.tokens_per_frame ** -0.5 if jac else 1.0
+    first_cf, every_cf = (int(c) for c in args.chunks.split(","))
+    cc = direction == "chunk_causal"
     prob = G.make_problem(B, H, dk, dv, w.frames, w.tokens_per_frame, G.BF16 if w.qkv_dtype == "bf16" else G.F32,
-                          G.F32, "auto", key_scale, args.intra)
+                          G.F32, "auto", key_scale, args.intra, first_cf, every_cf)
     ws = torch.empty(max(G.workspace_size(prob, direction), 16), dtype=torch.uint8, device=dev)
     out = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
     hT = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
@@ -198,7 +217,7 @@ def main():
     def step():
         G.forward(d["q"], d["k"], d["v"], d["log_gate"], d["beta"], h0, direction,
                   tokens_per_frame=w.tokens_per_frame, out=out, final_state=hT, workspace=ws,
-                  key_scale=key_scale, intra=args.intra)
+                  key_scale=key_scale, intra=args.intra, first_chunk_frames=first_cf, chunk_frames=every_cf)
 
     # ---- parity on a sampled head + CPU baseline (the same oracle run)
     parity, cpu_baseline = None, None
@@ -214,6 +233,9 @@ def main():
             if jac:
                 ro, rH = O.jacobi_forward(direction, *a, x["h0"][:1, hh:hh + 1], key_scale=key_scale,
                                           tokens_per_frame=w.tokens_per_frame)
+            elif cc:
+                ro, rH = O.chunk_causal(*a, x["h0"][:1, hh:hh + 1], tokens_per_frame=w.tokens_per_frame,
+                                        first_chunk_frames=first_cf, chunk_frames=every_cf)
             else:
                 ro, rH = O.forward(direction, *a, x["h0"][:1, hh:hh + 1])
             cpu_s = time.perf_counter() - t0
@@ -260,7 +282,7 @@ def main():
         del src, dst
 
     tokens_per_s = B * T / (ms / 1e3)
-    ndir = 2 if direction == "bidir" else 1
+    ndir = 2 if direction in ("bidir", "chunk_causal") else 1
     L = G.segment_plan(prob, direction) if hasattr(G, "segment_plan") else None
     canon = canonical_flops(w.tokens_per_frame, dk, dv) * B * H * w.frames * ndir
     kern = {k: {"launches": n, "avg_ms": (t / n if n else None)} for k, (n, t) in prof.items() if n}
@@ -280,7 +302,8 @@ def main():
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS, "traffic": read_traffic(dom, w.name + "_jacobi"), "kernel": dom}
     elif "seg_out_kernel" in kern and L:
-        fl = executed_flops(T, L, dk, B * H, ndir)
+        fl = (chunk_causal_flops(T, w.tokens_per_frame, L, dk, B * H, first_cf, every_cf) if cc
+              else executed_flops(T, L, dk, B * H, ndir))
         flops_exec = sum(fl.values())   # per call
         per_launch = {}
         for k in fl:
@@ -315,6 +338,7 @@ def main():
             "inputs": f"{w.qkv_dtype} q/k/v, fp32 log-gate/beta/state, fp32 out; fp16 MFMA operands, fp32 accumulation",
             "segment_tokens": None if jac else L, "seed": args.seed,
             "intra": args.intra, "key_scale": key_scale,
+            "chunks_frames": [first_cf, every_cf] if cc else None,
         },
         "layer": {"canonical_gflop": canon / 1e9, "executed_gflop": (flops_exec or 0) / 1e9,
                   "credited_tflops": layer_tflops, "pct_peak": 100 * layer_tflops / PEAK_TFLOPS,

@@ -23,11 +23,11 @@ ABI_VERSION = 1
 
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = range(5)
 F32, BF16 = 0, 1
-FORWARD, BACKWARD, BIDIRECTIONAL = 0, 1, 2
+FORWARD, BACKWARD, BIDIRECTIONAL, CHUNK_CAUSAL = 0, 1, 2, 3
 ALGO = {"auto": 0, "chunked": 1, "recurrent": 2}
 INTRA = {"sequential": 0, "jacobi": 1}
-DIRECTION = {"fwd": FORWARD, "bwd": BACKWARD, "bidir": BIDIRECTIONAL,
-             FORWARD: FORWARD, BACKWARD: BACKWARD, BIDIRECTIONAL: BIDIRECTIONAL}
+DIRECTION = {"fwd": FORWARD, "bwd": BACKWARD, "bidir": BIDIRECTIONAL, "chunk_causal": CHUNK_CAUSAL,
+             FORWARD: FORWARD, BACKWARD: BACKWARD, BIDIRECTIONAL: BIDIRECTIONAL, CHUNK_CAUSAL: CHUNK_CAUSAL}
 
 
 class GdnError(RuntimeError):
@@ -42,7 +42,8 @@ class Problem(ctypes.Structure):
                 ("frames", ctypes.c_int32), ("tokens_per_frame", ctypes.c_int32),
                 ("qkv_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("algo", ctypes.c_int32), ("key_scale", ctypes.c_float),
-                ("intra", ctypes.c_int32), ("reserved", ctypes.c_int32 * 4)]
+                ("intra", ctypes.c_int32), ("first_chunk_frames", ctypes.c_int32),
+                ("chunk_frames", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2)]
 
 
 _lib = None
@@ -98,7 +99,8 @@ def _check(status):
 
 
 def make_problem(batch, heads, d_k, d_v, frames, tokens_per_frame, qkv_dtype=BF16,
-                 out_dtype=BF16, algo="auto", key_scale=1.0, intra="sequential"):
+                 out_dtype=BF16, algo="auto", key_scale=1.0, intra="sequential", first_chunk_frames=0,
+                 chunk_frames=0):
     p = Problem()
     p.abi_version = ABI_VERSION
     p.batch, p.heads, p.d_k, p.d_v = batch, heads, d_k, d_v
@@ -107,6 +109,7 @@ def make_problem(batch, heads, d_k, d_v, frames, tokens_per_frame, qkv_dtype=BF1
     p.algo = ALGO[algo] if isinstance(algo, str) else int(algo)
     p.key_scale = float(key_scale)
     p.intra = INTRA[intra] if isinstance(intra, str) else int(intra)
+    p.first_chunk_frames, p.chunk_frames = int(first_chunk_frames), int(chunk_frames)
     return p
 
 
@@ -176,7 +179,7 @@ def _ptr(t):
 
 
 def _prepare(q, k, v, log_gate, beta, frames, tokens_per_frame, out_dtype, algo, key_scale,
-             intra="sequential"):
+             intra="sequential", chunks=(0, 0)):
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v), ("log_gate", log_gate), ("beta", beta)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda:
@@ -201,7 +204,7 @@ def _prepare(q, k, v, log_gate, beta, frames, tokens_per_frame, out_dtype, algo,
         raise ValueError(f"frames * tokens_per_frame = {frames * tokens_per_frame} != T = {T}")
     odt = torch.float32 if out_dtype is None else out_dtype
     p = make_problem(B, H, dk, dv, frames, tokens_per_frame, _dtype_code(q),
-                     _dtype_code(torch.empty(0, dtype=odt)), algo, key_scale, intra)
+                     _dtype_code(torch.empty(0, dtype=odt)), algo, key_scale, intra, *chunks)
     return p, (B, T, H, dk, dv), odt
 
 
@@ -226,18 +229,21 @@ def _workspace(problem, direction, workspace, device):
 
 def forward(q, k, v, log_gate, beta, initial_state=None, direction="bidir", *, frames=None,
             tokens_per_frame=None, key_scale=1.0, out_dtype=None, algo="auto",
-            out=None, final_state=None, want_state=True, workspace=None, intra="sequential"):
+            out=None, final_state=None, want_state=True, workspace=None, intra="sequential",
+            first_chunk_frames=0, chunk_frames=0):
     """Whole-sequence layer forward (gdn_forward); returns (out, final_state).
 
     q, k: [B,T,H,d_k]; v: [B,T,H,d_v] (fp32 or bf16, one dtype); log_gate,
     beta: [B,T,H] fp32; initial_state: [B,H,d_k,d_v] fp32 or None (zeros).
     The output is fp32 unless ``out_dtype`` says otherwise (a bf16 output adds
     a rounding of up to 2^-8 |o| per element).  ``intra="jacobi"`` selects the
-    frame-level transition (see gdn.h).
+    frame-level transition; ``direction="chunk_causal"`` with
+    ``first_chunk_frames`` / ``chunk_frames`` the chunk-causal layer (see gdn.h).
     """
     torch = _torch()
     p, (B, T, H, dk, dv), odt = _prepare(q, k, v, log_gate, beta, frames, tokens_per_frame,
-                                         out_dtype, algo, key_scale, intra)
+                                         out_dtype, algo, key_scale, intra,
+                                         (first_chunk_frames, chunk_frames))
     d = DIRECTION[direction]
     shape = (B, H, dk, dv)
     initial_state = _state_tensor(initial_state, shape, "initial_state")

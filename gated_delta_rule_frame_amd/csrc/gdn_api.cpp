@@ -30,7 +30,7 @@ gdn_status check_problem(const gdn_problem* pr, int direction, gdn::Problem* out
   if (!pr) return fail(GDN_ERR_INVALID_ARGUMENT, "problem is NULL");
   if (pr->abi_version != GDN_ABI_VERSION)
     return fail(GDN_ERR_INVALID_ARGUMENT, "abi_version %d != %d", pr->abi_version, GDN_ABI_VERSION);
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
     if (pr->reserved[i] != 0) return fail(GDN_ERR_INVALID_ARGUMENT, "reserved[%d] is not zero", i);
   if (pr->intra != GDN_INTRA_SEQUENTIAL && pr->intra != GDN_INTRA_JACOBI)
     return fail(GDN_ERR_INVALID_ARGUMENT, "unknown intra %d", pr->intra);
@@ -48,8 +48,13 @@ gdn_status check_problem(const gdn_problem* pr, int direction, gdn::Problem* out
   if (!std::isfinite(pr->key_scale))
     return fail(GDN_ERR_INVALID_ARGUMENT, "key_scale is not finite");
   if (direction >= 0 && direction != GDN_FORWARD && direction != GDN_BACKWARD &&
-      direction != GDN_BIDIRECTIONAL)
+      direction != GDN_BIDIRECTIONAL && direction != GDN_CHUNK_CAUSAL)
     return fail(GDN_ERR_INVALID_ARGUMENT, "unknown direction %d", direction);
+  if (direction == GDN_CHUNK_CAUSAL && (pr->first_chunk_frames < 1 || pr->chunk_frames < 1))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "GDN_CHUNK_CAUSAL needs first_chunk_frames and chunk_frames >= 1 "
+                "(got %d, %d)", pr->first_chunk_frames, pr->chunk_frames);
+  if (direction == GDN_CHUNK_CAUSAL && pr->intra == GDN_INTRA_JACOBI)
+    return fail(GDN_ERR_UNSUPPORTED, "GDN_CHUNK_CAUSAL is built for the token-wise transition only");
   const long long T = (long long)pr->frames * pr->tokens_per_frame;
   // Element offsets are 64-bit in every kernel; keep each tensor well inside
   // the range the launch grids and workspace arithmetic assume.
@@ -67,6 +72,8 @@ gdn_status check_problem(const gdn_problem* pr, int direction, gdn::Problem* out
   out->out_bf16 = pr->out_dtype == GDN_BF16;
   out->key_scale = pr->key_scale;
   out->jacobi = pr->intra == GDN_INTRA_JACOBI;
+  out->first_chunk_frames = pr->first_chunk_frames;
+  out->chunk_frames = pr->chunk_frames;
   return GDN_OK;
 }
 

@@ -83,6 +83,8 @@ struct Args {
   int slot0;            // map and chain kernels: slot of blockIdx direction index 0
   int heads_rev;        // map and output kernels: visit the (batch, head) pairs in reversed order
   int npos;             // map and output kernels: segments in the launch (gridDim.x may be larger)
+  long long cs_first;   // output kernel, chunk-causal reversed scan: tokens of the first chunk
+  long long cs_len;     // ... and of every later chunk (0: segments of L tokens from the chain)
   int dir;              // output kernel: the scan direction of this launch (1: reversed)
   int mode;             // output kernel: 0 store outputs, 1 store the partial, 2 add the partial
   int out_bf16;
@@ -1084,8 +1086,12 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
   const int seg = blockIdx.x;
   if (seg >= a.npos) return;                        // padding of the grid (whole workgroup)
   const int bh_ = a.heads_rev ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y, b = bh_ / a.H, h = bh_ % a.H;
-  const long long s0 = (long long)seg * a.L;
-  const long long s1 = (s0 + a.L < a.T) ? s0 + a.L : a.T;
+  // A segment is L tokens whose start state the chain computed, or (the
+  // chunk-causal reversed scan) one chunk of frames, started from zero.
+  const bool chunks = a.cs_len > 0;
+  const long long s0 = !chunks ? (long long)seg * a.L : seg == 0 ? 0 : a.cs_first + (long long)(seg - 1) * a.cs_len;
+  const long long e0 = !chunks ? s0 + a.L : seg == 0 ? a.cs_first : s0 + a.cs_len;
+  const long long s1 = e0 < a.T ? e0 : a.T;
   const int nsub = (int)((s1 - s0 + CH - 1) / CH);
   const size_t sbase = ((size_t)b * a.H + h) * D * D;
   const Inv I = inv_at<D, true>(smem);
@@ -1103,7 +1109,10 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
     const int slot = slot_of_dir(a.dirs, dir);
     const int pos = rev ? a.NS - 1 - seg : seg;
     f32x4 H[SPW][MD];
-    if (!helper) {
+    if (!helper && chunks) {
+#pragma unroll
+      for (int md = 0; md < MD; ++md) H[0][md] = zero4();
+    } else if (!helper) {
       const float* stp = a.starts + ((((size_t)slot * a.B + b) * a.H + h) * a.NS + pos) * (size_t)D * D;
       const __amdgpu_buffer_rsrc_t hr = block_rsrc(stp, D * D * 4);
       const uint32_t tso = (uint32_t)((col * D + 4 * g) * 4);   // starts are transposed
@@ -1258,7 +1267,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
     }
     if (nsub > 0) flush(nsub - 1);
     // final state: the scan's last segment
-    if (a.hT && pos == a.NS - 1 && (dir == 0 || a.dirs == 2)) {
+    if (a.hT && !chunks && pos == a.NS - 1 && (dir == 0 || a.dirs == 2)) {
       const __amdgpu_buffer_rsrc_t hr = block_rsrc(a.hT + sbase, D * D * 4);
 #pragma unroll
       for (int md = 0; md < MD; ++md)
@@ -1520,12 +1529,14 @@ __global__ __launch_bounds__(64 * (D / 16)) void jac_out_kernel(Args a) {
 
 struct Plan {
   int L, NS, ndir, dirs;
+  bool cc;       // chunk-causal: forward maps and chain only; the reversed scan runs per chunk
   size_t maps_off, starts_off, acc_off, bytes;
 };
 
 Plan make_plan(const Problem& p, int direction) {
   Plan pl{};
-  pl.dirs = direction == GDN_FORWARD ? 1 : direction == GDN_BACKWARD ? 2 : 3;
+  pl.cc = direction == GDN_CHUNK_CAUSAL;
+  pl.dirs = direction == GDN_FORWARD || pl.cc ? 1 : direction == GDN_BACKWARD ? 2 : 3;
   pl.ndir = pl.dirs == 3 ? 2 : 1;
   int L = g_segment_override.load(std::memory_order_relaxed);
   if (L <= 0) {
@@ -1547,7 +1558,7 @@ Plan make_plan(const Problem& p, int direction) {
   const size_t bhd = (size_t)pl.ndir * p.B * p.H;
   const size_t maps = bhd * (size_t)pl.NS * p.dk * (p.dk + p.dv) * sizeof(float);
   const size_t starts = bhd * (size_t)pl.NS * p.dk * p.dv * sizeof(float);
-  const size_t acc = (pl.dirs == 3 && p.out_bf16) ? (size_t)p.B * p.T * p.H * p.dv * sizeof(float) : 0;
+  const size_t acc = ((pl.dirs == 3 || pl.cc) && p.out_bf16) ? (size_t)p.B * p.T * p.H * p.dv * sizeof(float) : 0;
   pl.maps_off = 0;
   pl.starts_off = align_up(maps, 256);
   pl.acc_off = pl.starts_off + align_up(starts, 256);
@@ -1662,6 +1673,55 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
     return hipSuccess;
   };
   hipError_t e = hipSuccess;
+  if (pl.cc) {
+    // Chunk-causal: the reversed scan needs no maps or chain (each chunk
+    // starts from zero), so it runs first, on the side stream, storing the
+    // partial, beside the forward maps and chain; the forward outputs add it.
+    const long long cf = (long long)p.first_chunk_frames * p.S, cl_ = (long long)p.chunk_frames * p.S;
+    const int nchunks = p.T <= cf ? 1 : 1 + (int)((p.T - cf + cl_ - 1) / cl_);
+    auto rev_chunks = [&](hipStream_t st) -> hipError_t {
+      Args r = a;
+      r.dir = 1;
+      r.mode = 1;
+      r.cs_first = cf;
+      r.cs_len = cl_;
+      r.npos = nchunks;
+      prof_begin(st, GDN_KERNEL_SEG_OUT);
+      hipLaunchKernelGGL((seg_out_kernel<D>), dim3(padded(nchunks), bhc, 1), dim3(Geo<D>::NT), 0, st, r);
+      const hipError_t e2 = hipGetLastError();
+      if (e2 != hipSuccess) return e2;
+      prof_end(st, GDN_KERNEL_SEG_OUT);
+      return hipSuccess;
+    };
+    auto fwd_out = [&](hipStream_t st) -> hipError_t {
+      a.dir = 0;
+      a.mode = 2;
+      a.heads_rev = 0;
+      a.npos = pl.NS;
+      prof_begin(st, GDN_KERNEL_SEG_OUT);
+      hipLaunchKernelGGL((seg_out_kernel<D>), dim3(padded(pl.NS), bhc, 1), dim3(Geo<D>::NT), 0, st, a);
+      const hipError_t e2 = hipGetLastError();
+      if (e2 != hipSuccess) return e2;
+      prof_end(st, GDN_KERNEL_SEG_OUT);
+      return hipSuccess;
+    };
+    Side* side = g_concurrent_scans.load(std::memory_order_relaxed) ? side_stream() : nullptr;
+    if (!side) {
+      if ((e = rev_chunks(stream)) != hipSuccess) return e;
+      if ((e = maps_k(0, stream)) != hipSuccess) return e;
+      if ((e = chain_k(0, stream)) != hipSuccess) return e;
+      return fwd_out(stream);
+    }
+    std::lock_guard<std::mutex> lk(side->mu);
+    if ((e = hipEventRecord(side->fork, stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(side->stream, side->fork, 0)) != hipSuccess) return e;
+    if ((e = rev_chunks(side->stream)) != hipSuccess) return e;
+    if ((e = hipEventRecord(side->join, side->stream)) != hipSuccess) return e;
+    if ((e = maps_k(0, stream)) != hipSuccess) return e;
+    if ((e = chain_k(0, stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(stream, side->join, 0)) != hipSuccess) return e;
+    return fwd_out(stream);
+  }
   if (!both) {
     if ((e = maps_k(0, stream)) != hipSuccess) return e;
     if ((e = chain_k(0, stream)) != hipSuccess) return e;

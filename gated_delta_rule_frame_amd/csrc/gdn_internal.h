@@ -18,6 +18,7 @@ struct Problem {
   bool out_bf16;       // out element type (else fp32)
   float key_scale;
   bool jacobi;         // frame-level transition (GDN_INTRA_JACOBI)
+  int first_chunk_frames, chunk_frames;   // GDN_CHUNK_CAUSAL chunking (frames)
 };
 
 // Device pointers of one call.

@@ -28,7 +28,7 @@ __global__ __launch_bounds__(64) void recurrent_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* h0,
     void* __restrict__ out, float* hT, float* __restrict__ acc, long long T, int H, int DV,
-    int reverse, int out_mode, int out_bf16, float key_scale) {
+    int reverse, int out_mode, int out_bf16, float key_scale, long long reset_first, long long reset_every) {
   constexpr int R = DK / 4;
   const int lane = threadIdx.x;
   const int c = lane & 15, r0 = lane >> 4;
@@ -69,6 +69,15 @@ __global__ __launch_bounds__(64) void recurrent_kernel(
     }
     __syncthreads();
     for (int j = 0; j < nt; ++j) {
+      if (reset_every > 0) {
+        // chunk-causal reversed scan: it restarts from zero at the last
+        // token of every chunk (chunk ends at reset_first + m reset_every)
+        const long long e1 = T - (t0 + j);   // one past the token, in original order
+        if (e1 == reset_first || (e1 > reset_first && (e1 - reset_first) % reset_every == 0)) {
+#pragma unroll
+          for (int m = 0; m < R; ++m) st[m] = 0.f;
+        }
+      }
       const float a = expf(gs[j]);
       float p = 0.f;
 #pragma unroll
@@ -107,7 +116,8 @@ __global__ __launch_bounds__(64) void recurrent_kernel(
 
 template <bool BF16IN>
 hipError_t launch_dk(const Problem& p, const Tensors& t, bool reverse, const float* h0, int out_mode,
-                     float* acc, bool write_state, hipStream_t stream) {
+                     float* acc, bool write_state, hipStream_t stream, long long reset_first = 0,
+                     long long reset_every = 0) {
   dim3 grid(p.dv / kCols, p.H, p.B), block(64);
   float* hT = write_state ? t.hT : nullptr;
   prof_begin(stream, GDN_KERNEL_RECURRENT);
@@ -115,7 +125,8 @@ hipError_t launch_dk(const Problem& p, const Tensors& t, bool reverse, const flo
   case D:                                                                                     \
     hipLaunchKernelGGL((recurrent_kernel<BF16IN, D>), grid, block, 0, stream, t.q, t.k, t.v, \
                        t.g, t.beta, h0, t.out,           hT, acc, p.T, p.H, p.dv,  \
-                       reverse ? 1 : 0, out_mode, p.out_bf16 ? 1 : 0, p.key_scale);           \
+                       reverse ? 1 : 0, out_mode, p.out_bf16 ? 1 : 0, p.key_scale,            \
+                       reset_first, reset_every);                                             \
     break;
   switch (p.dk) {
     GDN_REC_CASE(16) GDN_REC_CASE(32) GDN_REC_CASE(48) GDN_REC_CASE(64)
@@ -133,16 +144,16 @@ hipError_t launch_dk(const Problem& p, const Tensors& t, bool reverse, const flo
 size_t recurrent_workspace(const Problem& p, int direction) {
   // The bidirectional sum goes through an fp32 accumulator so that the output
   // is rounded once.
-  if (direction != GDN_BIDIRECTIONAL) return 0;
+  if (direction != GDN_BIDIRECTIONAL && direction != GDN_CHUNK_CAUSAL) return 0;
   return (size_t)p.B * p.T * p.H * p.dv * sizeof(float);
 }
 
 hipError_t recurrent_launch(const Problem& p, int direction, const Tensors& t, void* workspace,
                             hipStream_t stream) {
   float* acc = static_cast<float*>(workspace);
-  auto go = [&](bool reverse, const float* h0, int mode, bool state) {
-    return p.qkv_bf16 ? launch_dk<true>(p, t, reverse, h0, mode, acc, state, stream)
-                      : launch_dk<false>(p, t, reverse, h0, mode, acc, state, stream);
+  auto go = [&](bool reverse, const float* h0, int mode, bool state, long long rf = 0, long long re = 0) {
+    return p.qkv_bf16 ? launch_dk<true>(p, t, reverse, h0, mode, acc, state, stream, rf, re)
+                      : launch_dk<false>(p, t, reverse, h0, mode, acc, state, stream, rf, re);
   };
   if (direction == GDN_FORWARD) return go(false, t.h0, 0, true);
   // Backward-only mode: initial_state seeds the reversed scan.
@@ -151,6 +162,8 @@ hipError_t recurrent_launch(const Problem& p, int direction, const Tensors& t, v
   // then the reversed scan from zero adds to it and writes `out`.
   hipError_t e = go(false, t.h0, 1, true);
   if (e != hipSuccess) return e;
+  if (direction == GDN_CHUNK_CAUSAL)   // reversed scan confined to each chunk of frames
+    return go(true, nullptr, 2, false, (long long)p.first_chunk_frames * p.S, (long long)p.chunk_frames * p.S);
   return go(true, nullptr, 2, false);
 }
 

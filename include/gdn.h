@@ -74,7 +74,14 @@ enum {
 };
 
 enum { GDN_F32 = 0, GDN_BF16 = 1 };                                   /* tensor dtypes */
-enum { GDN_FORWARD = 0, GDN_BACKWARD = 1, GDN_BIDIRECTIONAL = 2 };    /* directions */
+/* Directions.  CHUNK_CAUSAL: the forward scan over the whole sequence plus,
+ * for every chunk of frames, a reversed scan confined to that chunk and
+ * started from zero, outputs summed; the final state is the forward scan's
+ * ("SANA-WM ... Hybrid Linear Diffusion Transformer" summary, section 3.2,
+ * "Bidirectional and Chunk-Causal GDN Variants").  The chunks are
+ * first_chunk_frames frames, then chunk_frames frames each (the last may be
+ * shorter); see gdn_problem. */
+enum { GDN_FORWARD = 0, GDN_BACKWARD = 1, GDN_BIDIRECTIONAL = 2, GDN_CHUNK_CAUSAL = 3 };
 
 /* Algorithm selection.  AUTO picks the frame-chunked MFMA path for bf16 q/k/v
  * and the token-recurrent fp32 path for fp32 q/k/v (whose tolerance needs fp32
@@ -105,7 +112,9 @@ typedef struct gdn_problem {
   int32_t algo;               /* GDN_ALGO_* */
   float key_scale;            /* keys are multiplied by this on load (finite) */
   int32_t intra;              /* GDN_INTRA_* (0 = SEQUENTIAL) */
-  int32_t reserved[4];        /* must be zero */
+  int32_t first_chunk_frames; /* GDN_CHUNK_CAUSAL: frames of the first chunk (>= 1), else ignored */
+  int32_t chunk_frames;       /* GDN_CHUNK_CAUSAL: frames of each later chunk (>= 1), else ignored */
+  int32_t reserved[2];        /* must be zero */
 } gdn_problem;
 
 /* Version of this ABI (GDN_ABI_VERSION of the built library). */

@@ -65,7 +65,7 @@ def test_bad_problem_fields_are_rejected(field, value):
 
 def test_reserved_and_key_scale_and_direction_checks():
     p = prob()
-    p.reserved[2] = 1
+    p.reserved[1] = 1
     with pytest.raises(G.GdnError):
         G.workspace_size(p, "bidir")
     p = prob(key_scale=float("nan"))
@@ -137,3 +137,22 @@ def test_frame_level_transition_validation_and_workspace():
     assert G.workspace_size(p, "bidir") == maps + states
     assert G.workspace_size(p, "fwd") == (maps + states) // 2
     assert call_forward(p, ws=FAKE, ws_bytes=maps + states - 1) == G.ERR_WORKSPACE_TOO_SMALL
+
+
+def test_chunk_causal_validation_and_workspace():
+    """GDN_CHUNK_CAUSAL needs chunk sizes >= 1 and the token-wise transition;
+    its chunked-path workspace holds one scan's maps and states (plus the fp32
+    partial for a bf16 output), its recurrent one the fp32 partial."""
+    n = ctypes.c_size_t()
+    p = prob()
+    assert G.lib().gdn_workspace_size(ctypes.byref(p), G.CHUNK_CAUSAL, ctypes.byref(n)) == G.ERR_INVALID_ARGUMENT
+    p = prob(first_chunk_frames=2, chunk_frames=0)
+    assert G.lib().gdn_workspace_size(ctypes.byref(p), G.CHUNK_CAUSAL, ctypes.byref(n)) == G.ERR_INVALID_ARGUMENT
+    p = prob(first_chunk_frames=2, chunk_frames=1, intra="jacobi")
+    assert G.lib().gdn_workspace_size(ctypes.byref(p), G.CHUNK_CAUSAL, ctypes.byref(n)) == G.ERR_UNSUPPORTED
+    p = prob(first_chunk_frames=2, chunk_frames=1, algo="recurrent")
+    assert G.workspace_size(p, "chunk_causal") == 1 * 300 * 2 * 64 * 4
+    p32 = prob(first_chunk_frames=2, chunk_frames=1, algo="chunked", out_dtype=G.F32)
+    pbf = prob(first_chunk_frames=2, chunk_frames=1, algo="chunked", out_dtype=G.BF16)
+    assert G.workspace_size(pbf, "chunk_causal") - G.workspace_size(p32, "chunk_causal") >= 1 * 300 * 2 * 64 * 4
+    assert G.workspace_size(p32, "chunk_causal") < G.workspace_size(p32, "bidir")

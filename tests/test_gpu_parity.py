@@ -163,6 +163,69 @@ def test_concurrent_scans_match_in_order_schedule():
     assert rel_err(b[0], ro) <= TOL["bf16"] and rel_err(b[1], rH) <= TOL["bf16"]
 
 
+# ---------------------------------------------------------------- chunk-causal layer
+
+CC = {
+    # name: (workload, first chunk frames, later chunk frames)
+    "clip60s_4_3": (WORKLOADS[2].resized(frames=8, heads=2), 4, 3),          # chunks 4, 3, 1
+    "ragged_2_2": (WORKLOADS[1].resized(frames=5, tokens_per_frame=201, heads=2), 2, 2),
+    "batched_1_1": (WORKLOADS[4].resized(frames=3, heads=3), 1, 1),         # d = 64, initial state
+    "one_chunk": (WORKLOADS[1].resized(frames=3, heads=2), 5, 5),           # = bidirectional
+}
+
+
+def run_cc(w, x, first, every, algo, out_dtype=None, qkv=None):
+    d = to_device(x, qkv or w.qkv_dtype)
+    h0 = d["h0"] if np.any(x["h0"]) else None
+    out, hT = G.forward(d["q"], d["k"], d["v"], d["log_gate"], d["beta"], h0, "chunk_causal",
+                        tokens_per_frame=w.tokens_per_frame, algo=algo, out_dtype=out_dtype,
+                        first_chunk_frames=first, chunk_frames=every)
+    torch.cuda.synchronize()
+    return to_numpy(out), to_numpy(hT)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("name", list(CC))
+def test_chunk_causal_bf16(algo, name):
+    w, first, every = CC[name]
+    x = make_inputs(w, 11)
+    o, hT = run_cc(w, x, first, every, algo)
+    ro, rH = O.chunk_causal(*oracle_args(x)[0], x["h0"], tokens_per_frame=w.tokens_per_frame,
+                            first_chunk_frames=first, chunk_frames=every)
+    eo, eh = rel_err(o, ro), rel_err(hT, rH)
+    print(f"[parity] {w.name} chunk-causal {first},{every} {algo}: out {eo:.3e} state {eh:.3e}", flush=True)
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"], (eo, eh)
+
+
+def test_chunk_causal_fp32_recurrent():
+    w = WORKLOADS[0]
+    x = make_inputs(w, 12)
+    o, hT = run_cc(w, x, 2, 1, "auto")
+    ro, rH = O.chunk_causal(*oracle_args(x)[0], x["h0"], tokens_per_frame=w.tokens_per_frame,
+                            first_chunk_frames=2, chunk_frames=1)
+    assert rel_err(o, ro) <= TOL["f32"] and rel_err(hT, rH) <= TOL["f32"]
+
+
+def test_chunk_causal_bf16_output_and_schedules():
+    """bf16 output through the fp32 partial; the concurrent and in-order
+    schedules give bit-identical results."""
+    w, first, every = CC["clip60s_4_3"]
+    x = make_inputs(w, 13)
+    G.set_segment_tokens(512)
+    try:
+        a = run_cc(w, x, first, every, "chunked", out_dtype=torch.bfloat16)
+        G.set_concurrent_scans(False)
+        b = run_cc(w, x, first, every, "chunked", out_dtype=torch.bfloat16)
+    finally:
+        G.set_concurrent_scans(True)
+        G.set_segment_tokens(0)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    ro, rH = O.chunk_causal(*oracle_args(x)[0], x["h0"], tokens_per_frame=w.tokens_per_frame,
+                            first_chunk_frames=first, chunk_frames=every)
+    bound = TOL["bf16"] + 2.0 ** -8 * np.max(np.abs(ro)) / np.sqrt(np.mean(ro * ro))
+    assert rel_err(a[0], ro) <= bound and rel_err(a[1], rH) <= TOL["bf16"]
+
+
 # ---------------------------------------------------------------- frame-level (Jacobi) transition
 
 JAC = {
