@@ -19,6 +19,10 @@ order): q, k ~ N(0,1) then L2-normalised per (b, t, h); v ~ N(0,1);
 u ~ U(lo, hi) with log-gate g = -u (per token, or per (b, frame, h) and shared
 by the frame's tokens); beta = sigmoid(sigma_beta * N(0,1)); initial state
 h0 = sigma_h0 * N(0,1) only when sigma_h0 > 0 (otherwise zeros, no draw).
+Raw projections (``qk_spread`` > 0, the inputs of the feature prologue): q and
+k are not normalised; after h0, m_q and m_k ~ N(0,1) per (b, t, h) are drawn
+and q, k are multiplied by exp(qk_spread * m_q), exp(qk_spread * m_k), so
+that token magnitudes vary over about a decade.
 For bf16 workloads q, k, v are then rounded to bf16 (round to nearest even)
 once; every consumer receives exactly those values.
 """
@@ -49,6 +53,7 @@ class Workload:
     h0_sigma: float           # initial state ~ h0_sigma * N(0,1); 0 -> zeros
     mode: str                 # how the layer is run on it: "bidir" or "step"
     description: str = ""
+    qk_spread: float = 0.0    # > 0: raw (unnormalised) q, k with log-normal token magnitudes
 
     @property
     def tokens(self) -> int:
@@ -102,8 +107,10 @@ def make_inputs(w: Workload, seed: int = 0) -> dict:
     """
     B, H, T, F, S = w.batch, w.heads, w.tokens, w.frames, w.tokens_per_frame
     rng = np.random.Generator(np.random.PCG64(seed))
-    q = _l2_normalise(rng.standard_normal((B, T, H, w.d_k), dtype=np.float32))
-    k = _l2_normalise(rng.standard_normal((B, T, H, w.d_k), dtype=np.float32))
+    q = rng.standard_normal((B, T, H, w.d_k), dtype=np.float32)
+    k = rng.standard_normal((B, T, H, w.d_k), dtype=np.float32)
+    if w.qk_spread <= 0:
+        q, k = _l2_normalise(q), _l2_normalise(k)
     v = rng.standard_normal((B, T, H, w.d_v), dtype=np.float32)
     if w.gate_per_frame:
         u = rng.uniform(w.gate_lo, w.gate_hi, (B, F, H))
@@ -117,6 +124,11 @@ def make_inputs(w: Workload, seed: int = 0) -> dict:
         h0 = (w.h0_sigma * rng.standard_normal((B, H, w.d_k, w.d_v))).astype(np.float32)
     else:
         h0 = np.zeros((B, H, w.d_k, w.d_v), dtype=np.float32)
+    if w.qk_spread > 0:
+        mq = rng.standard_normal((B, T, H, 1))
+        mk = rng.standard_normal((B, T, H, 1))
+        q = (q * np.exp(w.qk_spread * mq)).astype(np.float32)
+        k = (k * np.exp(w.qk_spread * mk)).astype(np.float32)
     if w.qkv_dtype == "bf16":
         q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
     elif w.qkv_dtype != "f32":

@@ -36,17 +36,55 @@ Readings taken where the pages are silent or ambiguous:
   * ``key_scale`` multiplies every key before use (1.0 = keys as given); the
     pages' spatial key scale is 1/sqrt(D*S) on RMS-normalised keys, which for
     unit-norm keys is 1/sqrt(S).
+  * Feature prologue (``key_features``, ``query_features``): the key features
+    are ReLU of the key RMS-normalised over its d_k components, per token and
+    head, with no learned weight (the pages give none) and
+    ``PROLOGUE_EPS`` added to the mean square; the queries are
+    L2-normalised per token and head with ``PROLOGUE_EPS`` added to the sum of
+    squares (the pages call them normalised queries without saying how; unit
+    L2 norm is the token-wise Gated DeltaNet practice they refer to).  The
+    spatial scale 1/sqrt(D*S) stays the separate ``key_scale``.
 """
 from __future__ import annotations
 
 import numpy as np
 
 __all__ = ["fwd", "bwd", "bidir", "step", "jacobi", "jacobi_bwd", "jacobi_bidir", "forward",
-           "jacobi_forward", "chunk_causal", "chunk_bounds"]
+           "jacobi_forward", "chunk_causal", "chunk_bounds", "key_features", "query_features",
+           "PROLOGUE_EPS"]
+
+PROLOGUE_EPS = 1e-6
 
 
 def _as64(x):
     return np.asarray(x, dtype=np.float64)
+
+
+def key_features(k, eps=PROLOGUE_EPS):
+    """Key features before the spatial scale: ReLU(RMSNorm(k)).
+
+    [WM-summary] section 3.2, "Algebraic Stabilization for Spatial Token
+    Explosion": the keys are RMS-normalised and ReLU-activated, so a key's
+    squared norm is about d_k, before the 1/sqrt(D*S) scale.  Per token and
+    head over the last axis:
+        kbar = max(k / sqrt(mean(k^2) + eps), 0)
+    NaN inputs stay NaN.
+    """
+    k = _as64(k)
+    rms = np.sqrt(np.mean(k * k, axis=-1, keepdims=True) + eps)
+    return np.maximum(k / rms, 0.0)
+
+
+def query_features(q, eps=PROLOGUE_EPS):
+    """Normalised queries: q / sqrt(sum(q^2) + eps) per token and head.
+
+    [WM-summary] section 3.2, "Frame-wise Gated DeltaNet (GDN)": the update
+    reads the state with the normalised query; the token-wise Gated DeltaNet
+    normalises queries (and keys) to unit L2 norm ("Algebraic Stabilization
+    for Spatial Token Explosion", on the standard 1/sqrt(D) normalisation).
+    """
+    q = _as64(q)
+    return q / np.sqrt(np.sum(q * q, axis=-1, keepdims=True) + eps)
 
 
 def fwd(q, k, v, log_gate, beta, h0=None, key_scale=1.0):

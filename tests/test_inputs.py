@@ -40,3 +40,15 @@ def test_distributions():
     assert ((x["beta"] > 0) & (x["beta"] < 1)).all()
     assert 0.05 < x["h0"].std() < 0.15
     assert (make_inputs(WORKLOADS[0], 0)["h0"] == 0).all()
+
+
+def test_raw_projections_for_the_feature_prologue():
+    """qk_spread > 0: q, k are left unnormalised with token magnitudes spread
+    over about a decade; the other tensors are drawn exactly as without it."""
+    w = WORKLOADS[2].resized(frames=2, tokens_per_frame=50, heads=3)
+    a, b = make_inputs(w, 5), make_inputs(w.resized(qk_spread=1.0), 5)
+    for n in ("v", "log_gate", "beta", "h0"):
+        assert np.array_equal(a[n], b[n])
+    nk = np.linalg.norm(b["k"].astype(np.float64), axis=-1)
+    assert nk.max() / nk.min() > 10 and np.array_equal(bf16_round(b["k"]), b["k"])
+    assert not np.allclose(np.linalg.norm(b["q"], axis=-1), 1, atol=0.1)

@@ -402,3 +402,88 @@ def test_pins_reject_planted_mistakes(kind):
     # and the unmutated recurrence passes both
     o_r, H_r = _mutant_fwd("none", *[sq(z) for z in a], h0[0, 0])
     assert np.allclose(o_r, np.array(WORKED_O, float), atol=1e-12)
+
+
+# ----------------------------------------------------- feature prologue (keys and queries)
+# [WM-summary] section 3.2, "Algebraic Stabilization for Spatial Token Explosion":
+# key features ReLU(RMSNorm(K)) with squared norm about d_k, then 1/sqrt(D*S).
+
+def _key_pins(kf):
+    """The key-feature pins, as a predicate on a candidate implementation."""
+    ok = True
+    # worked by hand: k = (3, -4, 0, 0): mean square 25/4, RMS 5/2
+    ok &= np.allclose(kf(np.array([3.0, -4.0, 0.0, 0.0]), 0.0), [1.2, 0.0, 0.0, 0.0], rtol=0, atol=1e-15)
+    ok &= np.allclose(kf(np.array([3.0, -4.0, 0.0, 0.0]), 1e-6), [3 / np.sqrt(6.25 + 1e-6), 0, 0, 0],
+                      rtol=0, atol=1e-15)
+    rng = np.random.default_rng(21)
+    k = rng.standard_normal((5, 7, 3, 112)) * np.exp(rng.standard_normal((5, 7, 3, 1)))
+    # a non-negative key keeps all of its energy: squared norm exactly d_k
+    ok &= np.allclose(np.sum(kf(np.abs(k), 0.0) ** 2, axis=-1), 112.0, rtol=1e-13, atol=0)
+    # ReLU splits a key's normalised components between k and -k
+    both = kf(k, 0.0) + kf(-k, 0.0)
+    ok &= np.allclose(both, np.abs(k) / np.sqrt(np.mean(k * k, axis=-1, keepdims=True)), rtol=1e-13, atol=0)
+    # scale invariance per token
+    ok &= np.allclose(kf(k * 7.5, 0.0), kf(k, 0.0), rtol=1e-13, atol=1e-15)
+    return bool(ok)
+
+
+def _query_pins(qf):
+    ok = True
+    ok &= np.allclose(qf(np.array([3.0, 4.0]), 0.0), [0.6, 0.8], rtol=0, atol=1e-15)
+    rng = np.random.default_rng(22)
+    q = rng.standard_normal((4, 5, 3, 64)) * np.exp(rng.standard_normal((4, 5, 3, 1)))
+    ok &= np.allclose(np.sum(qf(q, 0.0) ** 2, axis=-1), 1.0, rtol=1e-13, atol=0)
+    ok &= np.allclose(qf(-q, 0.0), -qf(q, 0.0), rtol=0, atol=0)          # odd: no ReLU on queries
+    ok &= np.allclose(qf(q * 0.03, 0.0), qf(q, 0.0), rtol=1e-13, atol=1e-15)
+    return bool(ok)
+
+
+def test_P8_key_features_by_hand_and_invariants():
+    assert _key_pins(O.key_features)
+    # zero key: zeros (eps keeps the division finite); NaN stays NaN
+    assert np.array_equal(O.key_features(np.zeros(16)), np.zeros(16))
+    assert np.all(np.isnan(O.key_features(np.array([1.0, np.nan, -2.0, 3.0]))))
+
+
+def test_P8_query_normalisation_by_hand_and_invariants():
+    assert _query_pins(O.query_features)
+    assert np.array_equal(O.query_features(np.zeros(16)), np.zeros(16))
+    # the default epsilon enters the sum of squares
+    assert np.isclose(O.query_features(np.array([1e-3, 0.0]))[0], 1e-3 / np.sqrt(1e-6 + 1e-6), rtol=1e-15)
+
+
+def test_P8_spatial_scale_bounds_the_frame_trace_by_one():
+    """Page claim: with RMS-normalised ReLU keys, beta <= 1 and the scale
+    1/sqrt(D*S), tr(K^T diag(beta) K) <= 1, so |I - K^T diag(beta) K|_2 <= 1;
+    the 1/sqrt(D) scale alone breaks it at S = 880."""
+    rng = np.random.default_rng(23)
+    S, d = 880, 112
+    raw = rng.standard_normal((S, d)) * np.exp(rng.standard_normal((S, 1)))
+    beta = 1 / (1 + np.exp(-2 * rng.standard_normal(S)))
+    kb = O.key_features(raw)
+    for scale, ok in ((1 / np.sqrt(d * S), True), (1 / np.sqrt(d), False)):
+        Ks = kb * scale
+        A = Ks.T @ (beta[:, None] * Ks)
+        assert (np.trace(A) <= 1.0) == ok
+        assert (np.linalg.norm(np.eye(d) - A, 2) <= 1 + 1e-12) == ok
+
+
+PROLOGUE_MUTANTS = {
+    "sum_not_mean": (lambda k, e: np.maximum(k / np.sqrt(np.sum(k * k, -1, keepdims=True) + e), 0), None),
+    "relu_before_norm": (lambda k, e: (lambda r: r / np.sqrt(np.mean(r * r, -1, keepdims=True) + e))(
+        np.maximum(k, 0)), None),
+    "no_relu": (lambda k, e: k / np.sqrt(np.mean(k * k, -1, keepdims=True) + e), None),
+    "abs_not_relu": (lambda k, e: np.abs(k) / np.sqrt(np.mean(k * k, -1, keepdims=True) + e), None),
+    "query_rms": (None, lambda q, e: q / np.sqrt(np.mean(q * q, -1, keepdims=True) + e)),
+    "query_relu": (None, lambda q, e: np.maximum(q / np.sqrt(np.sum(q * q, -1, keepdims=True) + e), 0)),
+    "query_unnormalised": (None, lambda q, e: q),
+}
+
+
+@pytest.mark.parametrize("kind", list(PROLOGUE_MUTANTS))
+def test_prologue_pins_reject_planted_mistakes(kind):
+    kf, qf = PROLOGUE_MUTANTS[kind]
+    if kf is not None:
+        assert not _key_pins(kf)
+    if qf is not None:
+        assert not _query_pins(qf)
