@@ -177,6 +177,9 @@ def main():
     ap.add_argument("--intra", default="sequential", choices=["sequential", "jacobi"],
                     help="transition inside a frame: token-wise (the layer) or the frame-level form; "
                          "jacobi runs with the spatial key scale 1/sqrt(tokens per frame)")
+    ap.add_argument("--prologue", default="none", choices=["none", "features"],
+                    help="features: raw (unnormalised) q/k through the fused key-feature and query "
+                         "normalisation prologue, with the spatial key scale 1/sqrt(d_k * tokens per frame)")
     ap.add_argument("--no-parity", action="store_true", help="skip the oracle check and CPU baseline")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after timing, run one device-to-device copy of this many bytes (counter calibration)")
@@ -193,6 +196,9 @@ def main():
     if not torch.cuda.is_available():
         sys.exit("bench.py needs a GPU")
     w = {wl.name: wl for wl in WORKLOADS}[args.workload]
+    pro = args.prologue == "features"
+    if pro:
+        w = w.resized(qk_spread=1.0)
     direction = args.direction or ("bidir" if w.mode == "bidir" else "fwd")
     dev = torch.device("cuda:0")
     G.set_segment_tokens(args.segment)
@@ -205,11 +211,11 @@ def main():
     h0 = torch.from_numpy(x["h0"]).to(dev) if np.any(x["h0"]) else None
     B, T, H, dk, dv = w.batch, w.tokens, w.heads, w.d_k, w.d_v
     jac = args.intra == "jacobi"
-    key_scale = w.tokens_per_frame ** -0.5 if jac else 1.0
+    key_scale = (dk * w.tokens_per_frame) ** -0.5 if pro else w.tokens_per_frame ** -0.5 if jac else 1.0
     first_cf, every_cf = (int(c) for c in args.chunks.split(","))
     cc = direction == "chunk_causal"
     prob = G.make_problem(B, H, dk, dv, w.frames, w.tokens_per_frame, G.BF16 if w.qkv_dtype == "bf16" else G.F32,
-                          G.F32, "auto", key_scale, args.intra, first_cf, every_cf)
+                          G.F32, "auto", key_scale, args.intra, first_cf, every_cf, args.prologue)
     ws = torch.empty(max(G.workspace_size(prob, direction), 16), dtype=torch.uint8, device=dev)
     out = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
     hT = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
@@ -217,7 +223,8 @@ def main():
     def step():
         G.forward(d["q"], d["k"], d["v"], d["log_gate"], d["beta"], h0, direction,
                   tokens_per_frame=w.tokens_per_frame, out=out, final_state=hT, workspace=ws,
-                  key_scale=key_scale, intra=args.intra, first_chunk_frames=first_cf, chunk_frames=every_cf)
+                  key_scale=key_scale, intra=args.intra, first_chunk_frames=first_cf, chunk_frames=every_cf,
+                  prologue=args.prologue)
 
     # ---- parity on a sampled head + CPU baseline (the same oracle run)
     parity, cpu_baseline = None, None
@@ -230,14 +237,17 @@ def main():
         a = [x[n][:1, :, hh:hh + 1] for n in ("q", "k", "v", "log_gate", "beta")]
         with threadpool_limits(1):
             t0 = time.perf_counter()
+            if pro:
+                a[0], a[1] = O.query_features(a[0]), O.key_features(a[1])
             if jac:
                 ro, rH = O.jacobi_forward(direction, *a, x["h0"][:1, hh:hh + 1], key_scale=key_scale,
                                           tokens_per_frame=w.tokens_per_frame)
             elif cc:
-                ro, rH = O.chunk_causal(*a, x["h0"][:1, hh:hh + 1], tokens_per_frame=w.tokens_per_frame,
+                ro, rH = O.chunk_causal(*a, x["h0"][:1, hh:hh + 1], key_scale=key_scale,
+                                        tokens_per_frame=w.tokens_per_frame,
                                         first_chunk_frames=first_cf, chunk_frames=every_cf)
             else:
-                ro, rH = O.forward(direction, *a, x["h0"][:1, hh:hh + 1])
+                ro, rH = O.forward(direction, *a, x["h0"][:1, hh:hh + 1], key_scale=key_scale)
             cpu_s = time.perf_counter() - t0
         o = out[:1, :, hh:hh + 1].double().cpu().numpy()
         s = hT[:1, hh:hh + 1].double().cpu().numpy()
@@ -316,6 +326,12 @@ def main():
         traffic = read_traffic(dom, w.name)
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_TFLOPS, "traffic": traffic, "kernel": dom}
+    if "prologue_kernel" in kern:
+        # algorithmic bytes: q and k read once, two fp32 factors per (token, head) written
+        esz = 2 if w.qkv_dtype == "bf16" else 4
+        pb = B * T * H * (2 * dk * esz + 8)
+        launches = kern["prologue_kernel"]["launches"] / args.steps
+        kern["prologue_kernel"]["gbs"] = pb / launches / (kern["prologue_kernel"]["avg_ms"] / 1e3) / 1e9
     credited = flops_exec if jac else (min(canon, flops_exec) if flops_exec else canon)
     layer_tflops = credited / (ms / 1e3) / 1e12
 
@@ -337,7 +353,7 @@ def main():
             "frames": w.frames, "tokens_per_frame": w.tokens_per_frame, "tokens": T,
             "inputs": f"{w.qkv_dtype} q/k/v, fp32 log-gate/beta/state, fp32 out; fp16 MFMA operands, fp32 accumulation",
             "segment_tokens": None if jac else L, "seed": args.seed,
-            "intra": args.intra, "key_scale": key_scale,
+            "intra": args.intra, "key_scale": key_scale, "prologue": args.prologue,
             "chunks_frames": [first_cf, every_cf] if cc else None,
         },
         "layer": {"canonical_gflop": canon / 1e9, "executed_gflop": (flops_exec or 0) / 1e9,

@@ -26,6 +26,7 @@ F32, BF16 = 0, 1
 FORWARD, BACKWARD, BIDIRECTIONAL, CHUNK_CAUSAL = 0, 1, 2, 3
 ALGO = {"auto": 0, "chunked": 1, "recurrent": 2}
 INTRA = {"sequential": 0, "jacobi": 1}
+PROLOGUE = {"none": 0, "features": 1}
 DIRECTION = {"fwd": FORWARD, "bwd": BACKWARD, "bidir": BIDIRECTIONAL, "chunk_causal": CHUNK_CAUSAL,
              FORWARD: FORWARD, BACKWARD: BACKWARD, BIDIRECTIONAL: BIDIRECTIONAL, CHUNK_CAUSAL: CHUNK_CAUSAL}
 
@@ -43,7 +44,8 @@ class Problem(ctypes.Structure):
                 ("qkv_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("algo", ctypes.c_int32), ("key_scale", ctypes.c_float),
                 ("intra", ctypes.c_int32), ("first_chunk_frames", ctypes.c_int32),
-                ("chunk_frames", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2)]
+                ("chunk_frames", ctypes.c_int32), ("prologue", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 1)]
 
 
 _lib = None
@@ -100,7 +102,7 @@ def _check(status):
 
 def make_problem(batch, heads, d_k, d_v, frames, tokens_per_frame, qkv_dtype=BF16,
                  out_dtype=BF16, algo="auto", key_scale=1.0, intra="sequential", first_chunk_frames=0,
-                 chunk_frames=0):
+                 chunk_frames=0, prologue="none"):
     p = Problem()
     p.abi_version = ABI_VERSION
     p.batch, p.heads, p.d_k, p.d_v = batch, heads, d_k, d_v
@@ -110,6 +112,7 @@ def make_problem(batch, heads, d_k, d_v, frames, tokens_per_frame, qkv_dtype=BF1
     p.key_scale = float(key_scale)
     p.intra = INTRA[intra] if isinstance(intra, str) else int(intra)
     p.first_chunk_frames, p.chunk_frames = int(first_chunk_frames), int(chunk_frames)
+    p.prologue = PROLOGUE[prologue] if isinstance(prologue, str) else int(prologue)
     return p
 
 
@@ -125,7 +128,7 @@ def set_segment_tokens(tokens: int) -> None:
 
 
 KERNELS = ("seg_map_kernel", "seg_chain_kernel", "seg_out_kernel", "recurrent_kernel", "jac_map_kernel",
-           "jac_out_kernel")
+           "jac_out_kernel", "prologue_kernel")
 
 
 def profile_enable(on: bool = True) -> None:
@@ -179,7 +182,7 @@ def _ptr(t):
 
 
 def _prepare(q, k, v, log_gate, beta, frames, tokens_per_frame, out_dtype, algo, key_scale,
-             intra="sequential", chunks=(0, 0)):
+             intra="sequential", chunks=(0, 0), prologue="none"):
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v), ("log_gate", log_gate), ("beta", beta)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda:
@@ -204,7 +207,7 @@ def _prepare(q, k, v, log_gate, beta, frames, tokens_per_frame, out_dtype, algo,
         raise ValueError(f"frames * tokens_per_frame = {frames * tokens_per_frame} != T = {T}")
     odt = torch.float32 if out_dtype is None else out_dtype
     p = make_problem(B, H, dk, dv, frames, tokens_per_frame, _dtype_code(q),
-                     _dtype_code(torch.empty(0, dtype=odt)), algo, key_scale, intra, *chunks)
+                     _dtype_code(torch.empty(0, dtype=odt)), algo, key_scale, intra, *chunks, prologue)
     return p, (B, T, H, dk, dv), odt
 
 
@@ -230,7 +233,7 @@ def _workspace(problem, direction, workspace, device):
 def forward(q, k, v, log_gate, beta, initial_state=None, direction="bidir", *, frames=None,
             tokens_per_frame=None, key_scale=1.0, out_dtype=None, algo="auto",
             out=None, final_state=None, want_state=True, workspace=None, intra="sequential",
-            first_chunk_frames=0, chunk_frames=0):
+            first_chunk_frames=0, chunk_frames=0, prologue="none"):
     """Whole-sequence layer forward (gdn_forward); returns (out, final_state).
 
     q, k: [B,T,H,d_k]; v: [B,T,H,d_v] (fp32 or bf16, one dtype); log_gate,
@@ -238,12 +241,14 @@ def forward(q, k, v, log_gate, beta, initial_state=None, direction="bidir", *, f
     The output is fp32 unless ``out_dtype`` says otherwise (a bf16 output adds
     a rounding of up to 2^-8 |o| per element).  ``intra="jacobi"`` selects the
     frame-level transition; ``direction="chunk_causal"`` with
-    ``first_chunk_frames`` / ``chunk_frames`` the chunk-causal layer (see gdn.h).
+    ``first_chunk_frames`` / ``chunk_frames`` the chunk-causal layer;
+    ``prologue="features"`` applies the key features ReLU(RMSNorm(k)) and the
+    query normalisation on load (see gdn.h).
     """
     torch = _torch()
     p, (B, T, H, dk, dv), odt = _prepare(q, k, v, log_gate, beta, frames, tokens_per_frame,
                                          out_dtype, algo, key_scale, intra,
-                                         (first_chunk_frames, chunk_frames))
+                                         (first_chunk_frames, chunk_frames), prologue)
     d = DIRECTION[direction]
     shape = (B, H, dk, dv)
     initial_state = _state_tensor(initial_state, shape, "initial_state")
@@ -261,14 +266,14 @@ def forward(q, k, v, log_gate, beta, initial_state=None, direction="bidir", *, f
 
 
 def step(q, k, v, log_gate, beta, state_in=None, state_out=None, *, key_scale=1.0,
-         out_dtype=None, algo="auto", out=None, workspace=None, intra="sequential"):
+         out_dtype=None, algo="auto", out=None, workspace=None, intra="sequential", prologue="none"):
     """One frame of the chunk-causal forward scan (gdn_step); returns (out, state_out).
 
     The inputs hold exactly one frame ([B,S,H,d]); state_out may be state_in.
     """
     torch = _torch()
     p, (B, T, H, dk, dv), odt = _prepare(q, k, v, log_gate, beta, 1, None, out_dtype, algo,
-                                         key_scale, intra)
+                                         key_scale, intra, (0, 0), prologue)
     shape = (B, H, dk, dv)
     state_in = _state_tensor(state_in, shape, "state_in")
     if state_out is None:

@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libgdn.so")
 BUILD = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["gdn_recurrent.hip", "gdn_chunked.hip"]
+HIP_SOURCES = ["gdn_recurrent.hip", "gdn_chunked.hip", "gdn_prologue.hip"]
 HOST_SOURCES = ["gdn_api.cpp", "gdn_profile.cpp"]
 
 

@@ -30,8 +30,9 @@ gdn_status check_problem(const gdn_problem* pr, int direction, gdn::Problem* out
   if (!pr) return fail(GDN_ERR_INVALID_ARGUMENT, "problem is NULL");
   if (pr->abi_version != GDN_ABI_VERSION)
     return fail(GDN_ERR_INVALID_ARGUMENT, "abi_version %d != %d", pr->abi_version, GDN_ABI_VERSION);
-  for (int i = 0; i < 2; ++i)
-    if (pr->reserved[i] != 0) return fail(GDN_ERR_INVALID_ARGUMENT, "reserved[%d] is not zero", i);
+  if (pr->reserved[0] != 0) return fail(GDN_ERR_INVALID_ARGUMENT, "reserved[0] is not zero");
+  if (pr->prologue != GDN_PROLOGUE_NONE && pr->prologue != GDN_PROLOGUE_FEATURES)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "unknown prologue %d", pr->prologue);
   if (pr->intra != GDN_INTRA_SEQUENTIAL && pr->intra != GDN_INTRA_JACOBI)
     return fail(GDN_ERR_INVALID_ARGUMENT, "unknown intra %d", pr->intra);
   if (pr->batch < 1 || pr->heads < 1 || pr->frames < 1 || pr->tokens_per_frame < 1)
@@ -74,6 +75,7 @@ gdn_status check_problem(const gdn_problem* pr, int direction, gdn::Problem* out
   out->jacobi = pr->intra == GDN_INTRA_JACOBI;
   out->first_chunk_frames = pr->first_chunk_frames;
   out->chunk_frames = pr->chunk_frames;
+  out->prologue = pr->prologue == GDN_PROLOGUE_FEATURES;
   return GDN_OK;
 }
 

@@ -89,6 +89,8 @@ struct Args {
   int mode;             // output kernel: 0 store outputs, 1 store the partial, 2 add the partial
   int out_bf16;
   float c;              // key scale
+  const float* fk;      // feature prologue: per-(token, head) key factors ([B][T][H]), or null
+  const float* fq;      // ... and query factors
 };
 
 // Wavefront index as a wave-uniform (scalar) value, so that branches on it are
@@ -362,6 +364,7 @@ __device__ __forceinline__ void tile_store_t(__amdgpu_buffer_rsrc_t r, uint32_t 
 // the segment, given as n = 0) read as zeros through the buffer range check.
 struct StageKQ {
   uint4 k[2], q[2];
+  float fk[2], fq[2];   // feature prologue factors of the two rows
 };
 struct StageV {
   uint4 v[2];
@@ -370,7 +373,7 @@ struct StageG {
   float g, b;
 };
 
-template <int D, bool OUT>
+template <int D, bool OUT, bool PRO>
 __device__ __forceinline__ void fetch_kq(const Args& a, int b, int h, const Sub& sb, StageKQ& st) {
   const int t = threadIdx.x, i2 = t / (D / 8), c8 = t % (D / 8);
   const int HD = a.H * D;
@@ -386,6 +389,18 @@ __device__ __forceinline__ void fetch_kq(const Args& a, int b, int h, const Sub&
     if constexpr (OUT) {
       const u32x4_t vq = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
       st.q[r] = make_uint4(vq[0], vq[1], vq[2], vq[3]);
+    }
+  }
+  if constexpr (PRO) {
+    const long long go = ((long long)b * a.T + sb.t0) * a.H + h;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const uint32_t fo = (uint32_t)((lr + sb.sgn * r) * a.H * 4);
+      st.fk[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                rows_rsrc(a.fk + go, (long long)sb.n * a.H * 4), fo, 0, 0));
+      if constexpr (OUT)
+        st.fq[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                  rows_rsrc(a.fq + go, (long long)sb.n * a.H * 4), fo, 0, 0));
     }
   }
 }
@@ -420,14 +435,18 @@ __device__ __forceinline__ void stage_v(const Buf& B, const StageV& st) {
   for (int r = 0; r < 2; ++r) *reinterpret_cast<uint4*>(B.vr + (2 * i2 + r) * Geo<D>::LDV + 8 * c8) = st.v[r];
 }
 
-// Write the staged rows into buffer B: K and Q as fp16.
-template <int D, bool OUT>
+// Write the staged rows into buffer B: K and Q as fp16 (PRO: the key
+// features ReLU(f_k k) and the normalised queries f_q q).
+template <int D, bool OUT, bool PRO>
 __device__ __forceinline__ void stage_kq(const Buf& B, const StageKQ& st) {
   const int t = threadIdx.x, i2 = t / (D / 8), c8 = t % (D / 8);
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
-    *reinterpret_cast<uint4*>(B.kr + krow<D>(2 * i2 + r) + 8 * c8) = bf16x8_to_f16x8(st.k[r]);
-    if constexpr (OUT) *reinterpret_cast<uint4*>(B.qr + krow<D>(2 * i2 + r) + 8 * c8) = bf16x8_to_f16x8(st.q[r]);
+    *reinterpret_cast<uint4*>(B.kr + krow<D>(2 * i2 + r) + 8 * c8) =
+        PRO ? bf16x8_scaled_f16x8<true>(st.k[r], st.fk[r]) : bf16x8_to_f16x8(st.k[r]);
+    if constexpr (OUT)
+      *reinterpret_cast<uint4*>(B.qr + krow<D>(2 * i2 + r) + 8 * c8) =
+          PRO ? bf16x8_scaled_f16x8<false>(st.q[r], st.fq[r]) : bf16x8_to_f16x8(st.q[r]);
   }
 }
 
@@ -728,7 +747,7 @@ __device__ __forceinline__ f32x4 vals_tile(const bh* vr, int mt, int w, int cl, 
 // QO: Q only (the reversed scan of a bidirectional call, whose P is the
 // transpose of the forward scan's: every token's factor a (I - b k k^T) is
 // symmetric, so the product in reversed order is the transposed product).
-template <int D, bool QO>
+template <int D, bool QO, bool PRO>
 __device__ __forceinline__ void seg_map_body(Args a) {
   using G = Geo<D>;
   using L = Lay<D, false>;
@@ -771,7 +790,7 @@ __device__ __forceinline__ void seg_map_body(Args a) {
     if (helper) {
       fetch_gates(a, b, h, s0b, sg);
     } else {
-      fetch_kq<D, false>(a, b, h, s0b, sk);
+      fetch_kq<D, false, PRO>(a, b, h, s0b, sk);
       fetch_v<D>(a, b, h, s0b, sv);
     }
     __syncthreads();
@@ -779,9 +798,9 @@ __device__ __forceinline__ void seg_map_body(Args a) {
       stage_gates(buf_at<D, false>(smem, 0), sg, a.c);
       fetch_gates(a, b, h, s1b, sg);
     } else {
-      stage_kq<D, false>(buf_at<D, false>(smem, 0), sk);
+      stage_kq<D, false, PRO>(buf_at<D, false>(smem, 0), sk);
       stage_v<D>(buf_at<D, false>(smem, 0), sv);
-      fetch_kq<D, false>(a, b, h, s1b, sk);
+      fetch_kq<D, false, PRO>(a, b, h, s1b, sk);
       fetch_v<D>(a, b, h, s1b, sv);
     }
     __syncthreads();
@@ -808,8 +827,8 @@ __device__ __forceinline__ void seg_map_body(Args a) {
     const Buf Bc = buf_at<D, false>(smem, c & 1), Bn = buf_at<D, false>(smem, (c + 1) & 1);
       const Inv I = inv_at<D, false>(smem);
     // alpha
-    stage_kq<D, false>(Bn, sk);
-    fetch_kq<D, false>(a, b, h, piece(c + 2), sk);
+    stage_kq<D, false, PRO>(Bn, sk);
+    fetch_kq<D, false, PRO>(a, b, h, piece(c + 2), sk);
     {
       f16x8_t Xp[SPW][G::NP];
 #pragma unroll
@@ -868,16 +887,16 @@ __device__ __forceinline__ void seg_map_body(Args a) {
 }
 
 // [P | Q] maps: one workgroup per CU (LDS and registers).
-template <int D>
+template <int D, bool PRO>
 __global__ __launch_bounds__(Geo<D>::NT) void seg_map_kernel(Args a) {
-  seg_map_body<D, false>(a);
+  seg_map_body<D, false, PRO>(a);
 }
 // Q-only maps: their LDS allows two workgroups per CU, and asking for four
 // wavefronts per SIMD caps the registers at 128 (a few spill at D = 112).
 // Measured at the 60 s clip: 0.27 ms against 0.40 ms with one workgroup per CU.
-template <int D>
+template <int D, bool PRO>
 __global__ __launch_bounds__(Geo<D>::NT) __attribute__((amdgpu_waves_per_eu(4))) void seg_map_q_kernel(Args a) {
-  seg_map_body<D, true>(a);
+  seg_map_body<D, true, PRO>(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -1076,7 +1095,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_chain_kernel(Args a) {
 // state of the chain.  In a bidirectional call the reversed scan stores its
 // outputs as a partial that the forward scan's launch adds to its own.
 // Strip wave w owns state columns 16 w .. 16 w + 15.
-template <int D>
+template <int D, bool PRO>
 __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
   using G = Geo<D>;
   using L = Lay<D, true>;
@@ -1132,7 +1151,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
       if (helper) {
         fetch_gates(a, b, h, s0b, sg);
       } else {
-        fetch_kq<D, true>(a, b, h, s0b, sk);
+        fetch_kq<D, true, PRO>(a, b, h, s0b, sk);
         fetch_v<D>(a, b, h, s0b, sv);
       }
       __syncthreads();
@@ -1140,9 +1159,9 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
         stage_gates(buf_at<D, true>(smem, 0), sg, a.c);
         fetch_gates(a, b, h, s1b, sg);
       } else {
-        stage_kq<D, true>(buf_at<D, true>(smem, 0), sk);
+        stage_kq<D, true, PRO>(buf_at<D, true>(smem, 0), sk);
         stage_v<D>(buf_at<D, true>(smem, 0), sv);
-        fetch_kq<D, true>(a, b, h, s1b, sk);
+        fetch_kq<D, true, PRO>(a, b, h, s1b, sk);
         fetch_v<D>(a, b, h, s1b, sv);
       }
       __syncthreads();
@@ -1215,10 +1234,10 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
       // alpha.  Staging first: it waits for the prefetched rows, which were
       // issued before the stores and loads below (the load counter drains in
       // issue order).
-      stage_kq<D, true>(Bn, sk);
+      stage_kq<D, true, PRO>(Bn, sk);
       if (c > 0) flush(c - 1);
       load_pre(c);
-      fetch_kq<D, true>(a, b, h, piece(c + 2), sk);
+      fetch_kq<D, true, PRO>(a, b, h, piece(c + 2), sk);
       {
         f16x8_t Hp[SPW][G::NP];
         state_pairs<D>(H[0], Hp[0]);
@@ -1292,10 +1311,10 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
 // components per thread): K, V and per-row beta.
 struct JacStage {
   uint4 k[2], v[2];
-  float b[2];
+  float b[2], fk[2];   // beta and (feature prologue) key factor of the rows
 };
 
-template <int D>
+template <int D, bool PRO>
 __device__ __forceinline__ void jac_fetch(const Args& a, int b, int h, long long t0, int n, JacStage& st) {
   const int t = threadIdx.x, i2 = t / (D / 8), c8 = t % (D / 8);
   const int HD = a.H * D;
@@ -1310,19 +1329,11 @@ __device__ __forceinline__ void jac_fetch(const Args& a, int b, int h, long long
     st.k[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
     st.v[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
     st.b[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, (uint32_t)(row * a.H * 4), 0, 0));
+    if constexpr (PRO) {
+      const __amdgpu_buffer_rsrc_t rf = rows_rsrc(a.fk + ((long long)b * a.T + t0) * a.H + h, (long long)n * a.H * 4);
+      st.fk[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rf, (uint32_t)(row * a.H * 4), 0, 0));
+    }
   }
-}
-
-// Eight bf16 values times s, as fp16.
-__device__ __forceinline__ uint4 scaled_f16x8(uint4 x, float s) {
-  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-  uint32_t o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float lo = __uint_as_float(w[i] << 16) * s, hi = __uint_as_float(w[i] & 0xffff0000u) * s;
-    o[i] = static_cast<uint32_t>(f2h(lo)) | (static_cast<uint32_t>(f2h(hi)) << 16);
-  }
-  return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 // LDS of the map kernel: two buffers of K, c^2 beta K and c beta V rows (fp16,
@@ -1339,7 +1350,7 @@ struct JacLay {
 // M = c^2 K^T diag(beta) K and of N = c K^T diag(beta) V over the frame's
 // tokens, 64 at a time; both MFMA operands are transposing reads of the staged
 // rows (contraction over tokens, in the register-B token order).
-template <int D>
+template <int D, bool PRO>
 __global__ __launch_bounds__(64 * (D / 16)) void jac_map_kernel(Args a) {
   using J = JacLay<D>;
   constexpr int MD = D / 16;
@@ -1360,19 +1371,22 @@ __global__ __launch_bounds__(64 * (D / 16)) void jac_map_kernel(Args a) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int o = krow<D>(2 * i2 + r) + 8 * c8;
-      *reinterpret_cast<uint4*>(kr + o) = bf16x8_to_f16x8(st.k[r]);
-      *reinterpret_cast<uint4*>(bk + o) = scaled_f16x8(st.k[r], c * c * st.b[r]);
-      *reinterpret_cast<uint4*>(bv + o) = scaled_f16x8(st.v[r], c * st.b[r]);
+      // PRO: key features ReLU(f_k k); the factor is positive, so the ReLU
+      // of the scaled row is the scaled ReLU
+      const float fk = PRO ? st.fk[r] : 1.f;
+      *reinterpret_cast<uint4*>(kr + o) = PRO ? bf16x8_scaled_f16x8<true>(st.k[r], fk) : bf16x8_to_f16x8(st.k[r]);
+      *reinterpret_cast<uint4*>(bk + o) = bf16x8_scaled_f16x8<PRO>(st.k[r], c * c * st.b[r] * fk);
+      *reinterpret_cast<uint4*>(bv + o) = bf16x8_scaled_f16x8<false>(st.v[r], c * st.b[r]);
     }
   };
   f32x4 acc[MD][2];
 #pragma unroll
   for (int md = 0; md < MD; ++md) acc[md][0] = acc[md][1] = zero4();
   JacStage st;
-  jac_fetch<D>(a, b, h, tf, piece_n(0), st);
+  jac_fetch<D, PRO>(a, b, h, tf, piece_n(0), st);
   __syncthreads();   // zero fill done
   stage(0, st);
-  jac_fetch<D>(a, b, h, tf + CH, piece_n(1), st);
+  jac_fetch<D, PRO>(a, b, h, tf + CH, piece_n(1), st);
   __syncthreads();
   // lane (g, a + 4 j) addresses row 4 g + j, columns 4 a .. of a 16-column block
   const int toff = krow<D>(4 * g + (cl >> 2)) + 4 * (cl & 3);
@@ -1393,7 +1407,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void jac_map_kernel(Args a) {
       }
     }
     if (p + 1 < np) stage((p + 1) & 1, st);
-    jac_fetch<D>(a, b, h, tf + (long long)CH * (p + 2), piece_n(p + 2), st);
+    jac_fetch<D, PRO>(a, b, h, tf + (long long)CH * (p + 2), piece_n(p + 2), st);
     __syncthreads();
   }
   // maps: forward scan (position f, decay of the frame's first token) and
@@ -1426,7 +1440,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void jac_map_kernel(Args a) {
 // 16 w .. 16 w + 15.  The frame's end state (summed over the scans present) is
 // split into fp16 hi + lo parts (about 22 significant bits) and each 64-row
 // piece of Q is multiplied by both.
-template <int D>
+template <int D, bool PRO>
 __global__ __launch_bounds__(64 * (D / 16)) void jac_out_kernel(Args a) {
   using G = Geo<D>;
   constexpr int MD = D / 16;
@@ -1479,6 +1493,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void jac_out_kernel(Args a) {
   // Q rows: thread (i2, c8) holds rows 2 i2, 2 i2 + 1, components 8 c8 ..
   const int t = threadIdx.x, i2 = t / (D / 8), c8 = t % (D / 8);
   auto piece_n = [&](int p) { return p < np ? (S - CH * p < CH ? S - CH * p : CH) : 0; };
+  // PRO: the query factors of the two rows ride along in fq
+  float fq[2] = {1.f, 1.f};
   auto fetch = [&](int p, uint4 (&qv)[2]) {
     const __amdgpu_buffer_rsrc_t rq = rows_rsrc(a.q + ((long long)b * a.T + tf + CH * p) * HD + (long long)h * D,
                                                 (long long)piece_n(p) * HD * 2);
@@ -1486,11 +1502,20 @@ __global__ __launch_bounds__(64 * (D / 16)) void jac_out_kernel(Args a) {
     for (int r = 0; r < 2; ++r)
       qv[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                             rq, (uint32_t)((2 * i2 + r) * HD * 2 + 16 * c8), 0, 0));
+    if constexpr (PRO) {
+      const __amdgpu_buffer_rsrc_t rf = rows_rsrc(a.fq + ((long long)b * a.T + tf + CH * p) * a.H + h,
+                                                  (long long)piece_n(p) * a.H * 4);
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        fq[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rf, (uint32_t)((2 * i2 + r) * a.H * 4), 0, 0));
+    }
   };
   auto stage = [&](int buf, const uint4 (&qv)[2]) {
     hb* qr = reinterpret_cast<hb*>(lds_at(smem, (uint32_t)(buf * MAT)));
 #pragma unroll
-    for (int r = 0; r < 2; ++r) *reinterpret_cast<uint4*>(qr + krow<D>(2 * i2 + r) + 8 * c8) = bf16x8_to_f16x8(qv[r]);
+    for (int r = 0; r < 2; ++r)
+      *reinterpret_cast<uint4*>(qr + krow<D>(2 * i2 + r) + 8 * c8) =
+          PRO ? bf16x8_scaled_f16x8<false>(qv[r], fq[r]) : bf16x8_to_f16x8(qv[r]);
   };
   uint4 qv[2];
   fetch(0, qv);
@@ -1530,7 +1555,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void jac_out_kernel(Args a) {
 struct Plan {
   int L, NS, ndir, dirs;
   bool cc;       // chunk-causal: forward maps and chain only; the reversed scan runs per chunk
-  size_t maps_off, starts_off, acc_off, bytes;
+  size_t maps_off, starts_off, acc_off, fac_off, bytes;
 };
 
 Plan make_plan(const Problem& p, int direction) {
@@ -1562,7 +1587,8 @@ Plan make_plan(const Problem& p, int direction) {
   pl.maps_off = 0;
   pl.starts_off = align_up(maps, 256);
   pl.acc_off = pl.starts_off + align_up(starts, 256);
-  pl.bytes = pl.acc_off + align_up(acc, 256);
+  pl.fac_off = pl.acc_off + align_up(acc, 256);
+  pl.bytes = pl.fac_off + align_up(prologue_bytes(p), 256);
   return pl;
 }
 
@@ -1594,9 +1620,18 @@ Side* side_stream() {
   return ok[dev] ? &sides[dev] : nullptr;
 }
 
-template <int D>
+template <int D, bool PRO>
 hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws, hipStream_t stream) {
   Args a{};
+  if constexpr (PRO) {
+    // the factors first, on the call's stream (every later launch, and the
+    // side stream's fork, is ordered after it)
+    float* fac = reinterpret_cast<float*>(ws + pl.fac_off);
+    const hipError_t e = prologue_launch(p, t, fac, stream);
+    if (e != hipSuccess) return e;
+    a.fk = fac;
+    a.fq = fac + (size_t)p.B * p.T * p.H;
+  }
   a.q = static_cast<const bh*>(t.q);
   a.k = static_cast<const bh*>(t.k);
   a.v = static_cast<const bh*>(t.v);
@@ -1637,9 +1672,9 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
     prof_begin(st, GDN_KERNEL_SEG_MAP);
     a.npos = both && slot == 0 ? pl.NS : pl.NS - 1;
     if (both && slot == 1)
-      hipLaunchKernelGGL((seg_map_q_kernel<D>), dim3(padded(a.npos), bhc, 1), dim3(Geo<D>::NT), 0, st, a);
+      hipLaunchKernelGGL((seg_map_q_kernel<D, PRO>), dim3(padded(a.npos), bhc, 1), dim3(Geo<D>::NT), 0, st, a);
     else
-      hipLaunchKernelGGL((seg_map_kernel<D>), dim3(padded(a.npos), bhc, 1), dim3(Geo<D>::NT), 0, st, a);
+      hipLaunchKernelGGL((seg_map_kernel<D, PRO>), dim3(padded(a.npos), bhc, 1), dim3(Geo<D>::NT), 0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     prof_end(st, GDN_KERNEL_SEG_MAP);
@@ -1666,7 +1701,7 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
     a.heads_rev = both && dir == 1;
     prof_begin(st, GDN_KERNEL_SEG_OUT);
     a.npos = pl.NS;
-    hipLaunchKernelGGL((seg_out_kernel<D>), dim3(padded(pl.NS), bhc, 1), dim3(Geo<D>::NT), 0, st, a);
+    hipLaunchKernelGGL((seg_out_kernel<D, PRO>), dim3(padded(pl.NS), bhc, 1), dim3(Geo<D>::NT), 0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     prof_end(st, GDN_KERNEL_SEG_OUT);
@@ -1687,7 +1722,7 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
       r.cs_len = cl_;
       r.npos = nchunks;
       prof_begin(st, GDN_KERNEL_SEG_OUT);
-      hipLaunchKernelGGL((seg_out_kernel<D>), dim3(padded(nchunks), bhc, 1), dim3(Geo<D>::NT), 0, st, r);
+      hipLaunchKernelGGL((seg_out_kernel<D, PRO>), dim3(padded(nchunks), bhc, 1), dim3(Geo<D>::NT), 0, st, r);
       const hipError_t e2 = hipGetLastError();
       if (e2 != hipSuccess) return e2;
       prof_end(st, GDN_KERNEL_SEG_OUT);
@@ -1699,7 +1734,7 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
       a.heads_rev = 0;
       a.npos = pl.NS;
       prof_begin(st, GDN_KERNEL_SEG_OUT);
-      hipLaunchKernelGGL((seg_out_kernel<D>), dim3(padded(pl.NS), bhc, 1), dim3(Geo<D>::NT), 0, st, a);
+      hipLaunchKernelGGL((seg_out_kernel<D, PRO>), dim3(padded(pl.NS), bhc, 1), dim3(Geo<D>::NT), 0, st, a);
       const hipError_t e2 = hipGetLastError();
       if (e2 != hipSuccess) return e2;
       prof_end(st, GDN_KERNEL_SEG_OUT);
@@ -1773,13 +1808,13 @@ hipError_t chunked_launch(const Problem& p, int direction, const Tensors& t, voi
   const Plan pl = make_plan(p, direction);
   char* ws = static_cast<char*>(workspace);
   switch (p.dk) {
-    case 16: return launch_d<16>(p, pl, t, ws, stream);
-    case 32: return launch_d<32>(p, pl, t, ws, stream);
-    case 48: return launch_d<48>(p, pl, t, ws, stream);
-    case 64: return launch_d<64>(p, pl, t, ws, stream);
-    case 80: return launch_d<80>(p, pl, t, ws, stream);
-    case 96: return launch_d<96>(p, pl, t, ws, stream);
-    case 112: return launch_d<112>(p, pl, t, ws, stream);
+    case 16: return p.prologue ? launch_d<16, true>(p, pl, t, ws, stream) : launch_d<16, false>(p, pl, t, ws, stream);
+    case 32: return p.prologue ? launch_d<32, true>(p, pl, t, ws, stream) : launch_d<32, false>(p, pl, t, ws, stream);
+    case 48: return p.prologue ? launch_d<48, true>(p, pl, t, ws, stream) : launch_d<48, false>(p, pl, t, ws, stream);
+    case 64: return p.prologue ? launch_d<64, true>(p, pl, t, ws, stream) : launch_d<64, false>(p, pl, t, ws, stream);
+    case 80: return p.prologue ? launch_d<80, true>(p, pl, t, ws, stream) : launch_d<80, false>(p, pl, t, ws, stream);
+    case 96: return p.prologue ? launch_d<96, true>(p, pl, t, ws, stream) : launch_d<96, false>(p, pl, t, ws, stream);
+    case 112: return p.prologue ? launch_d<112, true>(p, pl, t, ws, stream) : launch_d<112, false>(p, pl, t, ws, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1790,7 +1825,7 @@ int chunked_segment_tokens(const Problem& p, int direction) { return make_plan(p
 namespace {
 struct JacPlan {
   int ndir, dirs;
-  size_t maps_off, starts_off, bytes;
+  size_t maps_off, starts_off, fac_off, bytes;
 };
 JacPlan jac_plan(const Problem& p, int direction) {
   JacPlan pl{};
@@ -1799,13 +1834,21 @@ JacPlan jac_plan(const Problem& p, int direction) {
   const size_t per = (size_t)pl.ndir * p.B * p.H * (size_t)(p.F + 1);
   pl.maps_off = 0;
   pl.starts_off = align_up(per * p.dk * (p.dk + p.dv) * sizeof(float), 256);
-  pl.bytes = pl.starts_off + align_up(per * p.dk * p.dv * sizeof(float), 256);
+  pl.fac_off = pl.starts_off + align_up(per * p.dk * p.dv * sizeof(float), 256);
+  pl.bytes = pl.fac_off + align_up(prologue_bytes(p), 256);
   return pl;
 }
 
-template <int D>
+template <int D, bool PRO>
 hipError_t jac_launch_d(const Problem& p, const JacPlan& pl, const Tensors& t, char* ws, hipStream_t stream) {
   Args a{};
+  if constexpr (PRO) {
+    float* fac = reinterpret_cast<float*>(ws + pl.fac_off);
+    const hipError_t e = prologue_launch(p, t, fac, stream);
+    if (e != hipSuccess) return e;
+    a.fk = fac;
+    a.fq = fac + (size_t)p.B * p.T * p.H;
+  }
   a.q = static_cast<const bh*>(t.q);
   a.k = static_cast<const bh*>(t.k);
   a.v = static_cast<const bh*>(t.v);
@@ -1827,7 +1870,7 @@ hipError_t jac_launch_d(const Problem& p, const JacPlan& pl, const Tensors& t, c
   const unsigned bhc = (unsigned)(p.B * p.H);
   hipError_t e;
   prof_begin(stream, GDN_KERNEL_JAC_MAP);
-  hipLaunchKernelGGL((jac_map_kernel<D>), dim3(p.F, bhc), dim3(64 * (D / 16)), 0, stream, a);
+  hipLaunchKernelGGL((jac_map_kernel<D, PRO>), dim3(p.F, bhc), dim3(64 * (D / 16)), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_end(stream, GDN_KERNEL_JAC_MAP);
   a.slot0 = 0;
@@ -1836,7 +1879,7 @@ hipError_t jac_launch_d(const Problem& p, const JacPlan& pl, const Tensors& t, c
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_end(stream, GDN_KERNEL_SEG_CHAIN);
   prof_begin(stream, GDN_KERNEL_JAC_OUT);
-  hipLaunchKernelGGL((jac_out_kernel<D>), dim3(p.F, bhc), dim3(64 * (D / 16)), 0, stream, a);
+  hipLaunchKernelGGL((jac_out_kernel<D, PRO>), dim3(p.F, bhc), dim3(64 * (D / 16)), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_end(stream, GDN_KERNEL_JAC_OUT);
   return hipSuccess;
@@ -1857,13 +1900,13 @@ hipError_t jacobi_launch(const Problem& p, int direction, const Tensors& t, void
   const JacPlan pl = jac_plan(p, direction);
   char* ws = static_cast<char*>(workspace);
   switch (p.dk) {
-    case 16: return jac_launch_d<16>(p, pl, t, ws, stream);
-    case 32: return jac_launch_d<32>(p, pl, t, ws, stream);
-    case 48: return jac_launch_d<48>(p, pl, t, ws, stream);
-    case 64: return jac_launch_d<64>(p, pl, t, ws, stream);
-    case 80: return jac_launch_d<80>(p, pl, t, ws, stream);
-    case 96: return jac_launch_d<96>(p, pl, t, ws, stream);
-    case 112: return jac_launch_d<112>(p, pl, t, ws, stream);
+    case 16: return p.prologue ? jac_launch_d<16, true>(p, pl, t, ws, stream) : jac_launch_d<16, false>(p, pl, t, ws, stream);
+    case 32: return p.prologue ? jac_launch_d<32, true>(p, pl, t, ws, stream) : jac_launch_d<32, false>(p, pl, t, ws, stream);
+    case 48: return p.prologue ? jac_launch_d<48, true>(p, pl, t, ws, stream) : jac_launch_d<48, false>(p, pl, t, ws, stream);
+    case 64: return p.prologue ? jac_launch_d<64, true>(p, pl, t, ws, stream) : jac_launch_d<64, false>(p, pl, t, ws, stream);
+    case 80: return p.prologue ? jac_launch_d<80, true>(p, pl, t, ws, stream) : jac_launch_d<80, false>(p, pl, t, ws, stream);
+    case 96: return p.prologue ? jac_launch_d<96, true>(p, pl, t, ws, stream) : jac_launch_d<96, false>(p, pl, t, ws, stream);
+    case 112: return p.prologue ? jac_launch_d<112, true>(p, pl, t, ws, stream) : jac_launch_d<112, false>(p, pl, t, ws, stream);
     default: return hipErrorInvalidValue;
   }
 }

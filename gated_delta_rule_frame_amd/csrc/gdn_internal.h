@@ -19,6 +19,7 @@ struct Problem {
   float key_scale;
   bool jacobi;         // frame-level transition (GDN_INTRA_JACOBI)
   int first_chunk_frames, chunk_frames;   // GDN_CHUNK_CAUSAL chunking (frames)
+  bool prologue;       // GDN_PROLOGUE_FEATURES
 };
 
 // Device pointers of one call.
@@ -50,6 +51,12 @@ const char* jacobi_unsupported_reason(const Problem& p);
 size_t jacobi_workspace(const Problem& p, int direction);
 hipError_t jacobi_launch(const Problem& p, int direction, const Tensors& t,
                          void* workspace, hipStream_t stream);
+
+// Feature prologue (gdn_prologue.hip): two fp32 factors per (token, head) in
+// the workspace, keys first: fac[n] = 1/sqrt(mean k^2 + eps) and
+// fac[rows + n] = 1/sqrt(sum q^2 + eps), n = (b T + t) H + h, rows = B T H.
+size_t prologue_bytes(const Problem& p);
+hipError_t prologue_launch(const Problem& p, const Tensors& t, float* fac, hipStream_t stream);
 
 void set_segment_tokens(int tokens);
 void set_concurrent_scans(bool on);

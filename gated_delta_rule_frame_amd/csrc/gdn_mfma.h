@@ -51,6 +51,24 @@ __device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 v) {
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
+// Eight bf16 values times s, rounded to the nearest fp16; with RELU, products
+// below zero become zero (NaN stays NaN).
+template <bool RELU>
+__device__ __forceinline__ uint4 bf16x8_scaled_f16x8(uint4 v, float s) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float lo = __uint_as_float(w[i] << 16) * s, hi = __uint_as_float(w[i] & 0xffff0000u) * s;
+    if constexpr (RELU) {
+      lo = lo < 0.f ? 0.f : lo;
+      hi = hi < 0.f ? 0.f : hi;
+    }
+    o[i] = static_cast<uint32_t>(f2h(lo)) | (static_cast<uint32_t>(f2h(hi)) << 16);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // Ordering of LDS traffic between lanes of one wavefront.

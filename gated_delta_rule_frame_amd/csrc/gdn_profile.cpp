@@ -103,6 +103,7 @@ const char* gdn_kernel_name(int32_t kernel) {
     case GDN_KERNEL_RECURRENT: return "recurrent_kernel";
     case GDN_KERNEL_JAC_MAP: return "jac_map_kernel";
     case GDN_KERNEL_JAC_OUT: return "jac_out_kernel";
+    case GDN_KERNEL_PROLOGUE: return "prologue_kernel";
     default: return "";
   }
 }

@@ -11,7 +11,9 @@
 // lane l owns column (l % 16) and rows r = (l / 16) + 4 m.  The two dot
 // products of a token (k^T H and q^T H) are a per-lane partial sum followed by
 // a 4-way cross-lane reduction (lanes l, l^16, l^32, l^48).  Tokens are staged
-// through LDS in blocks of 32.
+// through LDS in blocks of 32.  With the feature prologue, keys and queries
+// are multiplied by their per-(token, head) factors on load and the keys pass
+// through ReLU.
 #include "gdn_common.h"
 #include "gdn_internal.h"
 
@@ -28,7 +30,8 @@ __global__ __launch_bounds__(64) void recurrent_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* h0,
     void* __restrict__ out, float* hT, float* __restrict__ acc, long long T, int H, int DV,
-    int reverse, int out_mode, int out_bf16, float key_scale, long long reset_first, long long reset_every) {
+    int reverse, int out_mode, int out_bf16, float key_scale, long long reset_first, long long reset_every,
+    const float* __restrict__ fk, const float* __restrict__ fq) {
   constexpr int R = DK / 4;
   const int lane = threadIdx.x;
   const int c = lane & 15, r0 = lane >> 4;
@@ -52,9 +55,15 @@ __global__ __launch_bounds__(64) void recurrent_kernel(
     for (int idx = lane; idx < nt * DK; idx += 64) {
       const int j = idx / DK, i = idx % DK;
       const long long tau = reverse ? T - 1 - (t0 + j) : t0 + j;
-      const size_t off = (((size_t)b * T + tau) * H + h) * DK + i;
-      ks[j][i] = load_scalar<BF16IN>(k, off) * key_scale;
-      qs[j][i] = load_scalar<BF16IN>(q, off);
+      const size_t row = ((size_t)b * T + tau) * H + h, off = row * DK + i;
+      float kv = load_scalar<BF16IN>(k, off), qv = load_scalar<BF16IN>(q, off);
+      if (fk) {
+        kv *= fk[row];
+        kv = kv < 0.f ? 0.f : kv;
+        qv *= fq[row];
+      }
+      ks[j][i] = kv * key_scale;
+      qs[j][i] = qv;
     }
     for (int idx = lane; idx < nt * kCols; idx += 64) {
       const int j = idx / kCols, cc = idx % kCols;
@@ -116,8 +125,10 @@ __global__ __launch_bounds__(64) void recurrent_kernel(
 
 template <bool BF16IN>
 hipError_t launch_dk(const Problem& p, const Tensors& t, bool reverse, const float* h0, int out_mode,
-                     float* acc, bool write_state, hipStream_t stream, long long reset_first = 0,
+                     float* acc, const float* fac, bool write_state, hipStream_t stream, long long reset_first = 0,
                      long long reset_every = 0) {
+  const float* fk = fac;
+  const float* fq = fac ? fac + (size_t)p.B * p.T * p.H : nullptr;
   dim3 grid(p.dv / kCols, p.H, p.B), block(64);
   float* hT = write_state ? t.hT : nullptr;
   prof_begin(stream, GDN_KERNEL_RECURRENT);
@@ -126,7 +137,7 @@ hipError_t launch_dk(const Problem& p, const Tensors& t, bool reverse, const flo
     hipLaunchKernelGGL((recurrent_kernel<BF16IN, D>), grid, block, 0, stream, t.q, t.k, t.v, \
                        t.g, t.beta, h0, t.out,           hT, acc, p.T, p.H, p.dv,  \
                        reverse ? 1 : 0, out_mode, p.out_bf16 ? 1 : 0, p.key_scale,            \
-                       reset_first, reset_every);                                             \
+                       reset_first, reset_every, fk, fq);                                     \
     break;
   switch (p.dk) {
     GDN_REC_CASE(16) GDN_REC_CASE(32) GDN_REC_CASE(48) GDN_REC_CASE(64)
@@ -141,19 +152,30 @@ hipError_t launch_dk(const Problem& p, const Tensors& t, bool reverse, const flo
 
 }  // namespace
 
-size_t recurrent_workspace(const Problem& p, int direction) {
-  // The bidirectional sum goes through an fp32 accumulator so that the output
-  // is rounded once.
+namespace {
+// The bidirectional sum goes through an fp32 accumulator so that the output
+// is rounded once; the prologue factors follow it.
+size_t acc_bytes(const Problem& p, int direction) {
   if (direction != GDN_BIDIRECTIONAL && direction != GDN_CHUNK_CAUSAL) return 0;
-  return (size_t)p.B * p.T * p.H * p.dv * sizeof(float);
+  return align_up((size_t)p.B * p.T * p.H * p.dv * sizeof(float), 256);
+}
+}  // namespace
+
+size_t recurrent_workspace(const Problem& p, int direction) {
+  return acc_bytes(p, direction) + prologue_bytes(p);
 }
 
 hipError_t recurrent_launch(const Problem& p, int direction, const Tensors& t, void* workspace,
                             hipStream_t stream) {
   float* acc = static_cast<float*>(workspace);
+  float* fac = p.prologue ? reinterpret_cast<float*>(static_cast<char*>(workspace) + acc_bytes(p, direction)) : nullptr;
+  if (fac) {
+    const hipError_t e = prologue_launch(p, t, fac, stream);
+    if (e != hipSuccess) return e;
+  }
   auto go = [&](bool reverse, const float* h0, int mode, bool state, long long rf = 0, long long re = 0) {
-    return p.qkv_bf16 ? launch_dk<true>(p, t, reverse, h0, mode, acc, state, stream, rf, re)
-                      : launch_dk<false>(p, t, reverse, h0, mode, acc, state, stream, rf, re);
+    return p.qkv_bf16 ? launch_dk<true>(p, t, reverse, h0, mode, acc, fac, state, stream, rf, re)
+                      : launch_dk<false>(p, t, reverse, h0, mode, acc, fac, state, stream, rf, re);
   };
   if (direction == GDN_FORWARD) return go(false, t.h0, 0, true);
   // Backward-only mode: initial_state seeds the reversed scan.

@@ -99,6 +99,22 @@ enum { GDN_ALGO_AUTO = 0, GDN_ALGO_CHUNKED = 1, GDN_ALGO_RECURRENT = 2 };
  * machinery only: bf16 q/k/v, d_k = d_v <= 112, algo AUTO or CHUNKED. */
 enum { GDN_INTRA_SEQUENTIAL = 0, GDN_INTRA_JACOBI = 1 };
 
+/* Feature prologue applied to q and k on load.  NONE: q and k are used as
+ * given.  FEATURES: per token and head, the key is replaced by its features
+ * ReLU(RMSNorm(k)), k_i / sqrt(mean_j k_j^2 + 1e-6) with negative values set
+ * to zero and no learned weight, and the query by q / sqrt(sum_j q_j^2 +
+ * 1e-6); key_scale still multiplies the key features (the pages' spatial
+ * scale is key_scale = 1/sqrt(d_k * tokens_per_frame)).  "SANA-WM ... Hybrid
+ * Linear Diffusion Transformer" summary, section 3.2, "Algebraic
+ * Stabilization for Spatial Token Explosion" (RMS-normalised, ReLU-activated
+ * keys) and the token-wise update (normalised queries).  The normalised
+ * tensors are never written to memory: a first kernel reads q and k once and
+ * stores two fp32 factors per (token, head) in the workspace, and every
+ * kernel that loads q or k applies them (and the ReLU) as it loads.  Every
+ * path and direction supports it; the workspace grows by 8 * B * T * H
+ * bytes. */
+enum { GDN_PROLOGUE_NONE = 0, GDN_PROLOGUE_FEATURES = 1 };
+
 typedef struct gdn_problem {
   int32_t abi_version;        /* must equal GDN_ABI_VERSION */
   int32_t batch;              /* B >= 1 */
@@ -114,7 +130,8 @@ typedef struct gdn_problem {
   int32_t intra;              /* GDN_INTRA_* (0 = SEQUENTIAL) */
   int32_t first_chunk_frames; /* GDN_CHUNK_CAUSAL: frames of the first chunk (>= 1), else ignored */
   int32_t chunk_frames;       /* GDN_CHUNK_CAUSAL: frames of each later chunk (>= 1), else ignored */
-  int32_t reserved[2];        /* must be zero */
+  int32_t prologue;           /* GDN_PROLOGUE_* (0 = NONE) */
+  int32_t reserved[1];        /* must be zero */
 } gdn_problem;
 
 /* Version of this ABI (GDN_ABI_VERSION of the built library). */
@@ -184,7 +201,8 @@ enum {
   GDN_KERNEL_RECURRENT = 3,   /* token-sequential path */
   GDN_KERNEL_JAC_MAP = 4,     /* frame-level path: per-frame maps */
   GDN_KERNEL_JAC_OUT = 5,     /* frame-level path: outputs and final state */
-  GDN_KERNEL_COUNT = 6
+  GDN_KERNEL_PROLOGUE = 6,    /* feature prologue: per-token key and query factors */
+  GDN_KERNEL_COUNT = 7
 };
 gdn_status gdn_profile_enable(int32_t on);
 gdn_status gdn_profile_reset(void);

@@ -65,7 +65,7 @@ def test_bad_problem_fields_are_rejected(field, value):
 
 def test_reserved_and_key_scale_and_direction_checks():
     p = prob()
-    p.reserved[1] = 1
+    p.reserved[0] = 1
     with pytest.raises(G.GdnError):
         G.workspace_size(p, "bidir")
     p = prob(key_scale=float("nan"))
@@ -156,3 +156,24 @@ def test_chunk_causal_validation_and_workspace():
     pbf = prob(first_chunk_frames=2, chunk_frames=1, algo="chunked", out_dtype=G.BF16)
     assert G.workspace_size(pbf, "chunk_causal") - G.workspace_size(p32, "chunk_causal") >= 1 * 300 * 2 * 64 * 4
     assert G.workspace_size(p32, "chunk_causal") < G.workspace_size(p32, "bidir")
+
+
+def test_feature_prologue_validation_and_workspace():
+    """prologue is NONE or FEATURES; FEATURES adds two fp32 factors per
+    (token, head) to the workspace of every path and direction (each region
+    rounded up to 256 bytes)."""
+    p = prob(prologue=2)
+    with pytest.raises(G.GdnError) as e:
+        G.workspace_size(p, "bidir")
+    assert e.value.status == G.ERR_INVALID_ARGUMENT
+    fac = 2 * 1 * 300 * 2 * 4
+    rounded = (fac + 255) // 256 * 256
+    for kw in (dict(algo="recurrent"), dict(algo="chunked"), dict(intra="jacobi"),
+               dict(algo="recurrent", qkv_dtype=G.F32)):
+        for d in ("fwd", "bwd", "bidir"):
+            a = G.workspace_size(prob(**kw), d)
+            b = G.workspace_size(prob(prologue="features", **kw), d)
+            assert b - a in (fac, rounded), (kw, d, a, b)
+    p = prob(prologue="features", first_chunk_frames=2, chunk_frames=1)
+    assert G.workspace_size(p, "chunk_causal") > G.workspace_size(prob(first_chunk_frames=2, chunk_frames=1),
+                                                                  "chunk_causal")

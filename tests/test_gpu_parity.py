@@ -293,6 +293,121 @@ def test_jacobi_bf16_output():
     assert rel_err(o, ro) <= bound and rel_err(hT, rH) <= TOL["bf16"]
 
 
+# ---------------------------------------------------------------- feature prologue
+
+PRO = {
+    # name: (workload with raw q/k, key scale)
+    "clip60s": (WORKLOADS[2].resized(frames=3, heads=3, qk_spread=1.0), (112 * 880) ** -0.5),
+    "ragged": (WORKLOADS[1].resized(frames=3, tokens_per_frame=201, heads=2, qk_spread=1.0), 112 ** -0.5),
+    "batched": (WORKLOADS[4].resized(frames=2, heads=3, qk_spread=1.0), (64 * 880) ** -0.5),
+}
+
+
+def features(x):
+    """Oracle inputs with the prologue applied on the CPU (float64)."""
+    a = [x[n] for n in ("q", "k", "v", "log_gate", "beta")]
+    a[0], a[1] = O.query_features(a[0]), O.key_features(a[1])
+    return a
+
+
+def run_pro(w, x, direction, c, algo="auto", intra="sequential", out_dtype=None, chunks=(0, 0)):
+    d = to_device(x, w.qkv_dtype)
+    h0 = d["h0"] if np.any(x["h0"]) else None
+    out, hT = G.forward(d["q"], d["k"], d["v"], d["log_gate"], d["beta"], h0, direction,
+                        tokens_per_frame=w.tokens_per_frame, key_scale=c, algo=algo, intra=intra,
+                        out_dtype=out_dtype, prologue="features", first_chunk_frames=chunks[0],
+                        chunk_frames=chunks[1])
+    torch.cuda.synchronize()
+    return to_numpy(out), to_numpy(hT)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("name", list(PRO))
+@pytest.mark.parametrize("direction", ["fwd", "bwd", "bidir"])
+def test_feature_prologue_bf16(algo, name, direction):
+    """Raw q/k through the fused prologue against the oracle applied to
+    key_features(k), query_features(q)."""
+    w, c = PRO[name]
+    x = make_inputs(w, 31)
+    o, hT = run_pro(w, x, direction, c, algo=algo)
+    ro, rH = O.forward(direction, *features(x), x["h0"], key_scale=c)
+    eo, eh = rel_err(o, ro), rel_err(hT, rH)
+    print(f"[parity] {w.name} prologue {direction} {algo}: out {eo:.3e} state {eh:.3e}", flush=True)
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"], (eo, eh)
+
+
+def test_feature_prologue_fp32_recurrent():
+    w = WORKLOADS[0].resized(qk_spread=1.0)
+    x = make_inputs(w, 32)
+    for direction in ("fwd", "bidir"):
+        o, hT = run_pro(w, x, direction, 16 ** -0.5)
+        ro, rH = O.forward(direction, *features(x), x["h0"], key_scale=16 ** -0.5)
+        assert rel_err(o, ro) <= TOL["f32"] and rel_err(hT, rH) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("direction", ["fwd", "bidir"])
+def test_feature_prologue_jacobi(direction):
+    w, c = PRO["clip60s"]
+    x = make_inputs(w, 33)
+    o, hT = run_pro(w, x, direction, c, intra="jacobi")
+    ro, rH = O.jacobi_forward(direction, *features(x), x["h0"], key_scale=c, tokens_per_frame=w.tokens_per_frame)
+    eo, eh = rel_err(o, ro), rel_err(hT, rH)
+    print(f"[parity] {w.name} prologue jacobi {direction}: out {eo:.3e} state {eh:.3e}", flush=True)
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"], (eo, eh)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_feature_prologue_chunk_causal(algo):
+    w, c = PRO["ragged"]
+    x = make_inputs(w, 34)
+    o, hT = run_pro(w, x, "chunk_causal", c, algo=algo, chunks=(2, 1))
+    ro, rH = O.chunk_causal(*features(x), x["h0"], key_scale=c, tokens_per_frame=w.tokens_per_frame,
+                            first_chunk_frames=2, chunk_frames=1)
+    assert rel_err(o, ro) <= TOL["bf16"] and rel_err(hT, rH) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_feature_prologue_step_chain_matches_forward(algo):
+    """gdn_step with the prologue, frame after frame, against the forward scan:
+    the factors are per token, so framing cannot change them; the token-recurrent
+    path then agrees bit for bit, the chunked one (whose 64-token blocks start
+    at each call's first token) to rounding."""
+    w, c = PRO["batched"]
+    x = make_inputs(w, 35)
+    d = to_device(x, w.qkv_dtype)
+    S = w.tokens_per_frame
+    state = d["h0"].clone()
+    outs = []
+    for f in range(w.frames):
+        sl = slice(f * S, (f + 1) * S)
+        o, _ = G.step(*(d[n][:, sl].contiguous() for n in ("q", "k", "v", "log_gate", "beta")),
+                      state, state, key_scale=c, prologue="features", algo=algo)
+        outs.append(o)
+    o = to_numpy(torch.cat(outs, dim=1))
+    fo, fH = run_pro(w, x, "fwd", c, algo=algo)
+    if algo == "recurrent":
+        assert np.array_equal(o, fo) and np.array_equal(to_numpy(state), fH)
+    else:
+        assert rel_err(o, fo) <= 1e-2 and rel_err(to_numpy(state), fH) <= 1e-2
+    ro, rH = O.fwd(*features(x), x["h0"], key_scale=c)
+    assert rel_err(o, ro) <= TOL["bf16"] and rel_err(fH, rH) <= TOL["bf16"]
+
+
+def test_feature_prologue_is_invariant_to_token_magnitudes():
+    """Property at any size: the features do not depend on a positive factor
+    per (token, head) of the raw q and k (powers of two keep bf16 exact); the
+    results agree to rounding and to the epsilon, which is not scaled (hence
+    factors >= 1 only)."""
+    w, c = PRO["clip60s"]
+    x = make_inputs(w, 36)
+    rng = np.random.default_rng(37)
+    y = dict(x)
+    for n in ("q", "k"):
+        y[n] = (x[n] * 2.0 ** rng.integers(0, 4, x[n].shape[:3] + (1,))).astype(np.float32)
+    a, b = run_pro(w, x, "bidir", c), run_pro(w, y, "bidir", c)
+    assert rel_err(a[0], b[0]) <= 5e-3 and rel_err(a[1], b[1]) <= 5e-3
+
+
 FULL = [(1, "bidir", [0, 19]), (2, "bidir", [7]), (2, "fwd", [13]), (4, "bidir", [(0, 3), (1, 34)])]
 
 
@@ -315,3 +430,20 @@ def test_full_size_sampled_heads(algo, idx, direction, heads):
         print(f"[parity-full] {w.name} {direction} b{b} h{h}: out {eo:.3e} state {eh:.3e}",
               flush=True)
         assert eo <= tol and eh <= tol
+
+
+@pytest.mark.slow
+def test_full_size_feature_prologue_sampled_head():
+    """The 60 s clip with raw q/k through the prologue (bidirectional, key
+    scale 1/sqrt(D*S)) in the bench's launch configuration; head 5 against
+    the oracle over the whole sequence."""
+    w = WORKLOADS[2].resized(qk_spread=1.0)
+    c = (w.d_k * w.tokens_per_frame) ** -0.5
+    x = make_inputs(w, 0)
+    o, hT = run_pro(w, x, "bidir", c, algo="chunked")
+    h = 5
+    a = [t[:, :, h:h + 1] for t in features(x)]
+    ro, rH = O.bidir(*a, x["h0"][:, h:h + 1], key_scale=c)
+    eo, eh = rel_err(o[:, :, h:h + 1], ro), rel_err(hT[:, h:h + 1], rH)
+    print(f"[parity-full] {w.name} prologue bidir h{h}: out {eo:.3e} state {eh:.3e}", flush=True)
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"]
