@@ -35,7 +35,7 @@ METRIC = "GDN layer fwd tokens/s & % bf16 MFMA peak, 121×880-token 60 s clip, 1
 PEAK_TFLOPS = 2516.6        # MI355X dense fp16/bf16 MFMA, 256 CU x 4096 flop/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 TOL = {"f32": 1e-4, "bf16": 2e-2}
-KERNEL_SOURCES = ("gdn_chunked.hip", "gdn_mfma.h", "gdn_common.h")
+KERNEL_SOURCES = ("gdn_chunked.hip", "gdn_prologue.hip", "gdn_mfma.h", "gdn_common.h")
 
 
 # --------------------------------------------------------------- FLOP models
@@ -214,6 +214,8 @@ def main():
     key_scale = (dk * w.tokens_per_frame) ** -0.5 if pro else w.tokens_per_frame ** -0.5 if jac else 1.0
     first_cf, every_cf = (int(c) for c in args.chunks.split(","))
     cc = direction == "chunk_causal"
+    # name of the committed counter summaries for this configuration
+    tag = w.name + ("_jacobi" if jac else "") + ("_features" if pro else "") + ("_chunk_causal" if cc else "")
     prob = G.make_problem(B, H, dk, dv, w.frames, w.tokens_per_frame, G.BF16 if w.qkv_dtype == "bf16" else G.F32,
                           G.F32, "auto", key_scale, args.intra, first_cf, every_cf, args.prologue)
     ws = torch.empty(max(G.workspace_size(prob, direction), 16), dtype=torch.uint8, device=dev)
@@ -310,7 +312,7 @@ def main():
         dom = max(kern, key=lambda k: kern[k]["avg_ms"] * kern[k]["launches"])
         achieved = kern[dom].get("gbs", 0.0)
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS, "traffic": read_traffic(dom, w.name + "_jacobi"), "kernel": dom}
+                "frac": achieved / PEAK_HBM_GBS, "traffic": read_traffic(dom, tag), "kernel": dom}
     elif "seg_out_kernel" in kern and L:
         fl = (chunk_causal_flops(T, w.tokens_per_frame, L, dk, B * H, first_cf, every_cf) if cc
               else executed_flops(T, L, dk, B * H, ndir))
@@ -323,7 +325,7 @@ def main():
                 kern[k]["tflops"] = per_launch[k] / (kern[k]["avg_ms"] / 1e3) / 1e12
         dom = max(kern, key=lambda k: kern[k]["avg_ms"] * kern[k]["launches"])
         achieved = per_launch.get(dom, 0) / (kern[dom]["avg_ms"] / 1e3) / 1e12
-        traffic = read_traffic(dom, w.name)
+        traffic = read_traffic(dom, tag)
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_TFLOPS, "traffic": traffic, "kernel": dom}
     if "prologue_kernel" in kern:
