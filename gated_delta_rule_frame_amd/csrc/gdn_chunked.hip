@@ -500,14 +500,17 @@ __device__ __forceinline__ f32x4 gram_tile(const hb* kr, const hb* xr, int ta, i
   return acc;
 }
 
-// Lower-triangular 16x16-tile pairs (a <= b) of a 4x4 tile grid; the first
-// six are the strictly lower ones.
-__device__ __forceinline__ void tile_pair(int t, int& a, int& b) {
-  constexpr int A[10] = {0, 0, 0, 1, 1, 2, 0, 1, 2, 3};
-  constexpr int B[10] = {1, 2, 3, 2, 3, 3, 0, 1, 2, 3};
-  a = A[t];
-  b = B[t];
+// Lower-triangular 16x16-tile pairs (a <= b) of a 4x4 tile grid, 2 bits per
+// pair index (in registers, no table load); the first six are the strictly
+// lower ones: (0,1) (0,2) (0,3) (1,2) (1,3) (2,3) (0,0) (1,1) (2,2) (3,3).
+constexpr uint32_t pack_pairs(const int (&v)[10]) {
+  uint32_t r = 0;
+  for (int i = 0; i < 10; ++i) r |= (uint32_t)v[i] << (2 * i);
+  return r;
 }
+constexpr int kPairA[10] = {0, 0, 0, 1, 1, 2, 0, 1, 2, 3};
+constexpr int kPairB[10] = {1, 2, 3, 2, 3, 3, 0, 1, 2, 3};
+constexpr uint32_t kPackA = pack_pairs(kPairA), kPackB = pack_pairs(kPairB);
 
 // Helper: the diagonal 16x16 blocks of A of sub-chunk B (fp32), then their
 // inverses.
@@ -535,18 +538,35 @@ __device__ void gram_stage_helper(const Args& a, const Buf& B, const Inv& I) {
 }
 
 // Strip waves: the off-diagonal blocks of A (fp16) and, for the output pass,
-// P = c tril(Q K^T) * E.
+// P = c tril(Q K^T) * E.  Wave w takes tiles w, w + NSW, ...; the products of
+// all its tiles are formed before any epilogue, so that their LDS reads and
+// MFMAs overlap (the first NFULL tiles of every wave need no branch).
 template <int D, bool OUT>
 __device__ void gram_stage_strips(const Args& a, const Buf& B, const Inv& I) {
   using G = Geo<D>;
   const int wave = wave_id(), lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
   const float c2 = a.c * a.c;
   constexpr int NTILE = OUT ? 16 : 6;
-  for (int t = wave; t < NTILE; t += G::NSW) {
+  constexpr int NK = (NTILE + G::NSW - 1) / G::NSW, NFULL = NTILE / G::NSW;
+  f32x4 sk[NK];
+#pragma unroll
+  for (int k = 0; k < NK; ++k) {
+    const int t = wave + k * G::NSW;
+    if (k < NFULL || t < NTILE) {
+      const bool isp = t >= 6;
+      const int u = isp ? t - 6 : t;
+      const int ta = (kPackA >> (2 * u)) & 3, tb = (kPackB >> (2 * u)) & 3;
+      sk[k] = gram_tile<D>(B.kr, isp ? B.qr : B.kr, ta, tb, cl, g);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < NK; ++k) {
+    const int t = wave + k * G::NSW;
+    if (!(k < NFULL || t < NTILE)) continue;
     const bool isp = t >= 6;
-    int ta, tb;
-    tile_pair(isp ? t - 6 : t, ta, tb);
-    const f32x4 s = gram_tile<D>(B.kr, isp ? B.qr : B.kr, ta, tb, cl, g);
+    const int u = isp ? t - 6 : t;
+    const int ta = (kPackA >> (2 * u)) & 3, tb = (kPackB >> (2 * u)) & 3;
+    const f32x4 s = sk[k];
     const int x = 16 * tb + cl, y0 = 16 * ta + 4 * g;
     const float gx = B.g2[x];
     const f32x4 gy = ld4f(B.g2 + y0);
@@ -1095,7 +1115,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_chain_kernel(Args a) {
 // state of the chain.  In a bidirectional call the reversed scan stores its
 // outputs as a partial that the forward scan's launch adds to its own.
 // Strip wave w owns state columns 16 w .. 16 w + 15.
-template <int D, bool PRO>
+template <int D, bool PRO, bool OB>
 __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
   using G = Geo<D>;
   using L = Lay<D, true>;
@@ -1192,10 +1212,14 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
     constexpr int NTS = 64 * G::NSW, C4 = D / 4;   // strip threads; 4-column groups per row
     static_assert(CH * C4 == 4 * NTS, "four groups of four values per strip thread");
     const int t = threadIdx.x;
-    const bool half = mode != 1 && a.out_bf16;
+    // OB: this launch stores bf16 outputs (mode != 1 with a bf16 output),
+    // a template parameter so that every store is unconditional: stores
+    // behind a branch make the compiler assume they may not have been issued
+    // and wait for later stores where it waits for earlier loads.
+    constexpr bool half = OB;
     const long long esz = half ? 2 : 4;
     char* const dstb = static_cast<char*>(mode == 1 ? static_cast<void*>(a.acc) : a.out);
-    f32x4 pre[4];
+    f32x4 pre[4] = {zero4(), zero4(), zero4(), zero4()};
     auto rows_of = [&](int c) { return ((long long)b * a.T + piece(c).t0) * HD + (long long)h * D; };
     auto load_pre = [&](int c) {
       const Sub sb = piece(c);
@@ -1208,16 +1232,22 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
         pre[i] = __builtin_bit_cast(f32x4, v);   // whole-vector casts only: see the note on vector elements
       }
     };
-    auto flush = [&](int c) {   // store the staged outputs of sub-chunk c (rows past n fall outside the buffer)
-      const Sub sb = piece(c);
+    // Store the staged outputs of sub-chunk c (rows past n fall outside the
+    // buffer).  c = -1 stores nothing (an empty range) but issues the same
+    // stores, so that every iteration issues the same memory operations and
+    // the compiler's wait counts stay exact (a skipped flush in the first
+    // iteration made it wait for the stores of every later one).
+    auto flush = [&](int c) {
+      const Sub sb = piece(c < 0 ? 0 : c);
       const Inv I = inv_at<D, true>(smem);
-      const __amdgpu_buffer_rsrc_t rs = rows_rsrc(dstb + rows_of(c) * esz, (long long)sb.n * HD * esz);
+      const __amdgpu_buffer_rsrc_t rs =
+          rows_rsrc(dstb + rows_of(c < 0 ? 0 : c) * esz, c < 0 ? 0 : (long long)sb.n * HD * esz);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int k = t + NTS * i, row = k / C4, c4 = k % C4;
         const f32x4 val = ld4f(I.os + row * L::OSL + 4 * c4) + pre[i];
         const uint32_t off = (uint32_t)(((sb.r0 + sb.sgn * row) * (int)HD + 4 * c4) * esz);
-        if (half) {
+        if constexpr (half) {
           typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
           const u32x2_t w{f32_to_bf16_bits(val[0]) | ((uint32_t)f32_to_bf16_bits(val[1]) << 16),
                           f32_to_bf16_bits(val[2]) | ((uint32_t)f32_to_bf16_bits(val[3]) << 16)};
@@ -1233,11 +1263,12 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
       const Inv I = inv_at<D, true>(smem);
       // alpha.  Staging first: it waits for the prefetched rows, which were
       // issued before the stores and loads below (the load counter drains in
-      // issue order).
+      // issue order).  The K/Q rows of c+2 are requested in beta, after the
+      // first products (measured 2% faster than here: alpha's memory
+      // instructions queue behind the stores).
       stage_kq<D, true, PRO>(Bn, sk);
-      if (c > 0) flush(c - 1);
+      flush(c - 1);
       load_pre(c);
-      fetch_kq<D, true, PRO>(a, b, h, piece(c + 2), sk);
       {
         f16x8_t Hp[SPW][G::NP];
         state_pairs<D>(H[0], Hp[0]);
@@ -1257,6 +1288,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
           state_pairs<D>(H[0], Hp);
           state_times_rows_T<D>(Bc.qr, Hp, cl, g, O);
         }
+        fetch_kq<D, true, PRO>(a, b, h, piece(c + 2), sk);
         f16x8_t Rh[SPW][2];
         Rh[0][0] = tof16x8(R[0][0], R[0][1]);
         Rh[0][1] = tof16x8(R[0][2], R[0][3]);
@@ -1440,7 +1472,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void jac_map_kernel(Args a) {
 // 16 w .. 16 w + 15.  The frame's end state (summed over the scans present) is
 // split into fp16 hi + lo parts (about 22 significant bits) and each 64-row
 // piece of Q is multiplied by both.
-template <int D, bool PRO>
+template <int D, bool PRO, bool OB>
 __global__ __launch_bounds__(64 * (D / 16)) void jac_out_kernel(Args a) {
   using G = Geo<D>;
   constexpr int MD = D / 16;
@@ -1523,7 +1555,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void jac_out_kernel(Args a) {
   stage(0, qv);
   fetch(1, qv);
   __syncthreads();
-  const bool half = a.out_bf16;
+  constexpr bool half = OB;   // bf16 outputs; a template parameter so the stores are unconditional
   const long long esz = half ? 2 : 4;
   for (int p = 0; p < np; ++p) {
     const hb* qr = reinterpret_cast<const hb*>(lds_at(smem, (uint32_t)((p & 1) * MAT)));
@@ -1537,7 +1569,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void jac_out_kernel(Args a) {
     for (int mt = 0; mt < 4; ++mt) {
       const f32x4 val = O[mt] + Ol[mt];
       const uint32_t off = (uint32_t)(((16 * mt + cl) * (int)HD + 16 * wave + 4 * g) * esz);
-      if (half) {
+      if constexpr (half) {
         typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
         const u32x2_t w{f32_to_bf16_bits(val[0]) | ((uint32_t)f32_to_bf16_bits(val[1]) << 16),
                         f32_to_bf16_bits(val[2]) | ((uint32_t)f32_to_bf16_bits(val[3]) << 16)};
@@ -1693,6 +1725,13 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
     prof_end(st, GDN_KERNEL_SEG_CHAIN);
     return hipSuccess;
   };
+  // One output launch (x.mode and x.out_bf16 select the store type).
+  auto launch_out = [&](const Args& x, unsigned gx, hipStream_t st) {
+    if (x.mode != 1 && x.out_bf16)
+      hipLaunchKernelGGL((seg_out_kernel<D, PRO, true>), dim3(gx, bhc, 1), dim3(Geo<D>::NT), 0, st, x);
+    else
+      hipLaunchKernelGGL((seg_out_kernel<D, PRO, false>), dim3(gx, bhc, 1), dim3(Geo<D>::NT), 0, st, x);
+  };
   // Outputs of one scan direction; in a bidirectional call the forward scan
   // stores its partial and the reversed scan adds it.
   auto outputs = [&](int dir, hipStream_t st) -> hipError_t {
@@ -1701,7 +1740,7 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
     a.heads_rev = both && dir == 1;
     prof_begin(st, GDN_KERNEL_SEG_OUT);
     a.npos = pl.NS;
-    hipLaunchKernelGGL((seg_out_kernel<D, PRO>), dim3(padded(pl.NS), bhc, 1), dim3(Geo<D>::NT), 0, st, a);
+    launch_out(a, padded(pl.NS), st);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     prof_end(st, GDN_KERNEL_SEG_OUT);
@@ -1722,7 +1761,7 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
       r.cs_len = cl_;
       r.npos = nchunks;
       prof_begin(st, GDN_KERNEL_SEG_OUT);
-      hipLaunchKernelGGL((seg_out_kernel<D, PRO>), dim3(padded(nchunks), bhc, 1), dim3(Geo<D>::NT), 0, st, r);
+      launch_out(r, padded(nchunks), st);
       const hipError_t e2 = hipGetLastError();
       if (e2 != hipSuccess) return e2;
       prof_end(st, GDN_KERNEL_SEG_OUT);
@@ -1734,7 +1773,7 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
       a.heads_rev = 0;
       a.npos = pl.NS;
       prof_begin(st, GDN_KERNEL_SEG_OUT);
-      hipLaunchKernelGGL((seg_out_kernel<D, PRO>), dim3(padded(pl.NS), bhc, 1), dim3(Geo<D>::NT), 0, st, a);
+      launch_out(a, padded(pl.NS), st);
       const hipError_t e2 = hipGetLastError();
       if (e2 != hipSuccess) return e2;
       prof_end(st, GDN_KERNEL_SEG_OUT);
@@ -1879,7 +1918,10 @@ hipError_t jac_launch_d(const Problem& p, const JacPlan& pl, const Tensors& t, c
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_end(stream, GDN_KERNEL_SEG_CHAIN);
   prof_begin(stream, GDN_KERNEL_JAC_OUT);
-  hipLaunchKernelGGL((jac_out_kernel<D, PRO>), dim3(p.F, bhc), dim3(64 * (D / 16)), 0, stream, a);
+  if (p.out_bf16)
+    hipLaunchKernelGGL((jac_out_kernel<D, PRO, true>), dim3(p.F, bhc), dim3(64 * (D / 16)), 0, stream, a);
+  else
+    hipLaunchKernelGGL((jac_out_kernel<D, PRO, false>), dim3(p.F, bhc), dim3(64 * (D / 16)), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_end(stream, GDN_KERNEL_JAC_OUT);
   return hipSuccess;

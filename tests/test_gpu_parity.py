@@ -163,6 +163,67 @@ def test_concurrent_scans_match_in_order_schedule():
     assert rel_err(b[0], ro) <= TOL["bf16"] and rel_err(b[1], rH) <= TOL["bf16"]
 
 
+# ---------------------------------------------------------------- every head width
+
+DIMS = [16, 32, 48, 80, 96]
+
+
+@pytest.mark.parametrize("d", DIMS)
+@pytest.mark.parametrize("direction", ["fwd", "bwd", "bidir"])
+def test_chunked_every_head_width(d, direction):
+    """The chunked path's other instantiations (d = 64 and 112 run above):
+    300 tokens in segments of 128 (three segments, the last ragged), so the
+    maps, the chain and the outputs of every width are exercised."""
+    w = WORKLOADS[4].resized(frames=2, tokens_per_frame=150, heads=3, d_k=d, d_v=d)
+    x = make_inputs(w, 40 + d)
+    G.set_segment_tokens(128)
+    try:
+        check(w, x, direction, "chunked")
+    finally:
+        G.set_segment_tokens(0)
+
+
+@pytest.mark.parametrize("d", DIMS)
+def test_jacobi_every_head_width(d):
+    w = WORKLOADS[4].resized(frames=3, tokens_per_frame=70, heads=2, d_k=d, d_v=d)
+    x = make_inputs(w, 50 + d)
+    o, hT = run_jacobi(w, x, "bidir")
+    ro, rH = O.jacobi_bidir(*oracle_args(x)[0], x["h0"], key_scale=w.tokens_per_frame ** -0.5,
+                            tokens_per_frame=w.tokens_per_frame)
+    assert rel_err(o, ro) <= TOL["bf16"] and rel_err(hT, rH) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dk,dv", [(32, 64), (64, 16), (128, 128), (112, 48)])
+def test_recurrent_unequal_and_widest_head(dk, dv):
+    """The token-recurrent path takes d_k != d_v and d = 128 (fp32, bar 1e-4)."""
+    w = WORKLOADS[0].resized(frames=2, tokens_per_frame=24, heads=2, d_k=dk, d_v=dv, h0_sigma=0.1)
+    x = make_inputs(w, 60)
+    for direction in ("fwd", "bidir"):
+        check(w, x, direction, "auto")
+
+
+@pytest.mark.parametrize("d", [16, 48, 128])
+def test_feature_prologue_other_widths_recurrent(d):
+    w = WORKLOADS[0].resized(frames=2, tokens_per_frame=24, heads=2, d_k=d, d_v=d, qk_spread=1.0)
+    x = make_inputs(w, 70)
+    o, hT = run_pro(w, x, "bidir", d ** -0.5)
+    ro, rH = O.forward("bidir", *features(x), x["h0"], key_scale=d ** -0.5)
+    assert rel_err(o, ro) <= TOL["f32"] and rel_err(hT, rH) <= TOL["f32"]
+
+
+def test_many_segments_and_heads():
+    """Many (batch, head) pairs and segments of 64 tokens (the shortest):
+    B = 3, H = 7, 4 frames of 97 tokens (388 tokens, 7 segments)."""
+    w = WORKLOADS[4].resized(batch=3, heads=7, frames=4, tokens_per_frame=97)
+    x = make_inputs(w, 80)
+    G.set_segment_tokens(64)
+    try:
+        for direction in ("fwd", "bidir"):
+            check(w, x, direction, "chunked")
+    finally:
+        G.set_segment_tokens(0)
+
+
 # ---------------------------------------------------------------- chunk-causal layer
 
 CC = {
