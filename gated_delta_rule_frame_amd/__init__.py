@@ -75,6 +75,8 @@ def lib():
         L.gdn_set_segment_tokens.argtypes = [i32]
         L.gdn_set_concurrent_scans.restype = None
         L.gdn_set_concurrent_scans.argtypes = [i32]
+        L.gdn_set_chain_group.restype = None
+        L.gdn_set_chain_group.argtypes = [i32]
         L.gdn_profile_enable.restype = i32
         L.gdn_profile_enable.argtypes = [i32]
         L.gdn_profile_reset.restype = i32
@@ -148,6 +150,12 @@ def profile_read() -> dict:
         _check(lib().gdn_profile_read(i, ctypes.byref(n), ctypes.byref(ms)))
         out[name] = (n.value, ms.value)
     return out
+
+
+def set_chain_group(maps: int) -> None:
+    """How the chain of segment maps is evaluated: 0 automatic, 1 whole, m >= 2
+    groups of m maps (see gdn.h)."""
+    lib().gdn_set_chain_group(int(maps))
 
 
 def set_concurrent_scans(on: bool) -> None:

@@ -156,6 +156,8 @@ const char* gdn_last_error_message(void) { return g_last_error.c_str(); }
 
 void gdn_set_segment_tokens(int32_t tokens) { gdn::set_segment_tokens(tokens); }
 
+void gdn_set_chain_group(int32_t maps) { gdn::set_chain_group(maps); }
+
 void gdn_set_concurrent_scans(int32_t on) { gdn::set_concurrent_scans(on != 0); }
 
 gdn_status gdn_plan_segment_tokens(const gdn_problem* pr, int32_t direction, int32_t* tokens_out) {

@@ -63,6 +63,36 @@ constexpr int ADB = 260;        // float stride of the fp32 diagonal blocks of A
 constexpr float kLog2e = 1.4426950408889634f;
 
 std::atomic<int> g_segment_override{0};
+std::atomic<int> g_chain_group{0};
+
+// Maps per group of a split chain for `nsteps` steps, or 0 for the whole chain
+// in one pass.  Automatic: split chains of 16 steps or more into groups of
+// ceil(sqrt(nsteps / 2)) maps (serial steps 2m + G, minimal near that m).
+int chain_group(int nsteps) {
+  const int k = g_chain_group.load(std::memory_order_relaxed);
+  if (k == 1) return 0;
+  if (k >= 2) return nsteps > k ? k : 0;
+  if (nsteps < 16) return 0;
+  int m = 1;
+  while (2 * m * m < nsteps) ++m;
+  return m;
+}
+
+// Workspace of a (possibly split) chain: group maps and group start states.
+struct ChainWs {
+  int m = 0, groups = 0;
+  size_t gmaps_bytes = 0, gstarts_bytes = 0;
+};
+ChainWs chain_ws(int nsteps, size_t heads_dirs, int dk, int dv) {
+  ChainWs c;
+  c.m = chain_group(nsteps);
+  if (c.m > 0) {
+    c.groups = (nsteps + c.m - 1) / c.m;
+    c.gmaps_bytes = align_up(heads_dirs * c.groups * (size_t)dk * (dk + dv) * sizeof(float), 256);
+    c.gstarts_bytes = align_up(heads_dirs * c.groups * (size_t)dk * dv * sizeof(float), 256);
+  }
+  return c;
+}
 std::atomic<bool> g_concurrent_scans{true};
 
 struct Args {
@@ -91,6 +121,10 @@ struct Args {
   float c;              // key scale
   const float* fk;      // feature prologue: per-(token, head) key factors ([B][T][H]), or null
   const float* fq;      // ... and query factors
+  int ch_mode;          // chain kernel: 0 whole chain, 1 compose groups, 2 chain of groups, 3 expand groups
+  int ch_m, ch_groups;  // ... maps per group, groups
+  float* gmaps;         // ... composed group maps [ndir][B][H][groups][DK][DK+DV]
+  float* gstarts;       // ... group start states [ndir][B][H][groups][DK][DV] (transposed)
 };
 
 // Wavefront index as a wave-uniform (scalar) value, so that branches on it are
@@ -920,7 +954,7 @@ __global__ __launch_bounds__(Geo<D>::NT) __attribute__((amdgpu_waves_per_eu(4)))
 }
 
 // ---------------------------------------------------------------------------
-// 2. Segment chain.  grid (B * H, ndir), one workgroup of MD wavefronts per
+// 2. Segment chain.  grid (B * H, ndir[, groups]), one workgroup of MD wavefronts per
 // head and direction: H_{p+1} = P_p H_p + Q_p over the segments in scan order,
 // i.e. the prefix composition of the segments' affine maps.  Wavefront w
 // carries state columns 16 w .. 16 w + 15 in fp32 registers.  Each step the
@@ -956,6 +990,19 @@ __device__ __forceinline__ void split4(f32x4 v, s16x4_t& hi, s16x4_t& lo) {
   }
 }
 
+// Modes (Args::ch_mode), for chains long enough to be worth splitting:
+//   0  the whole chain over positions 0 .. NS-2 from the seed, storing every
+//      start state and the final one (position NS-1);
+//   1  compose: group g = blockIdx.z / 2 covers positions [g m, g m + m) (the
+//      last group fewer); part blockIdx.z % 2 = 0 runs its maps from I
+//      without Q (the product P_g), part 1 from 0 with Q (Q_g): the group's
+//      affine map, stored in gmaps like a segment map (P row-major, Q^T);
+//   2  the chain over the group maps from the seed, storing each group's
+//      start state in gstarts;
+//   3  expand: group g = blockIdx.z from its start state over its positions,
+//      storing every start state (the last group also the final one).
+// Serial steps: 2m + G instead of NS-1 (m ~ sqrt((NS-1)/2)), at the cost of
+// reading every map twice.
 template <int D, bool PT>
 __global__ __launch_bounds__(64 * (D / 16)) void seg_chain_kernel(Args a) {
   using C = ChainLay<D>;
@@ -964,30 +1011,50 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_chain_kernel(Args a) {
   const int wave = wave_id(), lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
   const int bh_ = blockIdx.x, b = bh_ / a.H, h = bh_ % a.H;
   const int slot = a.slot0 + (int)blockIdx.y, dir = dir_of_slot(a.dirs, slot);
-  const float* seed = (dir == 0 || a.dirs == 2) ? a.h0 : nullptr;
+  const int mode = a.ch_mode;
+  const int grp = mode == 1 ? (int)blockIdx.z >> 1 : (int)blockIdx.z;
+  const bool pmul_only = mode == 1 && (blockIdx.z & 1) == 0;   // compose P: seed I, no Q
   const int col = 16 * wave + cl;
   const uint32_t so = (uint32_t)((4 * g * D + col) * 4);        // lane offset within a [D][D] state
   const uint32_t xq = (uint32_t)((col * NX + D + 4 * g) * 4);   // lane offset of Q^T within a [D][2D] map
   const uint32_t tso = (uint32_t)((col * D + 4 * g) * 4);       // lane offset within a transposed state
-  const float* maps = a.maps + (((size_t)slot * a.B + b) * a.H + h) * (size_t)a.NS * D * NX;
+  const size_t hs = ((size_t)slot * a.B + b) * a.H + h;         // (slot, batch, head)
+  // positions of this launch: [p0, p1) of the maps read (segment maps, or the group maps in mode 2)
+  const int nsteps = a.NS - 1;
+  const int p0 = (mode == 1 || mode == 3) ? grp * a.ch_m : 0;
+  const int p1 = mode == 2 ? a.ch_groups : (mode == 1 || mode == 3) ? min(p0 + a.ch_m, nsteps) : nsteps;
+  const float* maps = mode == 2 ? a.gmaps + hs * (size_t)a.ch_groups * D * NX : a.maps + hs * (size_t)a.NS * D * NX;
   // PT: the reversed scan of a bidirectional call, which takes P_p as the
   // transpose of the forward scan's P of the same segment (its Q half is its
-  // own).
+  // own).  Never in mode 2 (group maps are stored in the plain layout).
   constexpr bool ptr = PT;
   const float* pmaps = ptr ? a.maps + ((size_t)b * a.H + h) * (size_t)a.NS * D * NX : maps;
-  float* starts = a.starts + (((size_t)slot * a.B + b) * a.H + h) * (size_t)a.NS * D * D;
+  float* starts = mode == 2 ? a.gstarts + hs * (size_t)a.ch_groups * D * D : a.starts + hs * (size_t)a.NS * D * D;
 
   for (int i = threadIdx.x; i < C::BYTES / 16; i += NTH) reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
 
   f32x4 H[MD];
-  {
-    const __amdgpu_buffer_rsrc_t r = block_rsrc(seed ? seed + ((size_t)b * a.H + h) * D * D : starts, seed ? D * D * 4 : 0);
+  if (mode == 1) {
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) H[md][rr] = (pmul_only && 16 * md + 4 * g + rr == col) ? 1.f : 0.f;
+  } else if (mode == 3) {
+    const __amdgpu_buffer_rsrc_t r = block_rsrc(a.gstarts + (hs * a.ch_groups + grp) * (size_t)D * D, D * D * 4);
+#pragma unroll
+    for (int md = 0; md < MD; ++md) H[md] = tile_load_t(r, tso, (uint32_t)(md * 16 * 4));
+  } else {
+    const float* seed = (dir == 0 || a.dirs == 2) ? a.h0 : nullptr;
+    const __amdgpu_buffer_rsrc_t r = block_rsrc(seed ? seed + ((size_t)b * a.H + h) * D * D : a.starts, seed ? D * D * 4 : 0);
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) H[md][rr] = block_load(r, so, (uint32_t)((16 * md + rr) * D * 4));
   }
-  const __amdgpu_buffer_rsrc_t st = block_rsrc(starts, (uint32_t)a.NS * D * D * 4);
+  // start states are stored in modes 0 and 3 (segment starts) and 2 (group starts)
+  const bool store_starts = mode != 1;
+  const __amdgpu_buffer_rsrc_t st =
+      block_rsrc(starts, store_starts ? (uint32_t)(mode == 2 ? a.ch_groups : a.NS) * D * D * 4 : 0);
 
   // Maps in flight, one step ahead: P (float4 number threadIdx.x + NTH i) and
   // Q (this lane's accumulator-layout tiles).
@@ -1013,8 +1080,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_chain_kernel(Args a) {
       }
     }
   };
+  // Q of map p; compose-P reads none (an empty range: zeros)
   auto fetch_q = [&](int p, f32x4 (&q)[MD]) {
-    const __amdgpu_buffer_rsrc_t m = block_rsrc(maps + (size_t)p * D * NX, D * NX * 4);
+    const __amdgpu_buffer_rsrc_t m = block_rsrc(maps + (size_t)p * D * NX, pmul_only ? 0 : D * NX * 4);
 #pragma unroll
     for (int md = 0; md < MD; ++md) q[md] = tile_load_t(m, xq, (uint32_t)(16 * md * 4));
   };
@@ -1032,14 +1100,13 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_chain_kernel(Args a) {
     }
   };
 
-  const int nsteps = a.NS - 1;
-  auto last = [&](int p) { return p < nsteps ? p : nsteps - 1; };   // clamped map index
+  auto last = [&](int p) { return p < p1 ? p : p1 - 1; };   // clamped map index
   PRegs pr;       // P of the next step's map
   f32x4 qn[MD];   // Q of the current step's map, then of the next one
-  // Step p: H_{p+1} = P_p H_p + Q_p with P_p staged in LDS buffer p & 1;
+  // Step p: H_{p+1} = P_p H_p + Q_p with P_p staged in LDS buffer (p - p0) & 1;
   // P_{p+1} is fetched meanwhile and staged at the end of the step.
   auto step = [&](int p) {
-    // start state of segment p
+    // start state of position p (compose stores none: an empty range)
 #pragma unroll
     for (int md = 0; md < MD; ++md) tile_store_t(st, tso, (uint32_t)((p * D * D + 16 * md) * 4), H[md]);
     s16x4_t hh[2 * NP], hl[2 * NP];
@@ -1057,7 +1124,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_chain_kernel(Args a) {
     for (int md = 0; md < MD; ++md) acc[md] = qn[md];
     fetch_q(last(p + 1), qn);
     fetch_p(last(p + 1), pr);
-    const bh* phi = reinterpret_cast<const bh*>(smem + (p & 1) * 2 * C::MAT);
+    const bh* phi = reinterpret_cast<const bh*>(smem + ((p - p0) & 1) * 2 * C::MAT);
     const bh* plo = phi + C::MAT / 2;
 #pragma unroll
     for (int q = 0; q < NP; ++q) {
@@ -1089,13 +1156,13 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_chain_kernel(Args a) {
     }
 #pragma unroll
     for (int md = 0; md < MD; ++md) H[md] = acc[md];
-    stage((p + 1) & 1, pr);
+    stage((p + 1 - p0) & 1, pr);
     __syncthreads();
   };
 
-  if (nsteps > 0) {
-    fetch_p(0, pr);
-    fetch_q(0, qn);
+  if (p1 > p0) {
+    fetch_p(p0, pr);
+    fetch_q(p0, qn);
     __syncthreads();   // zero fill done
     stage(0, pr);
     __syncthreads();
@@ -1104,9 +1171,25 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_chain_kernel(Args a) {
   // needs for the seed state on the loop's entry path is placed at the loop
   // header and executed every step, where it waits for the prefetched maps.
   __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
-  for (int p = 0; p < nsteps; ++p) step(p);
+  for (int p = p0; p < p1; ++p) step(p);
+  if (mode == 1) {
+    // the group's map: P_g row-major, Q_g transposed
+    const __amdgpu_buffer_rsrc_t xr = block_rsrc(a.gmaps + (hs * a.ch_groups + grp) * (size_t)D * NX, D * NX * 4);
+    if (pmul_only) {
+      const uint32_t xo = (uint32_t)((4 * g * NX + col) * 4);
 #pragma unroll
-  for (int md = 0; md < MD; ++md) tile_store_t(st, tso, (uint32_t)(((a.NS - 1) * D * D + 16 * md) * 4), H[md]);
+      for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) block_store(xr, xo, (uint32_t)((md * 16 + r) * NX * 4), H[md][r]);
+    } else {
+#pragma unroll
+      for (int md = 0; md < MD; ++md) tile_store_t(xr, xq, (uint32_t)(md * 16 * 4), H[md]);
+    }
+  } else if (mode == 0 || (mode == 3 && p1 == nsteps)) {
+    // the final state of the chain, at position NS - 1
+#pragma unroll
+    for (int md = 0; md < MD; ++md) tile_store_t(st, tso, (uint32_t)(((a.NS - 1) * D * D + 16 * md) * 4), H[md]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1587,7 +1670,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void jac_out_kernel(Args a) {
 struct Plan {
   int L, NS, ndir, dirs;
   bool cc;       // chunk-causal: forward maps and chain only; the reversed scan runs per chunk
-  size_t maps_off, starts_off, acc_off, fac_off, bytes;
+  ChainWs cw;    // split of the chain
+  size_t maps_off, starts_off, acc_off, fac_off, gmaps_off, gstarts_off, bytes;
 };
 
 Plan make_plan(const Problem& p, int direction) {
@@ -1620,8 +1704,35 @@ Plan make_plan(const Problem& p, int direction) {
   pl.starts_off = align_up(maps, 256);
   pl.acc_off = pl.starts_off + align_up(starts, 256);
   pl.fac_off = pl.acc_off + align_up(acc, 256);
-  pl.bytes = pl.fac_off + align_up(prologue_bytes(p), 256);
+  // bidirectional calls never split the chain (see launch_d)
+  if (pl.dirs != 3) pl.cw = chain_ws(pl.NS - 1, bhd, p.dk, p.dv);
+  pl.gmaps_off = pl.fac_off + align_up(prologue_bytes(p), 256);
+  pl.gstarts_off = pl.gmaps_off + pl.cw.gmaps_bytes;
+  pl.bytes = pl.gstarts_off + pl.cw.gstarts_bytes;
   return pl;
+}
+
+// The chain of `nsl` scan slots from a.slot0, whole or split (compose, chain
+// of groups, expand); `pt`: the reversed scan of a bidirectional call.
+template <int D>
+hipError_t chain_launch(Args a, const ChainWs& cw, unsigned bhc, unsigned nsl, bool pt, hipStream_t st,
+                        bool split = true) {
+  a.ch_m = cw.m;
+  a.ch_groups = cw.groups;
+  if (!split) a.ch_m = a.ch_groups = 0;
+  auto go = [&](int mode, unsigned gz, bool ptv) -> hipError_t {
+    a.ch_mode = mode;
+    if (ptv)
+      hipLaunchKernelGGL((seg_chain_kernel<D, true>), dim3(bhc, nsl, gz), dim3(64 * (D / 16)), 0, st, a);
+    else
+      hipLaunchKernelGGL((seg_chain_kernel<D, false>), dim3(bhc, nsl, gz), dim3(64 * (D / 16)), 0, st, a);
+    return hipGetLastError();
+  };
+  if (a.ch_m == 0) return go(0, 1, pt);
+  hipError_t e;
+  if ((e = go(1, 2 * cw.groups, pt)) != hipSuccess) return e;
+  if ((e = go(2, 1, false)) != hipSuccess) return e;
+  return go(3, cw.groups, pt);
 }
 
 // A library-owned stream per device (default priority) with a fork and a join
@@ -1683,6 +1794,8 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
   a.dirs = pl.dirs;
   a.out_bf16 = p.out_bf16 ? 1 : 0;
   a.c = p.key_scale;
+  a.gmaps = reinterpret_cast<float*>(ws + pl.gmaps_off);
+  a.gstarts = reinterpret_cast<float*>(ws + pl.gstarts_off);
   const unsigned bhc = (unsigned)(p.B * p.H);
   const bool both = pl.dirs == 3;
   // Workgroups are dealt to the 8 XCDs (each with its own L2) in turn.  With
@@ -1713,14 +1826,17 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
     return hipSuccess;
   };
   // Chain of the scan in `slot`.
+  // The split chain (many workgroups for a short time) pays off where the
+  // chain stands alone on the critical path; beside the other scan's maps
+  // and outputs in the two-stream bidirectional schedule, the single
+  // workgroup per head is faster (measured: 2.46 against 2.33 ms per step at
+  // the 60 s clip), so bidirectional calls never split (in either schedule,
+  // which keeps the two schedules' results identical).
+  const bool split = !both;
   auto chain_k = [&](int slot, hipStream_t st) -> hipError_t {
     a.slot0 = slot;
     prof_begin(st, GDN_KERNEL_SEG_CHAIN);
-    if (both && slot == 1)
-      hipLaunchKernelGGL((seg_chain_kernel<D, true>), dim3(bhc, 1), dim3(64 * (D / 16)), 0, st, a);
-    else
-      hipLaunchKernelGGL((seg_chain_kernel<D, false>), dim3(bhc, 1), dim3(64 * (D / 16)), 0, st, a);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = chain_launch<D>(a, pl.cw, bhc, 1, both && slot == 1, st, split);
     if (e != hipSuccess) return e;
     prof_end(st, GDN_KERNEL_SEG_CHAIN);
     return hipSuccess;
@@ -1864,7 +1980,8 @@ int chunked_segment_tokens(const Problem& p, int direction) { return make_plan(p
 namespace {
 struct JacPlan {
   int ndir, dirs;
-  size_t maps_off, starts_off, fac_off, bytes;
+  ChainWs cw;
+  size_t maps_off, starts_off, fac_off, gmaps_off, gstarts_off, bytes;
 };
 JacPlan jac_plan(const Problem& p, int direction) {
   JacPlan pl{};
@@ -1874,7 +1991,10 @@ JacPlan jac_plan(const Problem& p, int direction) {
   pl.maps_off = 0;
   pl.starts_off = align_up(per * p.dk * (p.dk + p.dv) * sizeof(float), 256);
   pl.fac_off = pl.starts_off + align_up(per * p.dk * p.dv * sizeof(float), 256);
-  pl.bytes = pl.fac_off + align_up(prologue_bytes(p), 256);
+  pl.cw = chain_ws(p.F, (size_t)pl.ndir * p.B * p.H, p.dk, p.dv);
+  pl.gmaps_off = pl.fac_off + align_up(prologue_bytes(p), 256);
+  pl.gstarts_off = pl.gmaps_off + pl.cw.gmaps_bytes;
+  pl.bytes = pl.gstarts_off + pl.cw.gstarts_bytes;
   return pl;
 }
 
@@ -1913,9 +2033,10 @@ hipError_t jac_launch_d(const Problem& p, const JacPlan& pl, const Tensors& t, c
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_end(stream, GDN_KERNEL_JAC_MAP);
   a.slot0 = 0;
+  a.gmaps = reinterpret_cast<float*>(ws + pl.gmaps_off);
+  a.gstarts = reinterpret_cast<float*>(ws + pl.gstarts_off);
   prof_begin(stream, GDN_KERNEL_SEG_CHAIN);
-  hipLaunchKernelGGL((seg_chain_kernel<D, false>), dim3(bhc, pl.ndir), dim3(64 * (D / 16)), 0, stream, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = chain_launch<D>(a, pl.cw, bhc, (unsigned)pl.ndir, false, stream)) != hipSuccess) return e;
   prof_end(stream, GDN_KERNEL_SEG_CHAIN);
   prof_begin(stream, GDN_KERNEL_JAC_OUT);
   if (p.out_bf16)
@@ -1954,6 +2075,7 @@ hipError_t jacobi_launch(const Problem& p, int direction, const Tensors& t, void
 }
 
 void set_segment_tokens(int tokens) { g_segment_override.store(tokens > 0 ? tokens : 0); }
+void set_chain_group(int maps) { g_chain_group.store(maps > 0 ? maps : 0); }
 void set_concurrent_scans(bool on) { g_concurrent_scans.store(on); }
 
 }  // namespace gdn

@@ -59,6 +59,7 @@ size_t prologue_bytes(const Problem& p);
 hipError_t prologue_launch(const Problem& p, const Tensors& t, float* fac, hipStream_t stream);
 
 void set_segment_tokens(int tokens);
+void set_chain_group(int maps);
 void set_concurrent_scans(bool on);
 int chunked_segment_tokens(const Problem& p, int direction);
 

@@ -215,6 +215,18 @@ const char* gdn_kernel_name(int32_t kernel);   /* static text; "" if unknown */
  * the workspace after setting it.  Thread-safe. */
 void gdn_set_segment_tokens(int32_t tokens);
 
+/* Tuning knob of the chunked and frame-level paths: how the serial chain of
+ * segment (or frame) maps is evaluated.  0 (default): automatic; a chain of 16
+ * or more maps is split into groups of about sqrt(maps / 2): each group's maps
+ * are composed in parallel, the group maps chained, then each group expanded
+ * from its start state (about 2 sqrt(2 maps) serial steps instead of one per
+ * map).  1: never split.  m >= 2: groups of m maps whenever the chain is
+ * longer than m.  Bidirectional calls of the chunked path never split (there
+ * the two scans' chains run beside the other scan's kernels).  Results differ
+ * only by rounding.  Process-wide; thread-safe; gdn_workspace_size() depends
+ * on it, so size the workspace after setting it. */
+void gdn_set_chain_group(int32_t maps);
+
 /* Tuning knob of the chunked path: 1 (default) lets a bidirectional call run
  * the two scans' segment maps and chains partly concurrently on a second,
  * library-owned stream; 0 runs every kernel on the call's stream, in order

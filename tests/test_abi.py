@@ -177,3 +177,25 @@ def test_feature_prologue_validation_and_workspace():
     p = prob(prologue="features", first_chunk_frames=2, chunk_frames=1)
     assert G.workspace_size(p, "chunk_causal") > G.workspace_size(prob(first_chunk_frames=2, chunk_frames=1),
                                                                   "chunk_causal")
+
+
+def test_split_chain_workspace():
+    """A split chain adds group maps and group start states to the workspace;
+    the knob is process-wide and restored."""
+    p = prob(frames=40, tokens_per_frame=100, algo="chunked")
+    try:
+        G.set_segment_tokens(64)
+        G.set_chain_group(1)
+        whole = G.workspace_size(p, "fwd")
+        G.set_chain_group(4)
+        split = G.workspace_size(p, "fwd")
+        bidir = G.workspace_size(p, "bidir")
+        G.set_chain_group(1)
+        assert bidir == G.workspace_size(p, "bidir")   # bidirectional chains are never split
+    finally:
+        G.set_chain_group(0)
+        G.set_segment_tokens(0)
+    steps = (40 * 100 + 63) // 64 - 1
+    groups = (steps + 3) // 4
+    extra = 1 * 2 * groups * 64 * (128 + 64) * 4
+    assert split - whole == pytest.approx(extra, abs=512)

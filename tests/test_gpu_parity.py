@@ -224,6 +224,61 @@ def test_many_segments_and_heads():
         G.set_segment_tokens(0)
 
 
+# ---------------------------------------------------------------- split chain
+
+@pytest.mark.parametrize("group", [2, 3, 7])
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+def test_split_chain_chunked(group, direction):
+    """The chain of segment maps split into groups (composed in parallel,
+    chained, expanded) agrees with the oracle and with the whole chain:
+    600 tokens in segments of 64 (10 segments, 9 chain steps)."""
+    w = WORKLOADS[4].resized(frames=4, tokens_per_frame=150, heads=3)
+    x = make_inputs(w, 90 + group)
+    G.set_segment_tokens(64)
+    try:
+        G.set_chain_group(1)
+        whole = run_gpu(w, x, direction, "chunked")
+        G.set_chain_group(group)
+        split = check(w, x, direction, "chunked")
+        o, hT = run_gpu(w, x, direction, "chunked")
+    finally:
+        G.set_chain_group(0)
+        G.set_segment_tokens(0)
+    # both are within the bar of the oracle; between them only the chain's
+    # rounding differs (start states feed the output kernel's fp16 operands,
+    # so a flipped fp16 rounding of a state element shows at ~2^-11 relative)
+    assert rel_err(o, whole[0]) <= 1e-2 and rel_err(hT, whole[1]) <= 1e-2, split
+
+
+@pytest.mark.parametrize("group", [2, 4])
+def test_split_chain_jacobi(group):
+    w = WORKLOADS[4].resized(frames=11, tokens_per_frame=40, heads=2)
+    x = make_inputs(w, 95)
+    G.set_chain_group(group)
+    try:
+        o, hT = run_jacobi(w, x, "bidir")
+    finally:
+        G.set_chain_group(0)
+    ro, rH = O.jacobi_bidir(*oracle_args(x)[0], x["h0"], key_scale=w.tokens_per_frame ** -0.5,
+                            tokens_per_frame=w.tokens_per_frame)
+    assert rel_err(o, ro) <= TOL["bf16"] and rel_err(hT, rH) <= TOL["bf16"]
+
+
+def test_split_chain_chunk_causal():
+    w = WORKLOADS[4].resized(frames=6, tokens_per_frame=100, heads=2)
+    x = make_inputs(w, 96)
+    G.set_segment_tokens(64)
+    G.set_chain_group(3)
+    try:
+        o, hT = run_cc(w, x, 2, 2, "chunked")
+    finally:
+        G.set_chain_group(0)
+        G.set_segment_tokens(0)
+    ro, rH = O.chunk_causal(*oracle_args(x)[0], x["h0"], tokens_per_frame=w.tokens_per_frame,
+                            first_chunk_frames=2, chunk_frames=2)
+    assert rel_err(o, ro) <= TOL["bf16"] and rel_err(hT, rH) <= TOL["bf16"]
+
+
 # ---------------------------------------------------------------- chunk-causal layer
 
 CC = {
