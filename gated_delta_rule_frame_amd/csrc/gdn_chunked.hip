@@ -119,8 +119,7 @@ struct Args {
   int mode;             // output kernel: 0 store outputs, 1 store the partial, 2 add the partial
   int out_bf16;
   float c;              // key scale
-  const float* fk;      // feature prologue: per-(token, head) key factors ([B][T][H]), or null
-  const float* fq;      // ... and query factors
+  const float* fac;     // feature prologue factors (fk, fq) per token, [B][H][T + 2][2] (token t at t + 1), or null
   int ch_mode;          // chain kernel: 0 whole chain, 1 compose groups, 2 chain of groups, 3 expand groups
   int ch_m, ch_groups;  // ... maps per group, groups
   float* gmaps;         // ... composed group maps [ndir][B][H][groups][DK][DK+DV]
@@ -396,6 +395,16 @@ __device__ __forceinline__ void tile_store_t(__amdgpu_buffer_rsrc_t r, uint32_t 
 // writing LDS so that the loads of sub-chunk c+2 are in flight while sub-chunk
 // c is computed.  Every load is unconditional: rows past n (and sub-chunks past
 // the segment, given as n = 0) read as zeros through the buffer range check.
+// Feature prologue factors of (b, h): pairs (fk, fq) of tokens t0 - 1 .. t0 + 64
+// of the padded per-head array (a pad pair of zeros before token 0 and after
+// token T - 1), so that the pair of rows (t, t + 1), t >= t0 - 1, is one
+// 16-byte load at byte (t - t0 + 1) * 8.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t fac_rsrc(const Args& a, int b, int h, long long t0) {
+  const long long i0 = ((long long)b * a.H + h) * (a.T + 2) + t0;   // pair of token t0 - 1
+  const long long avail = a.T - t0 + 2;                             // pairs through the trailing pad
+  return rows_rsrc(a.fac + 2 * i0, (avail < CH + 2 ? avail : CH + 2) * 8);
+}
+
 struct StageKQ {
   uint4 k[2], q[2];
   float fk[2], fq[2];   // feature prologue factors of the two rows
@@ -426,15 +435,24 @@ __device__ __forceinline__ void fetch_kq(const Args& a, int b, int h, const Sub&
     }
   }
   if constexpr (PRO) {
-    const long long go = ((long long)b * a.T + sb.t0) * a.H + h;
+    // rows lr and lr + sgn are adjacent tokens: one load of their two pairs
+    // (lower token first); rows past the sub-chunk read real neighbours or
+    // zeros, and their K/Q rows are zero anyway
+    const int lo = sb.sgn > 0 ? lr : lr - 1;   // sub-chunk row of the lower token
+    const __amdgpu_buffer_rsrc_t rf = fac_rsrc(a, b, h, sb.t0);
+    if constexpr (OUT) {
+      const f32x4 f = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rf, (uint32_t)((lo + 1) * 8), 0, 0));
+      const bool up = sb.sgn > 0;
+      st.fk[0] = up ? f[0] : f[2];
+      st.fq[0] = up ? f[1] : f[3];
+      st.fk[1] = up ? f[2] : f[0];
+      st.fq[1] = up ? f[3] : f[1];
+    } else {
+      // the map kernels need the key factors only (and have few registers)
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const uint32_t fo = (uint32_t)((lr + sb.sgn * r) * a.H * 4);
-      st.fk[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                rows_rsrc(a.fk + go, (long long)sb.n * a.H * 4), fo, 0, 0));
-      if constexpr (OUT)
-        st.fq[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                  rows_rsrc(a.fq + go, (long long)sb.n * a.H * 4), fo, 0, 0));
+      for (int r = 0; r < 2; ++r)
+        st.fk[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                 rf, (uint32_t)((lr + sb.sgn * r + 1) * 8), 0, 0));
     }
   }
 }
@@ -1444,10 +1462,12 @@ __device__ __forceinline__ void jac_fetch(const Args& a, int b, int h, long long
     st.k[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
     st.v[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
     st.b[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, (uint32_t)(row * a.H * 4), 0, 0));
-    if constexpr (PRO) {
-      const __amdgpu_buffer_rsrc_t rf = rows_rsrc(a.fk + ((long long)b * a.T + t0) * a.H + h, (long long)n * a.H * 4);
-      st.fk[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rf, (uint32_t)(row * a.H * 4), 0, 0));
-    }
+  }
+  if constexpr (PRO) {
+    const f32x4 f = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  fac_rsrc(a, b, h, t0), (uint32_t)((2 * i2 + 1) * 8), 0, 0));
+    st.fk[0] = f[0];
+    st.fk[1] = f[2];
   }
 }
 
@@ -1618,11 +1638,10 @@ __global__ __launch_bounds__(64 * (D / 16)) void jac_out_kernel(Args a) {
       qv[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                             rq, (uint32_t)((2 * i2 + r) * HD * 2 + 16 * c8), 0, 0));
     if constexpr (PRO) {
-      const __amdgpu_buffer_rsrc_t rf = rows_rsrc(a.fq + ((long long)b * a.T + tf + CH * p) * a.H + h,
-                                                  (long long)piece_n(p) * a.H * 4);
-#pragma unroll
-      for (int r = 0; r < 2; ++r)
-        fq[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rf, (uint32_t)((2 * i2 + r) * a.H * 4), 0, 0));
+      const f32x4 f = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    fac_rsrc(a, b, h, tf + CH * p), (uint32_t)((2 * i2 + 1) * 8), 0, 0));
+      fq[0] = f[1];
+      fq[1] = f[3];
     }
   };
   auto stage = [&](int buf, const uint4 (&qv)[2]) {
@@ -1772,8 +1791,7 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
     float* fac = reinterpret_cast<float*>(ws + pl.fac_off);
     const hipError_t e = prologue_launch(p, t, fac, stream);
     if (e != hipSuccess) return e;
-    a.fk = fac;
-    a.fq = fac + (size_t)p.B * p.T * p.H;
+    a.fac = fac;
   }
   a.q = static_cast<const bh*>(t.q);
   a.k = static_cast<const bh*>(t.k);
@@ -2005,8 +2023,7 @@ hipError_t jac_launch_d(const Problem& p, const JacPlan& pl, const Tensors& t, c
     float* fac = reinterpret_cast<float*>(ws + pl.fac_off);
     const hipError_t e = prologue_launch(p, t, fac, stream);
     if (e != hipSuccess) return e;
-    a.fk = fac;
-    a.fq = fac + (size_t)p.B * p.T * p.H;
+    a.fac = fac;
   }
   a.q = static_cast<const bh*>(t.q);
   a.k = static_cast<const bh*>(t.k);

@@ -53,8 +53,9 @@ hipError_t jacobi_launch(const Problem& p, int direction, const Tensors& t,
                          void* workspace, hipStream_t stream);
 
 // Feature prologue (gdn_prologue.hip): two fp32 factors per (token, head) in
-// the workspace, keys first: fac[n] = 1/sqrt(mean k^2 + eps) and
-// fac[rows + n] = 1/sqrt(sum q^2 + eps), n = (b T + t) H + h, rows = B T H.
+// the workspace, pairs (fk, fq) = (1/sqrt(mean k^2 + eps), 1/sqrt(sum q^2 + eps)):
+// fac[2 i], fac[2 i + 1] with i = (b H + h)(T + 2) + t + 1 (a zero pair before
+// token 0 and after token T - 1 of every (batch, head)).
 size_t prologue_bytes(const Problem& p);
 hipError_t prologue_launch(const Problem& p, const Tensors& t, float* fac, hipStream_t stream);
 

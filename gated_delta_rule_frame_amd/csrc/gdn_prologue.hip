@@ -13,7 +13,9 @@
 // apply the ReLU to keys) while staging, and the normalised tensors never
 // reach memory.  One pass reads q and k once: 16 lanes per row, each lane
 // one or two 16-byte pieces, a 16-lane shuffle reduction, four rows per lane
-// group in flight.
+// group in flight.  Layout: per (batch, head) the pairs (fk, fq) of tokens
+// -1 .. T (T + 2 pairs, the two pads zero), so that two neighbouring tokens'
+// factors are one 16-byte load for any token pair a kernel stages.
 #include "gdn_common.h"
 #include "gdn_internal.h"
 
@@ -21,7 +23,8 @@ namespace gdn {
 namespace {
 
 constexpr float kEps = 1e-6f;
-constexpr int kRowsPerBlock = 64;   // 16 lane groups x 4 rows
+constexpr int kTokensPerBlock = 16;   // 16 lane groups: 4 heads x 4 tokens, 4 rows each
+constexpr int kHeadsPerBlock = 4;
 
 __device__ __forceinline__ float sq_sum(uint4 u, bool bf16) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
@@ -48,22 +51,27 @@ __device__ __forceinline__ float group16_sum(float x) {
   return x;
 }
 
-// Block: 256 threads, rows blockIdx.x * 64 + 16 j + (threadIdx.x / 16), j < 4
-// (each wavefront reads 4 consecutive rows per j).  U 16-byte pieces per row.
+// Block: 256 threads, lane group grp = threadIdx.x / 16 on head
+// blockIdx.y * 4 + grp % 4 and tokens blockIdx.x * 16 + 4 (grp / 4) + j, j < 4,
+// of batch blockIdx.z: the four groups of a wavefront read the same token of
+// four neighbouring heads, one contiguous stretch of the [B, T, H, d] tensor
+// (a token's row of q or k is U 16-byte pieces), and each group writes the
+// factor pairs of four consecutive tokens (32 contiguous bytes).
 template <bool BF16IN, int DK>
 __global__ __launch_bounds__(256) void prologue_kernel(const uint4* __restrict__ q, const uint4* __restrict__ k,
-                                                       float* __restrict__ fk, float* __restrict__ fq,
-                                                       long long rows) {
+                                                       float2* __restrict__ fac, long long T, int H) {
   constexpr int U = DK * (BF16IN ? 2 : 4) / 16;   // <= 32
   constexpr int NU = (U + 15) / 16;
-  const int l = threadIdx.x & 15;
-  const long long r0 = (long long)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 4);
+  const int l = threadIdx.x & 15, grp = threadIdx.x >> 4;
+  const int h = blockIdx.y * kHeadsPerBlock + (grp & 3), b = blockIdx.z;
+  const long long t0 = (long long)blockIdx.x * kTokensPerBlock + 4 * (grp >> 2);
+  float2* const fh = fac + ((long long)b * H + h) * (T + 2) + 1;   // pair of token 0
   float sk[4], sq[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const long long row = r0 + 16 * j;
+    const long long t = t0 + j, row = ((long long)b * T + t) * H + h;
     sk[j] = sq[j] = 0.f;
-    if (row < rows) {
+    if (t < T && h < H) {
 #pragma unroll
       for (int i = 0; i < NU; ++i) {
         const int u = l + 16 * i;
@@ -76,11 +84,12 @@ __global__ __launch_bounds__(256) void prologue_kernel(const uint4* __restrict__
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float a = group16_sum(sk[j]), b = group16_sum(sq[j]);
-    const long long row = r0 + 16 * j;
-    if (l == 0 && row < rows) {
-      fk[row] = 1.f / __builtin_sqrtf(a / (float)DK + kEps);
-      fq[row] = 1.f / __builtin_sqrtf(b + kEps);
+    const float a = group16_sum(sk[j]), c = group16_sum(sq[j]);
+    const long long t = t0 + j;
+    if (l == 0 && t < T && h < H) {
+      fh[t] = make_float2(1.f / __builtin_sqrtf(a / (float)DK + kEps), 1.f / __builtin_sqrtf(c + kEps));
+      if (t == 0) fh[-1] = make_float2(0.f, 0.f);
+      if (t == T - 1) fh[T] = make_float2(0.f, 0.f);
     }
   }
 }
@@ -88,25 +97,24 @@ __global__ __launch_bounds__(256) void prologue_kernel(const uint4* __restrict__
 }  // namespace
 
 size_t prologue_bytes(const Problem& p) {
-  return p.prologue ? 2 * (size_t)p.B * p.T * p.H * sizeof(float) : 0;
+  return p.prologue ? 2 * (size_t)p.B * p.H * (p.T + 2) * sizeof(float) : 0;
 }
 
 hipError_t prologue_launch(const Problem& p, const Tensors& t, float* fac, hipStream_t stream) {
-  const long long rows = (long long)p.B * p.T * p.H;
-  const long long blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
-  float* fk = fac;
-  float* fq = fac + rows;
+  const dim3 grid((unsigned)((p.T + kTokensPerBlock - 1) / kTokensPerBlock),
+                  (unsigned)((p.H + kHeadsPerBlock - 1) / kHeadsPerBlock), (unsigned)p.B);
+  float2* f2 = reinterpret_cast<float2*>(fac);
   const uint4* q = static_cast<const uint4*>(t.q);
   const uint4* k = static_cast<const uint4*>(t.k);
   prof_begin(stream, GDN_KERNEL_PROLOGUE);
 #define GDN_PRO_CASE(D)                                                                                   \
   case D:                                                                                                 \
     if (p.qkv_bf16)                                                                                       \
-      hipLaunchKernelGGL((prologue_kernel<true, D>), dim3((unsigned)blocks), dim3(256), 0, stream, q, k, \
-                         fk, fq, rows);                                                                   \
+      hipLaunchKernelGGL((prologue_kernel<true, D>), grid, dim3(256), 0, stream, q, k, f2, p.T, \
+                         p.H);                                                                   \
     else                                                                                                  \
-      hipLaunchKernelGGL((prologue_kernel<false, D>), dim3((unsigned)blocks), dim3(256), 0, stream, q, k, \
-                         fk, fq, rows);                                                                   \
+      hipLaunchKernelGGL((prologue_kernel<false, D>), grid, dim3(256), 0, stream, q, k, f2, p.T, \
+                         p.H);                                                                   \
     break;
   switch (p.dk) {
     GDN_PRO_CASE(16) GDN_PRO_CASE(32) GDN_PRO_CASE(48) GDN_PRO_CASE(64)

@@ -31,7 +31,7 @@ __global__ __launch_bounds__(64) void recurrent_kernel(
     const float* __restrict__ g, const float* __restrict__ beta, const float* h0,
     void* __restrict__ out, float* hT, float* __restrict__ acc, long long T, int H, int DV,
     int reverse, int out_mode, int out_bf16, float key_scale, long long reset_first, long long reset_every,
-    const float* __restrict__ fk, const float* __restrict__ fq) {
+    const float* __restrict__ fac) {
   constexpr int R = DK / 4;
   const int lane = threadIdx.x;
   const int c = lane & 15, r0 = lane >> 4;
@@ -57,10 +57,12 @@ __global__ __launch_bounds__(64) void recurrent_kernel(
       const long long tau = reverse ? T - 1 - (t0 + j) : t0 + j;
       const size_t row = ((size_t)b * T + tau) * H + h, off = row * DK + i;
       float kv = load_scalar<BF16IN>(k, off), qv = load_scalar<BF16IN>(q, off);
-      if (fk) {
-        kv *= fk[row];
+      if (fac) {
+        // (fk, fq) of token tau: pair tau + 1 of this (batch, head)
+        const float* f = fac + 2 * (((size_t)b * H + h) * (T + 2) + tau + 1);
+        kv *= f[0];
         kv = kv < 0.f ? 0.f : kv;
-        qv *= fq[row];
+        qv *= f[1];
       }
       ks[j][i] = kv * key_scale;
       qs[j][i] = qv;
@@ -127,8 +129,6 @@ template <bool BF16IN>
 hipError_t launch_dk(const Problem& p, const Tensors& t, bool reverse, const float* h0, int out_mode,
                      float* acc, const float* fac, bool write_state, hipStream_t stream, long long reset_first = 0,
                      long long reset_every = 0) {
-  const float* fk = fac;
-  const float* fq = fac ? fac + (size_t)p.B * p.T * p.H : nullptr;
   dim3 grid(p.dv / kCols, p.H, p.B), block(64);
   float* hT = write_state ? t.hT : nullptr;
   prof_begin(stream, GDN_KERNEL_RECURRENT);
@@ -137,7 +137,7 @@ hipError_t launch_dk(const Problem& p, const Tensors& t, bool reverse, const flo
     hipLaunchKernelGGL((recurrent_kernel<BF16IN, D>), grid, block, 0, stream, t.q, t.k, t.v, \
                        t.g, t.beta, h0, t.out,           hT, acc, p.T, p.H, p.dv,  \
                        reverse ? 1 : 0, out_mode, p.out_bf16 ? 1 : 0, p.key_scale,            \
-                       reset_first, reset_every, fk, fq);                                     \
+                       reset_first, reset_every, fac);                                        \
     break;
   switch (p.dk) {
     GDN_REC_CASE(16) GDN_REC_CASE(32) GDN_REC_CASE(48) GDN_REC_CASE(64)

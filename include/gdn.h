@@ -111,7 +111,7 @@ enum { GDN_INTRA_SEQUENTIAL = 0, GDN_INTRA_JACOBI = 1 };
  * tensors are never written to memory: a first kernel reads q and k once and
  * stores two fp32 factors per (token, head) in the workspace, and every
  * kernel that loads q or k applies them (and the ReLU) as it loads.  Every
- * path and direction supports it; the workspace grows by 8 * B * T * H
+ * path and direction supports it; the workspace grows by 8 * B * H * (T + 2)
  * bytes. */
 enum { GDN_PROLOGUE_NONE = 0, GDN_PROLOGUE_FEATURES = 1 };
 

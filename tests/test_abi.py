@@ -166,7 +166,7 @@ def test_feature_prologue_validation_and_workspace():
     with pytest.raises(G.GdnError) as e:
         G.workspace_size(p, "bidir")
     assert e.value.status == G.ERR_INVALID_ARGUMENT
-    fac = 2 * 1 * 300 * 2 * 4
+    fac = 2 * 1 * 2 * (300 + 2) * 4   # (fk, fq) pairs of tokens -1 .. T per (batch, head)
     rounded = (fac + 255) // 256 * 256
     for kw in (dict(algo="recurrent"), dict(algo="chunked"), dict(intra="jacobi"),
                dict(algo="recurrent", qkv_dtype=G.F32)):
