@@ -20,32 +20,41 @@
 //
 // Schedule.  The token axis is cut, in original order, into segments of L
 // tokens (a multiple of 64) and each segment into 64-token sub-chunks; a scan
-// direction visits both in its own order.  Three launches per call:
+// direction visits both in its own order.  Per scan direction:
 //   1. seg_map_kernel   (parallel over segments): the segment's affine state
 //      map H_end = P H_start + Q, by running the sub-chunk chain on the
-//      augmented state X = [P | Q] from [I | 0] with values [0 | V];
+//      augmented state X = [P | Q] from [I | 0] with values [0 | V]
+//      (seg_map_q_kernel: Q alone, for the reversed scan of a bidirectional
+//      call, whose P is the transpose of the forward one);
 //   2. seg_chain_kernel (serial over segments, parallel over heads and value
 //      columns): H_{s+1} = P_s H_s + Q_s in split-bf16 (hi + lo) MFMA, i.e. the
-//      prefix composition of the segments' transition maps;
+//      prefix composition of the segments' transition maps, whole or split
+//      into groups (compose, chain of groups, expand);
 //   3. seg_out_kernel   (parallel over segments): each segment re-run from its
-//      true start state, writing outputs (both scan directions of a segment in
-//      one workgroup, summed before the single store) and the final state.
+//      true start state, writing outputs and the final state.  In a
+//      bidirectional call the forward launch stores an fp32 partial and the
+//      reversed launch adds it before the single final store.
+// The frame-level (Jacobi) transition at the end of this file reuses the
+// chain kernel between its own per-frame map and output kernels.
 //
 // Workgroups of the map and output kernels: one wavefront per 16-column strip
 // of the state ("strip waves", the state strip lives in its registers) plus
 // one helper wavefront.  Per sub-chunk c there are two phases:
-//   alpha: every wave writes its share of sub-chunk c+1 into the other LDS
-//          buffer and starts the global loads of c+2; the helper inverts
-//          I + A_c; the strip waves form Q H and K H and R.
-//   beta:  the strip waves form V', the outputs and the new state; all waves
-//          compute the Gram tiles (A and P) of sub-chunk c+1.
+//   alpha: the strip waves write their share of sub-chunk c+1's rows into the
+//          other LDS buffer (and store c-1's outputs) and form K H and R; the
+//          helper stages c+1's gate factors and inverts the off-diagonal
+//          blocks of I + A_c.
+//   beta:  the strip waves form Q H, V', the outputs and the new state and
+//          the off-diagonal Gram tiles (A and P) of sub-chunk c+1; the helper
+//          forms and inverts c+1's diagonal blocks.
 // so the triangular inverse, which is serial, overlaps the state products.
 // All states and accumulations are fp32.  MFMA operands are fp16: the bf16
 // inputs convert to fp16 exactly (in fp16's normal range) and each rounded
 // intermediate (Tm, H, R, V', P) keeps 11 significant bits.  Precondition of
 // this path: inputs and intermediate magnitudes stay below fp16's maximum
-// (65504).  Every MFMA here is the 16x16x32 f16 form except the 16x16 block
-// products of the inverse, which start from a zero accumulator.
+// (65504).  The map and output kernels use the 16x16x32 f16 MFMA (16x16x16
+// for the inverse's block products, from a zero accumulator); the chain uses
+// the 16x16x32 bf16 form on split operands.
 #include "gdn_common.h"
 #include "gdn_internal.h"
 #include "gdn_mfma.h"
@@ -1211,11 +1220,13 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_chain_kernel(Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// 3. Outputs.  grid (NS, B * H), one launch per requested direction (the
-// reversed scan first): each workgroup re-runs its segment from the start
-// state of the chain.  In a bidirectional call the reversed scan stores its
-// outputs as a partial that the forward scan's launch adds to its own.
-// Strip wave w owns state columns 16 w .. 16 w + 15.
+// 3. Outputs.  grid (segments padded to a multiple of 8, B * H), one launch
+// per scan direction: each workgroup re-runs its segment from the start state
+// of the chain (or, for the chunk-causal reversed scan, a chunk of frames from
+// zero).  Mode 1 stores the outputs as an fp32 partial, mode 2 adds the
+// partial before the single final store (bidirectional: the forward launch
+// stores, the reversed one adds; chunk-causal: the other way round).  Strip
+// wave w owns state columns 16 w .. 16 w + 15.
 template <int D, bool PRO, bool OB>
 __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
   using G = Geo<D>;
