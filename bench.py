@@ -170,7 +170,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="clip60s_121x880_h20d112")
     ap.add_argument("--direction", default=None, choices=["fwd", "bwd", "bidir", "chunk_causal"])
     ap.add_argument("--chunks", default="4,3",

@@ -224,6 +224,28 @@ def test_many_segments_and_heads():
         G.set_segment_tokens(0)
 
 
+# ---------------------------------------------------------------- degenerate sizes
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("direction", ["fwd", "bwd", "bidir"])
+def test_single_token_sequence(algo, direction):
+    """T = 1: one frame of one token (the shortest sequence)."""
+    w = WORKLOADS[4].resized(frames=1, tokens_per_frame=1, heads=3)
+    check(w, make_inputs(w, 100), direction, algo)
+
+
+@pytest.mark.parametrize("direction", ["fwd", "bidir"])
+def test_jacobi_many_one_token_frames(direction):
+    """200 frames of one token: the frame-level chain is 200 maps long (split
+    automatically), and a frame of one token equals the token-wise step."""
+    w = WORKLOADS[4].resized(frames=200, tokens_per_frame=1, heads=2)
+    x = make_inputs(w, 101)
+    o, hT = run_jacobi(w, x, direction)
+    ro, rH = O.jacobi_forward(direction, *oracle_args(x)[0], x["h0"], key_scale=1.0,
+                              tokens_per_frame=1)
+    assert rel_err(o, ro) <= TOL["bf16"] and rel_err(hT, rH) <= TOL["bf16"]
+
+
 # ---------------------------------------------------------------- split chain
 
 @pytest.mark.parametrize("group", [2, 3, 7])
