@@ -246,6 +246,30 @@ def test_jacobi_many_one_token_frames(direction):
     assert rel_err(o, ro) <= TOL["bf16"] and rel_err(hT, rH) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("case", ["beta0", "nodecay", "strongdecay", "beta1"])
+@pytest.mark.parametrize("algo", ALGOS)
+def test_degenerate_gates(case, algo):
+    """The method's degenerate gates: beta = 0 (no writes: the initial state,
+    decayed, is only read), g = 0 (no decay), g = -20 (the state forgets at
+    once: every exp(G) underflows to 0 inside a 64-token block) and beta = 1."""
+    w = WORKLOADS[4].resized(frames=3, tokens_per_frame=100, heads=2)
+    x = make_inputs(w, 110)
+    if case == "beta0":
+        x["beta"][:] = 0.0
+    elif case == "nodecay":
+        x["log_gate"][:] = 0.0
+    elif case == "strongdecay":
+        x["log_gate"][:] = -20.0
+    else:
+        x["beta"][:] = 1.0
+    o, hT = run_gpu(w, x, "bidir", algo)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(hT))
+    ro, rH = O.bidir(*oracle_args(x)[0], x["h0"])
+    eo, eh = rel_err(o, ro), rel_err(hT, rH)
+    print(f"[parity] degenerate {case} {algo}: out {eo:.3e} state {eh:.3e}", flush=True)
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"], (eo, eh)
+
+
 # ---------------------------------------------------------------- split chain
 
 @pytest.mark.parametrize("group", [2, 3, 7])
