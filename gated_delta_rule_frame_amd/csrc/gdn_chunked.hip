@@ -112,7 +112,7 @@ struct Args {
   const float* beta;
   const float* h0;      // initial state or null
   void* out;
-  float* acc;           // fp32 partial of the reversed scan (BIDIR)
+  hb* part;             // fp16 partial outputs of the first output launch of a two-scan call
   float* hT;            // final state or null
   float* maps;          // [ndir][B][H][NS][DK][DK+DV]
   float* starts;        // [ndir][B][H][NS][DK][DV]
@@ -1227,7 +1227,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_chain_kernel(Args a) {
 // partial before the single final store (bidirectional: the forward launch
 // stores, the reversed one adds; chunk-causal: the other way round).  Strip
 // wave w owns state columns 16 w .. 16 w + 15.
-template <int D, bool PRO, bool OB>
+template <int D, bool PRO, int ST>
 __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
   using G = Geo<D>;
   using L = Lay<D, true>;
@@ -1324,25 +1324,31 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
     constexpr int NTS = 64 * G::NSW, C4 = D / 4;   // strip threads; 4-column groups per row
     static_assert(CH * C4 == 4 * NTS, "four groups of four values per strip thread");
     const int t = threadIdx.x;
-    // OB: this launch stores bf16 outputs (mode != 1 with a bf16 output),
-    // a template parameter so that every store is unconditional: stores
-    // behind a branch make the compiler assume they may not have been issued
-    // and wait for later stores where it waits for earlier loads.
-    constexpr bool half = OB;
-    const long long esz = half ? 2 : 4;
-    char* const dstb = static_cast<char*>(mode == 1 ? static_cast<void*>(a.acc) : a.out);
-    f32x4 pre[4] = {zero4(), zero4(), zero4(), zero4()};
+    // ST: what this launch stores, a template parameter so that every store
+    // is unconditional (stores behind a branch make the compiler assume they
+    // may not have been issued and wait for later stores where it waits for
+    // earlier loads): 0 fp32 outputs, 1 bf16 outputs, 2 the fp16 partial of
+    // mode 1 (half the bytes of fp32 each way; it adds a rounding of 2^-11 of
+    // the partial's magnitude to the sum).
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    const long long esz = ST == 0 ? 4 : 2;
+    char* const dstb = static_cast<char*>(ST == 2 ? static_cast<void*>(a.part) : a.out);
+    u32x2_t pre[4] = {u32x2_t{0u, 0u}, u32x2_t{0u, 0u}, u32x2_t{0u, 0u}, u32x2_t{0u, 0u}};   // fp16 partial
     auto rows_of = [&](int c) { return ((long long)b * a.T + piece(c).t0) * HD + (long long)h * D; };
     auto load_pre = [&](int c) {
       const Sub sb = piece(c);
-      const __amdgpu_buffer_rsrc_t rs = rows_rsrc(a.acc + rows_of(c), mode == 2 ? (long long)sb.n * HD * 4 : 0);
+      const __amdgpu_buffer_rsrc_t rs = rows_rsrc(a.part + rows_of(c), mode == 2 ? (long long)sb.n * HD * 2 : 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int k = t + NTS * i, row = k / C4, c4 = k % C4;
-        const u32x4_t v =
-            __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(((sb.r0 + sb.sgn * row) * (int)HD + 4 * c4) * 4), 0, 0);
-        pre[i] = __builtin_bit_cast(f32x4, v);   // whole-vector casts only: see the note on vector elements
+        pre[i] = __builtin_amdgcn_raw_buffer_load_b64(rs, (uint32_t)(((sb.r0 + sb.sgn * row) * (int)HD + 4 * c4) * 2), 0, 0);
       }
+    };
+    auto pre_f32 = [](u32x2_t w) {
+      return f32x4{(float)__builtin_bit_cast(_Float16, (uint16_t)(w[0] & 0xffffu)),
+                   (float)__builtin_bit_cast(_Float16, (uint16_t)(w[0] >> 16)),
+                   (float)__builtin_bit_cast(_Float16, (uint16_t)(w[1] & 0xffffu)),
+                   (float)__builtin_bit_cast(_Float16, (uint16_t)(w[1] >> 16))};
     };
     // Store the staged outputs of sub-chunk c (rows past n fall outside the
     // buffer).  c = -1 stores nothing (an empty range) but issues the same
@@ -1357,12 +1363,15 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int k = t + NTS * i, row = k / C4, c4 = k % C4;
-        const f32x4 val = ld4f(I.os + row * L::OSL + 4 * c4) + pre[i];
+        const f32x4 val = ld4f(I.os + row * L::OSL + 4 * c4) + pre_f32(pre[i]);
         const uint32_t off = (uint32_t)(((sb.r0 + sb.sgn * row) * (int)HD + 4 * c4) * esz);
-        if constexpr (half) {
-          typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+        if constexpr (ST == 1) {
           const u32x2_t w{f32_to_bf16_bits(val[0]) | ((uint32_t)f32_to_bf16_bits(val[1]) << 16),
                           f32_to_bf16_bits(val[2]) | ((uint32_t)f32_to_bf16_bits(val[3]) << 16)};
+          __builtin_amdgcn_raw_buffer_store_b64(w, rs, off, 0, 0);
+        } else if constexpr (ST == 2) {
+          const u32x2_t w{(uint32_t)f2h(val[0]) | ((uint32_t)f2h(val[1]) << 16),
+                          (uint32_t)f2h(val[2]) | ((uint32_t)f2h(val[3]) << 16)};
           __builtin_amdgcn_raw_buffer_store_b64(w, rs, off, 0, 0);
         } else {
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, val), rs, off, 0, 0);
@@ -1729,7 +1738,8 @@ Plan make_plan(const Problem& p, int direction) {
   const size_t bhd = (size_t)pl.ndir * p.B * p.H;
   const size_t maps = bhd * (size_t)pl.NS * p.dk * (p.dk + p.dv) * sizeof(float);
   const size_t starts = bhd * (size_t)pl.NS * p.dk * p.dv * sizeof(float);
-  const size_t acc = ((pl.dirs == 3 || pl.cc) && p.out_bf16) ? (size_t)p.B * p.T * p.H * p.dv * sizeof(float) : 0;
+  // fp16 partial of the first output launch of a two-scan call
+  const size_t acc = (pl.dirs == 3 || pl.cc) ? (size_t)p.B * p.T * p.H * p.dv * 2 : 0;
   pl.maps_off = 0;
   pl.starts_off = align_up(maps, 256);
   pl.acc_off = pl.starts_off + align_up(starts, 256);
@@ -1814,7 +1824,7 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
   a.hT = t.hT;
   a.maps = reinterpret_cast<float*>(ws + pl.maps_off);
   a.starts = reinterpret_cast<float*>(ws + pl.starts_off);
-  a.acc = p.out_bf16 ? reinterpret_cast<float*>(ws + pl.acc_off) : static_cast<float*>(t.out);
+  a.part = reinterpret_cast<hb*>(ws + pl.acc_off);
   a.T = p.T;
   a.B = p.B;
   a.H = p.H;
@@ -1872,10 +1882,12 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
   };
   // One output launch (x.mode and x.out_bf16 select the store type).
   auto launch_out = [&](const Args& x, unsigned gx, hipStream_t st) {
-    if (x.mode != 1 && x.out_bf16)
-      hipLaunchKernelGGL((seg_out_kernel<D, PRO, true>), dim3(gx, bhc, 1), dim3(Geo<D>::NT), 0, st, x);
+    if (x.mode == 1)
+      hipLaunchKernelGGL((seg_out_kernel<D, PRO, 2>), dim3(gx, bhc, 1), dim3(Geo<D>::NT), 0, st, x);
+    else if (x.out_bf16)
+      hipLaunchKernelGGL((seg_out_kernel<D, PRO, 1>), dim3(gx, bhc, 1), dim3(Geo<D>::NT), 0, st, x);
     else
-      hipLaunchKernelGGL((seg_out_kernel<D, PRO, false>), dim3(gx, bhc, 1), dim3(Geo<D>::NT), 0, st, x);
+      hipLaunchKernelGGL((seg_out_kernel<D, PRO, 0>), dim3(gx, bhc, 1), dim3(Geo<D>::NT), 0, st, x);
   };
   // Outputs of one scan direction; in a bidirectional call the forward scan
   // stores its partial and the reversed scan adds it.

@@ -141,8 +141,8 @@ def test_frame_level_transition_validation_and_workspace():
 
 def test_chunk_causal_validation_and_workspace():
     """GDN_CHUNK_CAUSAL needs chunk sizes >= 1 and the token-wise transition;
-    its chunked-path workspace holds one scan's maps and states (plus the fp32
-    partial for a bf16 output), its recurrent one the fp32 partial."""
+    its chunked-path workspace holds one scan's maps and states and the fp16
+    partial of the reversed chunks, its recurrent one the fp32 partial."""
     n = ctypes.c_size_t()
     p = prob()
     assert G.lib().gdn_workspace_size(ctypes.byref(p), G.CHUNK_CAUSAL, ctypes.byref(n)) == G.ERR_INVALID_ARGUMENT
@@ -152,9 +152,11 @@ def test_chunk_causal_validation_and_workspace():
     assert G.lib().gdn_workspace_size(ctypes.byref(p), G.CHUNK_CAUSAL, ctypes.byref(n)) == G.ERR_UNSUPPORTED
     p = prob(first_chunk_frames=2, chunk_frames=1, algo="recurrent")
     assert G.workspace_size(p, "chunk_causal") == 1 * 300 * 2 * 64 * 4
+    # chunked: the fp16 partial of the reversed chunks, whatever the output dtype
     p32 = prob(first_chunk_frames=2, chunk_frames=1, algo="chunked", out_dtype=G.F32)
     pbf = prob(first_chunk_frames=2, chunk_frames=1, algo="chunked", out_dtype=G.BF16)
-    assert G.workspace_size(pbf, "chunk_causal") - G.workspace_size(p32, "chunk_causal") >= 1 * 300 * 2 * 64 * 4
+    assert G.workspace_size(pbf, "chunk_causal") == G.workspace_size(p32, "chunk_causal")
+    assert G.workspace_size(p32, "chunk_causal") - G.workspace_size(p32, "fwd") >= 1 * 300 * 2 * 64 * 2
     assert G.workspace_size(p32, "chunk_causal") < G.workspace_size(p32, "bidir")
 
 
