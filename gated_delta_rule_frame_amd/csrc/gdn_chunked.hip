@@ -999,6 +999,21 @@ struct ChainLay {
   static_assert(BYTES <= 160 * 1024, "workgroup LDS budget exceeded");
 };
 
+// CS: the chain of one head and scan runs as NH = 2 workgroups, each with the
+// state columns of NW strips (a wavefront per strip, one per SIMD): every
+// workgroup stages the whole map P_p, and a wavefront no longer shares its
+// SIMD's matrix core with another strip; a strip index past the state (D =
+// 112: 7 strips, 2 x 4 wavefronts) computes on zeros and stores nothing.
+// Faster per step (the whole chain, latency-bound: 0.40 -> 0.32 ms at the 60 s
+// clip) but less work per CU, so the split chain's many-workgroup launches,
+// bound by the GPU's capacity, keep one workgroup of MD wavefronts.
+template <int D, bool CS>
+struct ChainSplitCols {
+  static constexpr int MD = D / 16;
+  static constexpr int NH = CS && MD >= 2 ? 2 : 1;
+  static constexpr int NW = (MD + NH - 1) / NH;
+};
+
 typedef __attribute__((address_space(3))) const volatile s16x4_t lds_s16x4_t;
 __device__ __forceinline__ bf16x8_t fragB2(const bh* arow, int q, int g) {
   const s16x4_t x = *(lds_s16x4_t*)(arow + 16 * q + 4 * g);
@@ -1030,18 +1045,23 @@ __device__ __forceinline__ void split4(f32x4 v, s16x4_t& hi, s16x4_t& lo) {
 //      storing every start state (the last group also the final one).
 // Serial steps: 2m + G instead of NS-1 (m ~ sqrt((NS-1)/2)), at the cost of
 // reading every map twice.
-template <int D, bool PT>
-__global__ __launch_bounds__(64 * (D / 16)) void seg_chain_kernel(Args a) {
+template <int D, bool PT, bool CS>
+__global__ __launch_bounds__((64 * ChainSplitCols<D, CS>::NW)) void seg_chain_kernel(Args a) {
   using C = ChainLay<D>;
-  constexpr int MD = C::MD, NP = C::NP, LDC = C::LDC, NX = 2 * D, NTH = 64 * MD;
+  using SC = ChainSplitCols<D, CS>;
+  constexpr int MD = C::MD, NP = C::NP, LDC = C::LDC, NX = 2 * D, NTH = 64 * SC::NW;
+  constexpr int NPI = (D * D / 4 + NTH - 1) / NTH;   // float4 pieces of P per thread
   __shared__ __attribute__((aligned(16))) char smem[C::BYTES];
   const int wave = wave_id(), lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
   const int bh_ = blockIdx.x, b = bh_ / a.H, h = bh_ % a.H;
-  const int slot = a.slot0 + (int)blockIdx.y, dir = dir_of_slot(a.dirs, slot);
+  const int cgrp = (int)blockIdx.y % SC::NH;                     // column group of this workgroup
+  const int slot = a.slot0 + (int)blockIdx.y / SC::NH, dir = dir_of_slot(a.dirs, slot);
   const int mode = a.ch_mode;
   const int grp = mode == 1 ? (int)blockIdx.z >> 1 : (int)blockIdx.z;
   const bool pmul_only = mode == 1 && (blockIdx.z & 1) == 0;   // compose P: seed I, no Q
-  const int col = 16 * wave + cl;
+  const int strip = wave + SC::NW * cgrp;
+  const bool act = strip < MD;                                   // wave-uniform
+  const int col = 16 * (act ? strip : 0) + cl;
   const uint32_t so = (uint32_t)((4 * g * D + col) * 4);        // lane offset within a [D][D] state
   const uint32_t xq = (uint32_t)((col * NX + D + 4 * g) * 4);   // lane offset of Q^T within a [D][2D] map
   const uint32_t tso = (uint32_t)((col * D + 4 * g) * 4);       // lane offset within a transposed state
@@ -1067,32 +1087,34 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_chain_kernel(Args a) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) H[md][rr] = (pmul_only && 16 * md + 4 * g + rr == col) ? 1.f : 0.f;
   } else if (mode == 3) {
-    const __amdgpu_buffer_rsrc_t r = block_rsrc(a.gstarts + (hs * a.ch_groups + grp) * (size_t)D * D, D * D * 4);
+    const __amdgpu_buffer_rsrc_t r = block_rsrc(a.gstarts + (hs * a.ch_groups + grp) * (size_t)D * D, act ? D * D * 4 : 0);
 #pragma unroll
     for (int md = 0; md < MD; ++md) H[md] = tile_load_t(r, tso, (uint32_t)(md * 16 * 4));
   } else {
     const float* seed = (dir == 0 || a.dirs == 2) ? a.h0 : nullptr;
-    const __amdgpu_buffer_rsrc_t r = block_rsrc(seed ? seed + ((size_t)b * a.H + h) * D * D : a.starts, seed ? D * D * 4 : 0);
+    const __amdgpu_buffer_rsrc_t r =
+        block_rsrc(seed ? seed + ((size_t)b * a.H + h) * D * D : a.starts, seed && act ? D * D * 4 : 0);
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) H[md][rr] = block_load(r, so, (uint32_t)((16 * md + rr) * D * 4));
   }
   // start states are stored in modes 0 and 3 (segment starts) and 2 (group starts)
-  const bool store_starts = mode != 1;
+  const bool store_starts = mode != 1 && act;
   const __amdgpu_buffer_rsrc_t st =
       block_rsrc(starts, store_starts ? (uint32_t)(mode == 2 ? a.ch_groups : a.NS) * D * D * 4 : 0);
 
   // Maps in flight, one step ahead: P (float4 number threadIdx.x + NTH i) and
   // Q (this lane's accumulator-layout tiles).
-  typedef float4 PRegs[MD];
+  typedef float4 PRegs[NPI];
   // Thread element f = threadIdx.x + NTH i holds row `row`, columns 4 c4 ..
   // 4 c4 + 3 of the staged P; transposed, those are one column of four rows
   // of the stored map (dword loads, coalesced along the column index).
   auto fetch_p = [&](int p, PRegs& r) {
     const __amdgpu_buffer_rsrc_t m = block_rsrc(pmaps + (size_t)(ptr ? a.NS - 1 - p : p) * D * NX, D * NX * 4);
+    // pieces past the map (f >= D * D / 4) address past it: zeros
 #pragma unroll
-    for (int i = 0; i < MD; ++i) {
+    for (int i = 0; i < NPI; ++i) {
       const int f = threadIdx.x + NTH * i;
       if constexpr (ptr) {
         const int row = f % D, c4 = f / D;
@@ -1109,7 +1131,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_chain_kernel(Args a) {
   };
   // Q of map p; compose-P reads none (an empty range: zeros)
   auto fetch_q = [&](int p, f32x4 (&q)[MD]) {
-    const __amdgpu_buffer_rsrc_t m = block_rsrc(maps + (size_t)p * D * NX, pmul_only ? 0 : D * NX * 4);
+    const __amdgpu_buffer_rsrc_t m = block_rsrc(maps + (size_t)p * D * NX, pmul_only || !act ? 0 : D * NX * 4);
 #pragma unroll
     for (int md = 0; md < MD; ++md) q[md] = tile_load_t(m, xq, (uint32_t)(16 * md * 4));
   };
@@ -1117,13 +1139,15 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_chain_kernel(Args a) {
     bh* phi = reinterpret_cast<bh*>(smem + buf * 2 * C::MAT);
     bh* plo = phi + C::MAT / 2;
 #pragma unroll
-    for (int i = 0; i < MD; ++i) {
+    for (int i = 0; i < NPI; ++i) {
       const int f = threadIdx.x + NTH * i;
       const int row = ptr ? f % D : f / (D / 4), c4 = ptr ? f / D : f % (D / 4);
       s16x4_t hi, lo;
       split4(f32x4{r[i].x, r[i].y, r[i].z, r[i].w}, hi, lo);
-      *reinterpret_cast<s16x4_t*>(phi + row * LDC + 4 * c4) = hi;
-      *reinterpret_cast<s16x4_t*>(plo + row * LDC + 4 * c4) = lo;
+      if (NPI * NTH == D * D / 4 || f < D * D / 4) {
+        *reinterpret_cast<s16x4_t*>(phi + row * LDC + 4 * c4) = hi;
+        *reinterpret_cast<s16x4_t*>(plo + row * LDC + 4 * c4) = lo;
+      }
     }
   };
 
@@ -1201,7 +1225,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_chain_kernel(Args a) {
   for (int p = p0; p < p1; ++p) step(p);
   if (mode == 1) {
     // the group's map: P_g row-major, Q_g transposed
-    const __amdgpu_buffer_rsrc_t xr = block_rsrc(a.gmaps + (hs * a.ch_groups + grp) * (size_t)D * NX, D * NX * 4);
+    const __amdgpu_buffer_rsrc_t xr = block_rsrc(a.gmaps + (hs * a.ch_groups + grp) * (size_t)D * NX, act ? D * NX * 4 : 0);
     if (pmul_only) {
       const uint32_t xo = (uint32_t)((4 * g * NX + col) * 4);
 #pragma unroll
@@ -1762,10 +1786,21 @@ hipError_t chain_launch(Args a, const ChainWs& cw, unsigned bhc, unsigned nsl, b
   if (!split) a.ch_m = a.ch_groups = 0;
   auto go = [&](int mode, unsigned gz, bool ptv) -> hipError_t {
     a.ch_mode = mode;
-    if (ptv)
-      hipLaunchKernelGGL((seg_chain_kernel<D, true>), dim3(bhc, nsl, gz), dim3(64 * (D / 16)), 0, st, a);
-    else
-      hipLaunchKernelGGL((seg_chain_kernel<D, false>), dim3(bhc, nsl, gz), dim3(64 * (D / 16)), 0, st, a);
+    if (mode == 0) {   // the whole chain: two column-group workgroups per head
+      using SC = ChainSplitCols<D, true>;
+      const dim3 grid(bhc, nsl * SC::NH, gz), block(64 * SC::NW);
+      if (ptv)
+        hipLaunchKernelGGL((seg_chain_kernel<D, true, true>), grid, block, 0, st, a);
+      else
+        hipLaunchKernelGGL((seg_chain_kernel<D, false, true>), grid, block, 0, st, a);
+    } else {
+      using SC = ChainSplitCols<D, false>;
+      const dim3 grid(bhc, nsl * SC::NH, gz), block(64 * SC::NW);
+      if (ptv)
+        hipLaunchKernelGGL((seg_chain_kernel<D, true, false>), grid, block, 0, st, a);
+      else
+        hipLaunchKernelGGL((seg_chain_kernel<D, false, false>), grid, block, 0, st, a);
+    }
     return hipGetLastError();
   };
   if (a.ch_m == 0) return go(0, 1, pt);
