@@ -57,11 +57,13 @@ def subchunk_sizes(T, L, c=64):
     return segs
 
 
-def out_flops(n, d):
+def out_flops(n, d, inverse=True):
     """Algorithmic flops of the output pass on one sub-chunk of n tokens:
-    strict-lower K K^T, causal Q K^T, the triangular inverse (n^3/3), K H and
-    Q H, Tm diag(beta) R and P V' (triangular), and the state update."""
-    return n * (n - 1) * d + 3 * n * (n + 1) * d + 6 * n * d * d + n ** 3 // 3
+    causal Q K^T, K H and Q H, Tm diag(beta) R and P V' (triangular), the
+    state update, and (inverse: unless it loads the map kernel's) the
+    strict-lower K K^T and the triangular inverse (n^3/3)."""
+    tri = n * (n - 1) * d + n ** 3 // 3 if inverse else 0
+    return tri + 3 * n * (n + 1) * d + 6 * n * d * d
 
 
 def map_flops(n, d, q_only=False):
@@ -72,15 +74,18 @@ def map_flops(n, d, q_only=False):
     return n * (n - 1) * d + w * n * (n + 1) * d + 4 * w * n * d * d + n ** 3 // 3
 
 
-def executed_flops(T, L, d, bh, ndir):
+def executed_flops(T, L, d, bh, ndir, reuse=True):
     """Algorithmic flops per call of each of the chunked path's kernels, summed
     over its launches (a bidirectional call launches each kernel once per scan
-    direction)."""
+    direction).  reuse: the output kernel of a forward- or backward-only call
+    loads the map kernel's sub-chunk inverses (the library default; with more
+    than one segment), and the map kernel then covers every segment."""
     segs = subchunk_sizes(T, L)
-    per_out = sum(out_flops(n, d) for seg in segs for n in seg)
+    reuse = reuse and len(segs) > 1 and ndir == 1
+    per_out = sum(out_flops(n, d, inverse=not reuse) for seg in segs for n in seg)
     if ndir == 1:
-        # maps of every segment but the last of the scan
-        maps = sum(map_flops(n, d) for seg in segs[:-1] for n in seg)
+        # maps of every segment but the last of the scan (all with reuse)
+        maps = sum(map_flops(n, d) for seg in (segs if reuse else segs[:-1]) for n in seg)
     else:
         # forward maps of every segment (the last one's P, transposed, is the
         # reversed scan's first), reversed maps (Q only) of all but the first
@@ -95,8 +100,8 @@ def chunk_causal_flops(T, S, L, d, bh, first, every):
     """Per-call flops of the chunk-causal layer on the chunked path: the
     forward scan's maps, chain and outputs, and the reversed scan's outputs
     over each chunk of frames (its segments are the chunks: no maps, no
-    chain)."""
-    fl = executed_flops(T, L, d, bh, 1)
+    chain, so they always form their inverses)."""
+    fl = executed_flops(T, L, d, bh, 1, reuse=False)   # two-scan calls form their inverses
     bounds, t0, n = [], 0, first * S
     while t0 < T:
         bounds.append((t0, min(T, t0 + n)))
@@ -186,6 +191,9 @@ def main():
     ap.add_argument("--prologue", default="none", choices=["none", "features"],
                     help="features: raw (unnormalised) q/k through the fused key-feature and query "
                          "normalisation prologue, with the spatial key scale 1/sqrt(d_k * tokens per frame)")
+    ap.add_argument("--inverse-reuse", default="on", choices=["on", "off"],
+                    help="on: the output kernel of a forward- or backward-only call loads the "
+                         "segment-map kernel's sub-chunk inverses (identical results); off: it forms them again")
     ap.add_argument("--no-parity", action="store_true", help="skip the oracle check and CPU baseline")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after timing, run one device-to-device copy of this many bytes (counter calibration)")
@@ -208,6 +216,7 @@ def main():
     direction = args.direction or ("bidir" if w.mode == "bidir" else "fwd")
     dev = torch.device("cuda:0")
     G.set_segment_tokens(args.segment)
+    G.set_inverse_reuse(args.inverse_reuse == "on")
 
     x = make_inputs(w, args.seed)
     qkv_dt = torch.bfloat16 if w.qkv_dtype == "bf16" else torch.float32
@@ -221,7 +230,9 @@ def main():
     first_cf, every_cf = (int(c) for c in args.chunks.split(","))
     cc = direction == "chunk_causal"
     # name of the committed counter summaries for this configuration
-    tag = w.name + ("_jacobi" if jac else "") + ("_features" if pro else "") + ("_chunk_causal" if cc else "")
+    tag = w.name + ("_" + direction if direction in ("fwd", "bwd") else "") + ("_jacobi" if jac else "") + \
+        ("_features" if pro else "") + ("_chunk_causal" if cc else "") + \
+        ("" if args.inverse_reuse == "on" or jac or direction in ("bidir", "chunk_causal") else "_inverse_formed")
     prob = G.make_problem(B, H, dk, dv, w.frames, w.tokens_per_frame, G.BF16 if w.qkv_dtype == "bf16" else G.F32,
                           G.F32, "auto", key_scale, args.intra, first_cf, every_cf, args.prologue)
     ws = torch.empty(max(G.workspace_size(prob, direction), 16), dtype=torch.uint8, device=dev)
@@ -330,8 +341,9 @@ def main():
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS, "traffic": read_traffic(dom, tag), "kernel": dom}
     elif "seg_out_kernel" in kern and L:
+        reuse = args.inverse_reuse == "on"
         fl = (chunk_causal_flops(T, w.tokens_per_frame, L, dk, B * H, first_cf, every_cf) if cc
-              else executed_flops(T, L, dk, B * H, ndir))
+              else executed_flops(T, L, dk, B * H, ndir, reuse))
         flops_exec = sum(fl.values())   # per call
         per_launch = {}
         for k in fl:
@@ -373,6 +385,7 @@ def main():
             "segment_tokens": None if jac else L, "seed": args.seed,
             "intra": args.intra, "key_scale": key_scale, "prologue": args.prologue,
             "chunks_frames": [first_cf, every_cf] if cc else None,
+            "inverse_reuse": None if jac or direction in ("bidir", "chunk_causal") else args.inverse_reuse == "on",
         },
         "layer": {"canonical_gflop": canon / 1e9, "executed_gflop": (flops_exec or 0) / 1e9,
                   "credited_tflops": layer_tflops, "pct_peak": 100 * layer_tflops / PEAK_TFLOPS,

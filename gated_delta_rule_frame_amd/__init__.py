@@ -15,7 +15,7 @@ import ctypes
 import os
 
 __all__ = ["forward", "step", "workspace_size", "make_problem", "lib", "GdnError",
-           "set_segment_tokens", "set_concurrent_scans", "segment_plan", "profile_enable", "profile_reset", "profile_read",
+           "set_segment_tokens", "set_concurrent_scans", "set_chain_group", "set_inverse_reuse", "segment_plan", "profile_enable", "profile_reset", "profile_read",
            "FORWARD", "BACKWARD", "BIDIRECTIONAL", "ABI_VERSION", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
@@ -77,6 +77,8 @@ def lib():
         L.gdn_set_concurrent_scans.argtypes = [i32]
         L.gdn_set_chain_group.restype = None
         L.gdn_set_chain_group.argtypes = [i32]
+        L.gdn_set_inverse_reuse.restype = None
+        L.gdn_set_inverse_reuse.argtypes = [i32]
         L.gdn_profile_enable.restype = i32
         L.gdn_profile_enable.argtypes = [i32]
         L.gdn_profile_reset.restype = i32
@@ -162,6 +164,12 @@ def set_concurrent_scans(on: bool) -> None:
     """Let bidirectional calls overlap the two scans on a second stream (default
     on); see gdn.h."""
     lib().gdn_set_concurrent_scans(1 if on else 0)
+
+
+def set_inverse_reuse(on: bool) -> None:
+    """Let the output kernels load the segment-map kernels' sub-chunk inverses
+    instead of forming them again (default on; identical results); see gdn.h."""
+    lib().gdn_set_inverse_reuse(1 if on else 0)
 
 
 def segment_plan(problem: Problem, direction=BIDIRECTIONAL) -> int:

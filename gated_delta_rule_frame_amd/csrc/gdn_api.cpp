@@ -160,6 +160,8 @@ void gdn_set_chain_group(int32_t maps) { gdn::set_chain_group(maps); }
 
 void gdn_set_concurrent_scans(int32_t on) { gdn::set_concurrent_scans(on != 0); }
 
+void gdn_set_inverse_reuse(int32_t on) { gdn::set_inverse_reuse(on != 0); }
+
 gdn_status gdn_plan_segment_tokens(const gdn_problem* pr, int32_t direction, int32_t* tokens_out) {
   try {
     if (!tokens_out) return fail(GDN_ERR_INVALID_ARGUMENT, "tokens_out is NULL");

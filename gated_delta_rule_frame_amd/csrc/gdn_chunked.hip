@@ -103,6 +103,7 @@ ChainWs chain_ws(int nsteps, size_t heads_dirs, int dk, int dv) {
   return c;
 }
 std::atomic<bool> g_concurrent_scans{true};
+std::atomic<bool> g_tm_reuse{true};
 
 struct Args {
   const bh* q;
@@ -133,6 +134,9 @@ struct Args {
   int ch_m, ch_groups;  // ... maps per group, groups
   float* gmaps;         // ... composed group maps [ndir][B][H][groups][DK][DK+DV]
   float* gstarts;       // ... group start states [ndir][B][H][groups][DK][DV] (transposed)
+  hb* tm;               // Tm diag(beta) of every sub-chunk, [ndir][B][H][U][10][16][16] (U = ceil(T / 64),
+                        // the 10 lower 16x16 blocks), stored by the map kernels and read by the output
+                        // kernels; null: the map kernels store nothing
 };
 
 // Wavefront index as a wave-uniform (scalar) value, so that branches on it are
@@ -713,6 +717,98 @@ __device__ void tinv_offdiag(const Inv& I, const Buf& B) {
   (void)tinv_block(I, B, 3, 0, cat8(d[0], t10), true, cat8(t20, z), cl, g);
 }
 
+// --- reuse of the inverse ----------------------------------------------------------
+// The map kernels store every sub-chunk's Tm diag(beta) and the output kernels
+// of the same scan load it instead of forming and inverting I + A again: the
+// same sub-chunks, rows and arithmetic, so the blocks are bit-identical.  Per
+// sub-chunk the 10 lower 16x16 blocks (the upper ones are zero) as 320 pieces
+// of 16 bytes: piece k is half k % 2 of row (k / 2) % 16 of block k / 32, the
+// blocks in the order (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) .. (3,3).
+constexpr int kTmPieces = 320;
+constexpr int kTmElems = kTmPieces * 8;   // fp16 elements per sub-chunk
+constexpr int kTmRowBlk[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+constexpr int kTmColBlk[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+constexpr uint32_t kPackTr = pack_pairs(kTmRowBlk), kPackTc = pack_pairs(kTmColBlk);
+
+// Element offset of piece k in a Tm rows buffer (B.tt).
+__device__ __forceinline__ int tm_piece_lds(int k) {
+  const int blk = k >> 5, r = (k >> 1) & 15, half = k & 1;
+  const int bi = (kPackTr >> (2 * blk)) & 3, bj = (kPackTc >> (2 * blk)) & 3;
+  return (16 * bi + r) * LDT + 16 * bj + 8 * half;
+}
+
+// The Tm blocks of sub-chunk sb of scan slot `slot` (empty for n = 0, or
+// without a Tm buffer).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tm_rsrc(const Args& a, int slot, int b, int h, const Sub& sb) {
+  const long long U = (a.T + CH - 1) / CH;
+  const hb* p = a.tm + ((((long long)slot * a.B + b) * a.H + h) * U + sb.t0 / CH) * kTmElems;
+  return rows_rsrc(p, a.tm != nullptr && sb.n > 0 ? kTmElems * 2 : 0);
+}
+
+// Map kernels (strip waves): store the Tm blocks of buffer B.  Every lane
+// issues the same stores; pieces past 320 read a valid LDS address and fall
+// outside the buffer.
+template <int D>
+__device__ __forceinline__ void store_tm(__amdgpu_buffer_rsrc_t r, const Buf& B) {
+  constexpr int NTS = 64 * Geo<D>::NSW, NI = (kTmPieces + NTS - 1) / NTS;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int k = (int)threadIdx.x + NTS * i;
+    const uint4 x = *reinterpret_cast<const uint4*>(B.tt + tm_piece_lds(k < kTmPieces ? k : kTmPieces - 1));
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{x.x, x.y, x.z, x.w}, r, (uint32_t)(16 * k), 0, 0);
+  }
+}
+
+// Output kernels (helper wave): five pieces per lane.
+struct StageTm {
+  uint4 x[5];
+};
+__device__ __forceinline__ void fetch_tm(__amdgpu_buffer_rsrc_t r, StageTm& st) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)(16 * (lane + 64 * i)), 0, 0);
+    st.x[i] = make_uint4(v[0], v[1], v[2], v[3]);
+  }
+}
+__device__ __forceinline__ void stage_tm(const Buf& B, const StageTm& st) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) *reinterpret_cast<uint4*>(B.tt + tm_piece_lds(lane + 64 * i)) = st.x[i];
+}
+
+// P tiles t0, t0 + dt, .. (below 10) of sub-chunk B: P = c tril(Q K^T) * E,
+// products first, then epilogues.
+template <int D, int NK>
+__device__ __forceinline__ void gram_p_tiles(const Args& a, const Buf& B, int t0, int dt) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
+  f32x4 sk[NK];
+#pragma unroll
+  for (int k = 0; k < NK; ++k) {
+    const int u = t0 + k * dt;
+    if (u < 10) {
+      const int ta = (kPackA >> (2 * u)) & 3, tb = (kPackB >> (2 * u)) & 3;
+      sk[k] = gram_tile<D>(B.kr, B.qr, ta, tb, cl, g);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < NK; ++k) {
+    const int u = t0 + k * dt;
+    if (u >= 10) continue;
+    const int ta = (kPackA >> (2 * u)) & 3, tb = (kPackB >> (2 * u)) & 3;
+    const f32x4 s = sk[k];
+    const int x = 16 * tb + cl, y0 = 16 * ta + 4 * g;
+    const float gx = B.g2[x], cc = a.c;
+    const f32x4 gy = ld4f(B.g2 + y0);
+    store4_h(B.pp + x * LDT + y0, (x >= y0 + 0) ? cc * s[0] * ex2(gx - gy[0]) : 0.f,
+             (x >= y0 + 1) ? cc * s[1] * ex2(gx - gy[1]) : 0.f, (x >= y0 + 2) ? cc * s[2] * ex2(gx - gy[2]) : 0.f,
+             (x >= y0 + 3) ? cc * s[3] * ex2(gx - gy[3]) : 0.f);
+  }
+}
+// With the inverse loaded, the helper forms the last kHelperP(NSW) P tiles and
+// the strip waves one each of the rest.
+constexpr int kHelperP(int nsw) { return 10 - nsw > 3 ? 10 - nsw : 3; }
+
 // --- strip-wave products ----------------------------------------------------------
 // State strip: X[md] (md = 0 .. MD-1), the 16x16 accumulator tiles of rows
 // 16 md .. 16 md + 15 of the wave's 16 state columns, fp32.
@@ -949,6 +1045,7 @@ __device__ __forceinline__ void seg_map_body(Args a) {
       }
       state_update<D, SPW>(Bc.kr, Vs, Bc.eg[CH - 1], cl, g, X);
     }
+    store_tm<D>(tm_rsrc(a, slot, b, h, piece(c)), Bc);
     if (c + 1 < nsub) gram_stage_strips<D, false>(a, Bn, I);
     __syncthreads();
   }
@@ -1251,11 +1348,14 @@ __global__ __launch_bounds__((64 * ChainSplitCols<D, CS>::NW)) void seg_chain_ke
 // partial before the single final store (bidirectional: the forward launch
 // stores, the reversed one adds; chunk-causal: the other way round).  Strip
 // wave w owns state columns 16 w .. 16 w + 15.
-template <int D, bool PRO, int ST>
+template <int D, bool PRO, int ST, bool TML>
 __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
   using G = Geo<D>;
   using L = Lay<D, true>;
   constexpr int MD = G::MD, SPW = 1;
+  // TML: the Tm blocks come from the map kernel of this scan; the helper
+  // stages them and forms most of the P tiles instead of inverting I + A.
+  constexpr int HP = kHelperP(G::NSW), SP = 10 - HP;   // P tiles of the helper, of the strips
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
   const int wave = wave_id(), lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
   const int seg = blockIdx.x;
@@ -1302,10 +1402,12 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
     StageKQ sk;
     StageV sv;
     StageG sg;
+    StageTm stm;
     {
       const Sub s0b = piece(0), s1b = piece(1);
       if (helper) {
         fetch_gates(a, b, h, s0b, sg);
+        if constexpr (TML) fetch_tm(tm_rsrc(a, slot, b, h, s0b), stm);
       } else {
         fetch_kq<D, true, PRO>(a, b, h, s0b, sk);
         fetch_v<D>(a, b, h, s0b, sv);
@@ -1314,6 +1416,10 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
       if (helper) {
         stage_gates(buf_at<D, true>(smem, 0), sg, a.c);
         fetch_gates(a, b, h, s1b, sg);
+        if constexpr (TML) {
+          stage_tm(buf_at<D, true>(smem, 0), stm);
+          fetch_tm(tm_rsrc(a, slot, b, h, s1b), stm);
+        }
       } else {
         stage_kq<D, true, PRO>(buf_at<D, true>(smem, 0), sk);
         stage_v<D>(buf_at<D, true>(smem, 0), sv);
@@ -1321,20 +1427,35 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
         fetch_v<D>(a, b, h, s1b, sv);
       }
       __syncthreads();
-      if (helper) gram_stage_helper<D>(a, buf_at<D, true>(smem, 0), I);
-      else gram_stage_strips<D, true>(a, buf_at<D, true>(smem, 0), I);
+      if constexpr (TML) {
+        if (helper) gram_p_tiles<D, HP>(a, buf_at<D, true>(smem, 0), SP, 1);
+        else gram_p_tiles<D, 1>(a, buf_at<D, true>(smem, 0), wave < SP ? wave : 10, 0);
+      } else {
+        if (helper) gram_stage_helper<D>(a, buf_at<D, true>(smem, 0), I);
+        else gram_stage_strips<D, true>(a, buf_at<D, true>(smem, 0), I);
+      }
       __syncthreads();
     }
     if (helper) {
-      // helper: gate factors of c+1, inverse of c, diagonal A blocks of c+1
+      // helper: gate factors of c+1, and either the inverse of c and the
+      // diagonal A blocks of c+1, or (TML) c+1's Tm blocks and P tiles
       for (int c = 0; c < nsub; ++c) {
         const Buf Bc = buf_at<D, true>(smem, c & 1), Bn = buf_at<D, true>(smem, (c + 1) & 1);
-      const Inv I = inv_at<D, true>(smem);
+        const Inv I = inv_at<D, true>(smem);
         stage_gates(Bn, sg, a.c);
         fetch_gates(a, b, h, piece(c + 2), sg);
-        tinv_offdiag(I, Bc);
+        if constexpr (TML) {
+          stage_tm(Bn, stm);
+          fetch_tm(tm_rsrc(a, slot, b, h, piece(c + 2)), stm);
+        } else {
+          tinv_offdiag(I, Bc);
+        }
         __syncthreads();
-        if (c + 1 < nsub) gram_stage_helper<D>(a, Bn, I);
+        if constexpr (TML) {
+          if (c + 1 < nsub) gram_p_tiles<D, HP>(a, Bn, SP, 1);
+        } else {
+          if (c + 1 < nsub) gram_stage_helper<D>(a, Bn, I);
+        }
         __syncthreads();
       }
       return;
@@ -1458,7 +1579,11 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
         Vs[0][1] = tof16x8(Vn[0][2] * d2, Vn[0][3] * d3);
         state_update<D, SPW>(Bc.kr, Vs, Bc.eg[CH - 1], cl, g, H);
       }
-      if (c + 1 < nsub) gram_stage_strips<D, true>(a, Bn, I);
+      if constexpr (TML) {
+        if (c + 1 < nsub) gram_p_tiles<D, 1>(a, Bn, wave < SP ? wave : 10, 0);
+      } else {
+        if (c + 1 < nsub) gram_stage_strips<D, true>(a, Bn, I);
+      }
       __syncthreads();
     }
     if (nsub > 0) flush(nsub - 1);
@@ -1734,7 +1859,7 @@ struct Plan {
   int L, NS, ndir, dirs;
   bool cc;       // chunk-causal: forward maps and chain only; the reversed scan runs per chunk
   ChainWs cw;    // split of the chain
-  size_t maps_off, starts_off, acc_off, fac_off, gmaps_off, gstarts_off, bytes;
+  size_t maps_off, starts_off, acc_off, fac_off, gmaps_off, gstarts_off, tm_off, tm_bytes, bytes;
 };
 
 Plan make_plan(const Problem& p, int direction) {
@@ -1772,7 +1897,13 @@ Plan make_plan(const Problem& p, int direction) {
   if (pl.dirs != 3) pl.cw = chain_ws(pl.NS - 1, bhd, p.dk, p.dv);
   pl.gmaps_off = pl.fac_off + align_up(prologue_bytes(p), 256);
   pl.gstarts_off = pl.gmaps_off + pl.cw.gmaps_bytes;
-  pl.bytes = pl.gstarts_off + pl.cw.gstarts_bytes;
+  // Tm blocks of every sub-chunk of a forward- or backward-only call with
+  // maps (fp16, 5 KB per sub-chunk), whether or not their reuse is switched
+  // on (two-scan calls form them in both kernels: see launch_d)
+  const size_t U = (size_t)((p.T + CH - 1) / CH);
+  pl.tm_bytes = pl.NS >= 2 && pl.dirs != 3 && !pl.cc ? align_up(bhd * U * kTmElems * 2, 256) : 0;
+  pl.tm_off = pl.gstarts_off + pl.cw.gstarts_bytes;
+  pl.bytes = pl.tm_off + pl.tm_bytes;
   return pl;
 }
 
@@ -1870,6 +2001,12 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
   a.c = p.key_scale;
   a.gmaps = reinterpret_cast<float*>(ws + pl.gmaps_off);
   a.gstarts = reinterpret_cast<float*>(ws + pl.gstarts_off);
+  // Reuse of the map kernel's Tm blocks by the output kernel: forward- and
+  // backward-only calls (measured at the 60 s clip, output kernel alone:
+  // 0.613 -> 0.590 ms for a forward call; for the partial-storing and -adding
+  // launches of a bidirectional call 0.597 -> 0.612 ms, so two-scan calls
+  // form their own).
+  a.tm = pl.tm_bytes && g_tm_reuse.load(std::memory_order_relaxed) ? reinterpret_cast<hb*>(ws + pl.tm_off) : nullptr;
   const unsigned bhc = (unsigned)(p.B * p.H);
   const bool both = pl.dirs == 3;
   // Workgroups are dealt to the 8 XCDs (each with its own L2) in turn.  With
@@ -1877,9 +2014,11 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
   // heads lands on the same XCD, so the cache lines their rows share (a head's
   // slice of a token row is not line-aligned) are fetched from memory once.
   auto padded = [](int n) { return (unsigned)((n + 7) / 8 * 8); };
-  // Maps of the scan in `slot`: segments 0 .. NS-2 in scan order, and for the
-  // forward scan of a bidirectional call also the last one (its transpose is
-  // the reversed scan's first P); that reversed scan forms Q only.
+  // Maps of the scan in `slot`: segments 0 .. NS-2 in scan order, and also the
+  // last one for the forward scan of a bidirectional call (its transpose is
+  // the reversed scan's first P) and wherever the output kernels reuse the
+  // map kernels' Tm blocks; the reversed scan of a bidirectional call forms Q
+  // only.
   // In a bidirectional call the second map and output launches visit the heads
   // in reversed order, so that they start on the heads whose inputs (and
   // partial outputs) the first launch touched last, which the memory-side
@@ -1889,7 +2028,7 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
     a.slot0 = slot;
     a.heads_rev = both && slot == 1;
     prof_begin(st, GDN_KERNEL_SEG_MAP);
-    a.npos = both && slot == 0 ? pl.NS : pl.NS - 1;
+    a.npos = (both && slot == 0) || a.tm ? pl.NS : pl.NS - 1;
     if (both && slot == 1)
       hipLaunchKernelGGL((seg_map_q_kernel<D, PRO>), dim3(padded(a.npos), bhc, 1), dim3(Geo<D>::NT), 0, st, a);
     else
@@ -1916,13 +2055,24 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
     return hipSuccess;
   };
   // One output launch (x.mode and x.out_bf16 select the store type).
+  // x.tm: load the map kernel's Tm blocks.
   auto launch_out = [&](const Args& x, unsigned gx, hipStream_t st) {
-    if (x.mode == 1)
-      hipLaunchKernelGGL((seg_out_kernel<D, PRO, 2>), dim3(gx, bhc, 1), dim3(Geo<D>::NT), 0, st, x);
-    else if (x.out_bf16)
-      hipLaunchKernelGGL((seg_out_kernel<D, PRO, 1>), dim3(gx, bhc, 1), dim3(Geo<D>::NT), 0, st, x);
-    else
-      hipLaunchKernelGGL((seg_out_kernel<D, PRO, 0>), dim3(gx, bhc, 1), dim3(Geo<D>::NT), 0, st, x);
+    const dim3 grid(gx, bhc, 1), block(Geo<D>::NT);
+    if (x.tm) {
+      if (x.mode == 1)
+        hipLaunchKernelGGL((seg_out_kernel<D, PRO, 2, true>), grid, block, 0, st, x);
+      else if (x.out_bf16)
+        hipLaunchKernelGGL((seg_out_kernel<D, PRO, 1, true>), grid, block, 0, st, x);
+      else
+        hipLaunchKernelGGL((seg_out_kernel<D, PRO, 0, true>), grid, block, 0, st, x);
+    } else {
+      if (x.mode == 1)
+        hipLaunchKernelGGL((seg_out_kernel<D, PRO, 2, false>), grid, block, 0, st, x);
+      else if (x.out_bf16)
+        hipLaunchKernelGGL((seg_out_kernel<D, PRO, 1, false>), grid, block, 0, st, x);
+      else
+        hipLaunchKernelGGL((seg_out_kernel<D, PRO, 0, false>), grid, block, 0, st, x);
+    }
   };
   // Outputs of one scan direction; in a bidirectional call the forward scan
   // stores its partial and the reversed scan adds it.
@@ -1947,6 +2097,7 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
     const int nchunks = p.T <= cf ? 1 : 1 + (int)((p.T - cf + cl_ - 1) / cl_);
     auto rev_chunks = [&](hipStream_t st) -> hipError_t {
       Args r = a;
+      r.tm = nullptr;   // the chunks have no maps
       r.dir = 1;
       r.mode = 1;
       r.cs_first = cf;
@@ -2152,5 +2303,6 @@ hipError_t jacobi_launch(const Problem& p, int direction, const Tensors& t, void
 void set_segment_tokens(int tokens) { g_segment_override.store(tokens > 0 ? tokens : 0); }
 void set_chain_group(int maps) { g_chain_group.store(maps > 0 ? maps : 0); }
 void set_concurrent_scans(bool on) { g_concurrent_scans.store(on); }
+void set_inverse_reuse(bool on) { g_tm_reuse.store(on); }
 
 }  // namespace gdn

@@ -62,6 +62,7 @@ hipError_t prologue_launch(const Problem& p, const Tensors& t, float* fac, hipSt
 void set_segment_tokens(int tokens);
 void set_chain_group(int maps);
 void set_concurrent_scans(bool on);
+void set_inverse_reuse(bool on);
 int chunked_segment_tokens(const Problem& p, int direction);
 
 // Kernel timing hooks (gdn_profile.cpp): no-ops unless profiling is enabled.

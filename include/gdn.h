@@ -234,6 +234,18 @@ void gdn_set_chain_group(int32_t maps);
  * at a time.  Results are identical.  Process-wide; thread-safe. */
 void gdn_set_concurrent_scans(int32_t on);
 
+/* Tuning knob of the chunked path: 1 (default) lets the output kernel of a
+ * forward- or backward-only call load each sub-chunk's inverse Tm diag(beta)
+ * (the solve of the sub-chunk's triangular system, 5 KB of fp16 per sub-chunk
+ * and head in the workspace) as the scan's segment-map kernel formed it,
+ * instead of forming it again; 0 forms it in both.  Results are identical
+ * either way (the same arithmetic on the same rows); the map kernel then
+ * covers every segment.  Bidirectional and chunk-causal calls (whose output
+ * launches store or add a partial, where loading measured slower) and calls
+ * with a single segment always form it.  gdn_workspace_size() does not depend
+ * on it.  Process-wide; thread-safe. */
+void gdn_set_inverse_reuse(int32_t on);
+
 /* Tokens per segment the chunked path would use for (problem, direction), or
  * 0 when the call would take the token-recurrent path.  Host only. */
 gdn_status gdn_plan_segment_tokens(const gdn_problem* problem, int32_t direction, int32_t* tokens_out);

@@ -156,7 +156,8 @@ def test_chunk_causal_validation_and_workspace():
     p32 = prob(first_chunk_frames=2, chunk_frames=1, algo="chunked", out_dtype=G.F32)
     pbf = prob(first_chunk_frames=2, chunk_frames=1, algo="chunked", out_dtype=G.BF16)
     assert G.workspace_size(pbf, "chunk_causal") == G.workspace_size(p32, "chunk_causal")
-    assert G.workspace_size(p32, "chunk_causal") - G.workspace_size(p32, "fwd") >= 1 * 300 * 2 * 64 * 2
+    tm = 2 * ((300 + 63) // 64) * 5120   # the forward-only call's sub-chunk inverse blocks (5 segments)
+    assert G.workspace_size(p32, "chunk_causal") - (G.workspace_size(p32, "fwd") - tm) >= 1 * 300 * 2 * 64 * 2
     assert G.workspace_size(p32, "chunk_causal") < G.workspace_size(p32, "bidir")
 
 
@@ -201,3 +202,28 @@ def test_split_chain_workspace():
     groups = (steps + 3) // 4
     extra = 1 * 2 * groups * 64 * (128 + 64) * 4
     assert split - whole == pytest.approx(extra, abs=512)
+
+
+def test_inverse_reuse_workspace():
+    """A forward-only chunked call with more than one segment holds 5 KB of
+    fp16 inverse blocks per 64-token sub-chunk and head, whether or not their
+    reuse is switched on; a bidirectional call holds none."""
+    p = prob(frames=40, tokens_per_frame=100, algo="chunked")   # 4000 tokens: 63 sub-chunks
+    try:
+        G.set_chain_group(1)
+        G.set_segment_tokens(4096)      # one segment: no maps, no inverse blocks
+        one = G.workspace_size(p, "fwd")
+        one_bi = G.workspace_size(p, "bidir")
+        G.set_segment_tokens(512)       # 8 segments
+        on = G.workspace_size(p, "fwd")
+        on_bi = G.workspace_size(p, "bidir")
+        G.set_inverse_reuse(False)
+        assert G.workspace_size(p, "fwd") == on
+    finally:
+        G.set_inverse_reuse(True)
+        G.set_chain_group(0)
+        G.set_segment_tokens(0)
+    per_seg = 2 * 64 * (128 + 64) * 4           # one scan's map and start state, 2 heads
+    tm = 2 * 63 * 5120
+    assert on - one == pytest.approx(7 * per_seg + tm, abs=1024)
+    assert on_bi - one_bi == pytest.approx(2 * 7 * per_seg, abs=1024)

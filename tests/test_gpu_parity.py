@@ -163,6 +163,41 @@ def test_concurrent_scans_match_in_order_schedule():
     assert rel_err(b[0], ro) <= TOL["bf16"] and rel_err(b[1], rH) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("prologue", [False, True])
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+def test_inverse_reuse_is_bit_identical(direction, prologue):
+    """An output kernel that loads the segment-map kernel's sub-chunk
+    inverses gives bit-identical outputs and final states to forming them
+    again (the same rows and arithmetic): 1005 tokens in segments of 192 (6
+    segments, a ragged last sub-chunk), d = 112, with and without the feature
+    prologue; both agree with the oracle.  (Two-scan calls always form
+    them.)"""
+    w = WORKLOADS[1].resized(frames=5, tokens_per_frame=201, heads=2, qk_spread=1.0 if prologue else 0.0)
+    x = make_inputs(w, 22)
+    c = 112 ** -0.5 if prologue else 1.0
+
+    def run():
+        if prologue:
+            return run_pro(w, x, direction, c, algo="chunked")
+        return run_gpu(w, x, direction, "chunked")
+
+    G.set_segment_tokens(192)
+    try:
+        G.set_inverse_reuse(False)
+        a = run()
+        G.set_inverse_reuse(True)
+        b = run()
+    finally:
+        G.set_inverse_reuse(True)
+        G.set_segment_tokens(0)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    args = features(x) if prologue else list(oracle_args(x)[0])
+    ro, rH = O.forward(direction, *args, x["h0"], key_scale=c)
+    eo, eh = rel_err(b[0], ro), rel_err(b[1], rH)
+    print(f"[parity] inverse reuse {direction} prologue={prologue}: out {eo:.3e} state {eh:.3e}", flush=True)
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"], (eo, eh)
+
+
 # ---------------------------------------------------------------- every head width
 
 DIMS = [16, 32, 48, 80, 96]
