@@ -578,15 +578,20 @@ constexpr int kPairB[10] = {1, 2, 3, 2, 3, 3, 0, 1, 2, 3};
 constexpr uint32_t kPackA = pack_pairs(kPairA), kPackB = pack_pairs(kPairB);
 
 // Helper: the diagonal 16x16 blocks of A of sub-chunk B (fp32), then their
-// inverses.
+// inverses.  The four products are formed before any result is stored: a
+// load placed after an LDS store waits for it (the compiler cannot prove the
+// two apart), which would serialise the blocks.
 template <int D>
 __device__ void gram_stage_helper(const Args& a, const Buf& B, const Inv& I) {
   const int lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
   const float c2 = a.c * a.c;
   {
+    f32x4 sb[4];
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) sb[blk] = gram_tile<D>(B.kr, B.kr, blk, blk, cl, g);
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
-      const f32x4 s = gram_tile<D>(B.kr, B.kr, blk, blk, cl, g);
+      const f32x4 s = sb[blk];
       const int x = 16 * blk + cl, y0 = 16 * blk + 4 * g;
       const float gx = B.g2[x], bx = c2 * B.bt[x];
       const f32x4 gy = ld4f(B.g2 + y0);
@@ -605,47 +610,76 @@ __device__ void gram_stage_helper(const Args& a, const Buf& B, const Inv& I) {
 // Strip waves: the off-diagonal blocks of A (fp16) and, for the output pass,
 // P = c tril(Q K^T) * E.  Wave w takes tiles w, w + NSW, ...; the products of
 // all its tiles are formed before any epilogue, so that their LDS reads and
-// MFMAs overlap (the first NFULL tiles of every wave need no branch).
+// MFMAs overlap (the first NFULL tiles of every wave need no branch), and the
+// epilogues read their gate factors before their first store.  The output
+// kernel forms the products before it stages its outputs and runs the
+// epilogues after (a read placed after an LDS store waits for it).
 template <int D, bool OUT>
-__device__ void gram_stage_strips(const Args& a, const Buf& B, const Inv& I) {
-  using G = Geo<D>;
+struct GramStrips {
+  static constexpr int NTILE = OUT ? 16 : 6;
+  static constexpr int NK = (NTILE + Geo<D>::NSW - 1) / Geo<D>::NSW, NFULL = NTILE / Geo<D>::NSW;
+};
+template <int D, bool OUT>
+__device__ __forceinline__ void gram_strips_products(const Buf& B, f32x4 (&sk)[GramStrips<D, OUT>::NK]) {
+  using GS = GramStrips<D, OUT>;
   const int wave = wave_id(), lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
-  const float c2 = a.c * a.c;
-  constexpr int NTILE = OUT ? 16 : 6;
-  constexpr int NK = (NTILE + G::NSW - 1) / G::NSW, NFULL = NTILE / G::NSW;
-  f32x4 sk[NK];
 #pragma unroll
-  for (int k = 0; k < NK; ++k) {
-    const int t = wave + k * G::NSW;
-    if (k < NFULL || t < NTILE) {
+  for (int k = 0; k < GS::NK; ++k) {
+    const int t = wave + k * Geo<D>::NSW;
+    if (k < GS::NFULL || t < GS::NTILE) {
       const bool isp = t >= 6;
       const int u = isp ? t - 6 : t;
       const int ta = (kPackA >> (2 * u)) & 3, tb = (kPackB >> (2 * u)) & 3;
       sk[k] = gram_tile<D>(B.kr, isp ? B.qr : B.kr, ta, tb, cl, g);
     }
   }
+}
+template <int D, bool OUT>
+__device__ __forceinline__ void gram_strips_epilogues(const Args& a, const Buf& B, const Inv& I,
+                                                      const f32x4 (&sk)[GramStrips<D, OUT>::NK]) {
+  using GS = GramStrips<D, OUT>;
+  const int wave = wave_id(), lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
+  const float c2 = a.c * a.c;
+  float gx[GS::NK], bx[GS::NK];
+  f32x4 gy[GS::NK];
 #pragma unroll
-  for (int k = 0; k < NK; ++k) {
-    const int t = wave + k * G::NSW;
-    if (!(k < NFULL || t < NTILE)) continue;
+  for (int k = 0; k < GS::NK; ++k) {
+    const int t = wave + k * Geo<D>::NSW;
+    if (!(k < GS::NFULL || t < GS::NTILE)) continue;
+    const bool isp = t >= 6;
+    const int u = isp ? t - 6 : t;
+    const int ta = (kPackA >> (2 * u)) & 3, tb = (kPackB >> (2 * u)) & 3;
+    const int x = 16 * tb + cl, y0 = 16 * ta + 4 * g;
+    gx[k] = B.g2[x];
+    gy[k] = ld4f(B.g2 + y0);
+    bx[k] = isp ? a.c : c2 * B.bt[x];
+  }
+#pragma unroll
+  for (int k = 0; k < GS::NK; ++k) {
+    const int t = wave + k * Geo<D>::NSW;
+    if (!(k < GS::NFULL || t < GS::NTILE)) continue;
     const bool isp = t >= 6;
     const int u = isp ? t - 6 : t;
     const int ta = (kPackA >> (2 * u)) & 3, tb = (kPackB >> (2 * u)) & 3;
     const f32x4 s = sk[k];
     const int x = 16 * tb + cl, y0 = 16 * ta + 4 * g;
-    const float gx = B.g2[x];
-    const f32x4 gy = ld4f(B.g2 + y0);
+    const float f = bx[k], gxx = gx[k];
+    const f32x4 gyy = gy[k];
     if (!isp) {
-      const float bx = c2 * B.bt[x];
-      store4_h(I.ao + x * LDT + y0, bx * s[0] * ex2(gx - gy[0]), bx * s[1] * ex2(gx - gy[1]),
-               bx * s[2] * ex2(gx - gy[2]), bx * s[3] * ex2(gx - gy[3]));
+      store4_h(I.ao + x * LDT + y0, f * s[0] * ex2(gxx - gyy[0]), f * s[1] * ex2(gxx - gyy[1]),
+               f * s[2] * ex2(gxx - gyy[2]), f * s[3] * ex2(gxx - gyy[3]));
     } else {
-      const float cc = a.c;
-      store4_h(B.pp + x * LDT + y0, (x >= y0 + 0) ? cc * s[0] * ex2(gx - gy[0]) : 0.f,
-               (x >= y0 + 1) ? cc * s[1] * ex2(gx - gy[1]) : 0.f, (x >= y0 + 2) ? cc * s[2] * ex2(gx - gy[2]) : 0.f,
-               (x >= y0 + 3) ? cc * s[3] * ex2(gx - gy[3]) : 0.f);
+      store4_h(B.pp + x * LDT + y0, (x >= y0 + 0) ? f * s[0] * ex2(gxx - gyy[0]) : 0.f,
+               (x >= y0 + 1) ? f * s[1] * ex2(gxx - gyy[1]) : 0.f, (x >= y0 + 2) ? f * s[2] * ex2(gxx - gyy[2]) : 0.f,
+               (x >= y0 + 3) ? f * s[3] * ex2(gxx - gyy[3]) : 0.f);
     }
   }
+}
+template <int D, bool OUT>
+__device__ void gram_stage_strips(const Args& a, const Buf& B, const Inv& I) {
+  f32x4 sk[GramStrips<D, OUT>::NK];
+  gram_strips_products<D, OUT>(B, sk);
+  gram_strips_epilogues<D, OUT>(a, B, I, sk);
 }
 
 // --- triangular inverse (helper wavefront) ------------------------------------------
@@ -684,37 +718,53 @@ __device__ void tinv_diag(const Inv& I, const Buf& B) {
   }
 }
 
-__device__ __forceinline__ f16x4_t tinv_block(const Inv& I, const Buf& B, int i, int j, f16x8_t p0, bool two,
-                                              f16x8_t p1, int cl, int g) {
-  const hb* arow = I.ao + (16 * i + cl) * LDT + 16 * j;
-  f32x4 m = mfma32(fragA2(arow, 0, g), p0, zero4());
-  if (two) m = mfma32(fragA2(arow, 2, g), p1, m);
+// One off-diagonal block T_ij = -T_ii M, M = sum_k A_ik T_kj (the A row
+// fragments a0, a1 against the T column pairs p0, p1): returns -T_ij in
+// accumulator layout (fp16, for the next level) and (T_ii M)^T in tr (lane
+// holds [cl][4g + r]) for the store.
+__device__ __forceinline__ f16x4_t tinv_block(f16x8_t a0, f16x8_t p0, bool two, f16x8_t a1, f16x8_t p1,
+                                              f16x4_t tii, f32x4& tr) {
+  f32x4 m = mfma32(a0, p0, zero4());
+  if (two) m = mfma32(a1, p1, m);
   const f16x4_t mh = tof16(m);
-  const f16x4_t tii = ld4(I.td + (16 * i + cl) * LDD + 4 * g);
   const f32x4 tc = mfma16(tii, mh);          // T_ii M: lane holds [4g + r][cl]
-  const f32x4 tr = mfma16(mh, tii);          // (T_ii M)^T: lane holds [cl][4g + r]
-  const f32x4 bb = ld4f(B.bt + 16 * j + 4 * g);
-  store4_h(B.tt + (16 * i + cl) * LDT + 16 * j + 4 * g, -tr[0] * bb[0], -tr[1] * bb[1], -tr[2] * bb[2],
-           -tr[3] * bb[3]);
+  tr = mfma16(mh, tii);                      // (T_ii M)^T: lane holds [cl][4g + r]
   return tof16(-tc);
 }
 
+// Every LDS operand is read first and every result stored last, so that no
+// read waits behind a store (see gram_stage_helper).
 __device__ void tinv_offdiag(const Inv& I, const Buf& B) {
   const int lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
   // diagonal blocks 0..2 in accumulator layout (lane: rows 4g + r, column cl)
-  f16x4_t d[3];
+  f16x4_t d[3], tii[3];
+  f32x4 bb[3];
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) d[j][r] = __builtin_bit_cast(_Float16, I.td[(16 * j + 4 * g + r) * LDD + cl]);
+    tii[j] = ld4(I.td + (16 * (j + 1) + cl) * LDD + 4 * g);   // T_{j+1, j+1}, row-operand layout
+    bb[j] = ld4f(B.bt + 16 * j + 4 * g);
   }
+  auto arow = [&](int i, int j) { return I.ao + (16 * i + cl) * LDT + 16 * j; };
+  const f16x8_t a10 = fragA2(arow(1, 0), 0, g), a21 = fragA2(arow(2, 1), 0, g), a32 = fragA2(arow(3, 2), 0, g);
+  const f16x8_t a20 = fragA2(arow(2, 0), 0, g), a31 = fragA2(arow(3, 1), 0, g);
+  const f16x8_t a30 = fragA2(arow(3, 0), 0, g), a30b = fragA2(arow(3, 0), 2, g);
   const f16x4_t z = zero_h4();
-  const f16x4_t t10 = tinv_block(I, B, 1, 0, cat8(d[0], z), false, cat8(z, z), cl, g);
-  const f16x4_t t21 = tinv_block(I, B, 2, 1, cat8(d[1], z), false, cat8(z, z), cl, g);
-  (void)tinv_block(I, B, 3, 2, cat8(d[2], z), false, cat8(z, z), cl, g);
-  const f16x4_t t20 = tinv_block(I, B, 2, 0, cat8(d[0], t10), false, cat8(z, z), cl, g);
-  (void)tinv_block(I, B, 3, 1, cat8(d[1], t21), false, cat8(z, z), cl, g);
-  (void)tinv_block(I, B, 3, 0, cat8(d[0], t10), true, cat8(t20, z), cl, g);
+  const f16x8_t zz = cat8(z, z);
+  f32x4 tr[6];
+  const f16x4_t t10 = tinv_block(a10, cat8(d[0], z), false, zz, zz, tii[0], tr[0]);
+  const f16x4_t t21 = tinv_block(a21, cat8(d[1], z), false, zz, zz, tii[1], tr[1]);
+  (void)tinv_block(a32, cat8(d[2], z), false, zz, zz, tii[2], tr[2]);
+  const f16x4_t t20 = tinv_block(a20, cat8(d[0], t10), false, zz, zz, tii[1], tr[3]);
+  (void)tinv_block(a31, cat8(d[1], t21), false, zz, zz, tii[2], tr[4]);
+  (void)tinv_block(a30, cat8(d[0], t10), true, a30b, cat8(t20, z), tii[2], tr[5]);
+  // Tm diag(beta) blocks (i, j): rows 16 i + cl, columns 16 j + 4g ..
+  constexpr int bi[6] = {1, 2, 3, 2, 3, 3}, bj[6] = {0, 1, 2, 0, 1, 0};
+#pragma unroll
+  for (int k = 0; k < 6; ++k)
+    store4_h(B.tt + (16 * bi[k] + cl) * LDT + 16 * bj[k] + 4 * g, -tr[k][0] * bb[bj[k]][0],
+             -tr[k][1] * bb[bj[k]][1], -tr[k][2] * bb[bj[k]][2], -tr[k][3] * bb[bj[k]][3]);
 }
 
 // --- reuse of the inverse ----------------------------------------------------------
@@ -778,11 +828,10 @@ __device__ __forceinline__ void stage_tm(const Buf& B, const StageTm& st) {
 }
 
 // P tiles t0, t0 + dt, .. (below 10) of sub-chunk B: P = c tril(Q K^T) * E,
-// products first, then epilogues.
+// products first, then epilogues (gate factors read before the first store).
 template <int D, int NK>
-__device__ __forceinline__ void gram_p_tiles(const Args& a, const Buf& B, int t0, int dt) {
+__device__ __forceinline__ void gram_p_products(const Buf& B, int t0, int dt, f32x4 (&sk)[NK]) {
   const int lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
-  f32x4 sk[NK];
 #pragma unroll
   for (int k = 0; k < NK; ++k) {
     const int u = t0 + k * dt;
@@ -791,6 +840,20 @@ __device__ __forceinline__ void gram_p_tiles(const Args& a, const Buf& B, int t0
       sk[k] = gram_tile<D>(B.kr, B.qr, ta, tb, cl, g);
     }
   }
+}
+template <int NK>
+__device__ __forceinline__ void gram_p_epilogues(const Args& a, const Buf& B, int t0, int dt, const f32x4 (&sk)[NK]) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
+  float gx[NK];
+  f32x4 gy[NK];
+#pragma unroll
+  for (int k = 0; k < NK; ++k) {
+    const int u = t0 + k * dt;
+    if (u >= 10) continue;
+    const int ta = (kPackA >> (2 * u)) & 3, tb = (kPackB >> (2 * u)) & 3;
+    gx[k] = B.g2[16 * tb + cl];
+    gy[k] = ld4f(B.g2 + 16 * ta + 4 * g);
+  }
 #pragma unroll
   for (int k = 0; k < NK; ++k) {
     const int u = t0 + k * dt;
@@ -798,12 +861,18 @@ __device__ __forceinline__ void gram_p_tiles(const Args& a, const Buf& B, int t0
     const int ta = (kPackA >> (2 * u)) & 3, tb = (kPackB >> (2 * u)) & 3;
     const f32x4 s = sk[k];
     const int x = 16 * tb + cl, y0 = 16 * ta + 4 * g;
-    const float gx = B.g2[x], cc = a.c;
-    const f32x4 gy = ld4f(B.g2 + y0);
-    store4_h(B.pp + x * LDT + y0, (x >= y0 + 0) ? cc * s[0] * ex2(gx - gy[0]) : 0.f,
-             (x >= y0 + 1) ? cc * s[1] * ex2(gx - gy[1]) : 0.f, (x >= y0 + 2) ? cc * s[2] * ex2(gx - gy[2]) : 0.f,
-             (x >= y0 + 3) ? cc * s[3] * ex2(gx - gy[3]) : 0.f);
+    const float gxx = gx[k], cc = a.c;
+    const f32x4 gyy = gy[k];
+    store4_h(B.pp + x * LDT + y0, (x >= y0 + 0) ? cc * s[0] * ex2(gxx - gyy[0]) : 0.f,
+             (x >= y0 + 1) ? cc * s[1] * ex2(gxx - gyy[1]) : 0.f, (x >= y0 + 2) ? cc * s[2] * ex2(gxx - gyy[2]) : 0.f,
+             (x >= y0 + 3) ? cc * s[3] * ex2(gxx - gyy[3]) : 0.f);
   }
+}
+template <int D, int NK>
+__device__ __forceinline__ void gram_p_tiles(const Args& a, const Buf& B, int t0, int dt) {
+  f32x4 sk[NK];
+  gram_p_products<D, NK>(B, t0, dt, sk);
+  gram_p_epilogues<NK>(a, B, t0, dt, sk);
 }
 // With the inverse loaded, the helper forms the last kHelperP(NSW) P tiles and
 // the strip waves one each of the rest.
@@ -1568,21 +1637,32 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) O[mt] = Bc.eg[16 * mt + cl] * O[mt];
         tri_times_T(Bc.pp, Vh[0], cl, g, O);
-        // staging rows: row 16 mt + cl, columns 16 wave + 4 g ..
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          *reinterpret_cast<f32x4*>(I.os + (16 * mt + cl) * L::OSL + 16 * wave + 4 * g) = O[mt];
         f16x8_t Vs[SPW][2];
         const f32x4 d0 = ld4f(Bc.dn + 4 * g), d1 = ld4f(Bc.dn + 16 + 4 * g);
         const f32x4 d2 = ld4f(Bc.dn + 32 + 4 * g), d3 = ld4f(Bc.dn + 48 + 4 * g);
         Vs[0][0] = tof16x8(Vn[0][0] * d0, Vn[0][1] * d1);
         Vs[0][1] = tof16x8(Vn[0][2] * d2, Vn[0][3] * d3);
         state_update<D, SPW>(Bc.kr, Vs, Bc.eg[CH - 1], cl, g, H);
-      }
-      if constexpr (TML) {
-        if (c + 1 < nsub) gram_p_tiles<D, 1>(a, Bn, wave < SP ? wave : 10, 0);
-      } else {
-        if (c + 1 < nsub) gram_stage_strips<D, true>(a, Bn, I);
+        // The Gram products of c+1, then the output staging, then the Gram
+        // epilogues: every LDS read of the phase is placed before its first
+        // LDS store, which it would otherwise wait behind.
+        const bool more = c + 1 < nsub;
+        f32x4 skp[1];
+        f32x4 sks[GramStrips<D, true>::NK];
+        if constexpr (TML) {
+          if (more) gram_p_products<D, 1>(Bn, wave < SP ? wave : 10, 0, skp);
+        } else {
+          if (more) gram_strips_products<D, true>(Bn, sks);
+        }
+        // staging rows: row 16 mt + cl, columns 16 wave + 4 g ..
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          *reinterpret_cast<f32x4*>(I.os + (16 * mt + cl) * L::OSL + 16 * wave + 4 * g) = O[mt];
+        if constexpr (TML) {
+          if (more) gram_p_epilogues<1>(a, Bn, wave < SP ? wave : 10, 0, skp);
+        } else {
+          if (more) gram_strips_epilogues<D, true>(a, Bn, I, sks);
+        }
       }
       __syncthreads();
     }
