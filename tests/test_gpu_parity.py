@@ -140,14 +140,15 @@ def test_chunked_matches_recurrent_gpu(algo):
     assert rel_err(b[0], a[0]) <= 2e-2 and rel_err(b[1], a[1]) <= 2e-2
 
 
-def test_concurrent_scans_match_in_order_schedule():
+@pytest.mark.parametrize("name,seg", [("clip60s", 256), ("batched", 192), ("ragged", 64), ("clip5s", 1024)])
+def test_concurrent_scans_match_in_order_schedule(name, seg):
     """A bidirectional chunked call gives bit-identical results whether the two
     scans overlap on the library's second stream or run in order on the
-    caller's stream (same kernels, same inputs, no reduction order changes);
-    several segments, so both chains step."""
-    w = SMALL["clip60s"]
+    caller's stream (same kernels, same inputs, no reduction order changes):
+    7, 14, 7 and 3 segments, batch 2 with an initial state, a ragged tail."""
+    w = SMALL[name]
     x = make_inputs(w, 5)
-    G.set_segment_tokens(256)
+    G.set_segment_tokens(seg)
     try:
         G.set_concurrent_scans(False)
         a = run_gpu(w, x, "bidir", "chunked")
