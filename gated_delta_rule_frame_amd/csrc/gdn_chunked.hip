@@ -1153,10 +1153,11 @@ __global__ __launch_bounds__(Geo<D>::NT) __attribute__((amdgpu_waves_per_eu(4)))
 }
 
 // ---------------------------------------------------------------------------
-// 2. Segment chain.  grid (B * H, ndir[, groups]), one workgroup of MD wavefronts per
-// head and direction: H_{p+1} = P_p H_p + Q_p over the segments in scan order,
-// i.e. the prefix composition of the segments' affine maps.  Wavefront w
-// carries state columns 16 w .. 16 w + 15 in fp32 registers.  Each step the
+// 2. Segment chain.  grid (B * H, ndir x column groups[, groups]), per head and
+// direction one workgroup of MD wavefronts (or two, see ChainSplitCols):
+// H_{p+1} = P_p H_p + Q_p over the segments in scan order, i.e. the prefix
+// composition of the segments' affine maps.  A wavefront carries the state
+// columns of its 16-column strip in fp32 registers.  Each step the
 // map P_p is staged once into LDS as split bf16 (x = hi + lo) and the product
 // is formed as hi*hi + hi*lo + lo*hi with fp32 accumulation (about 16
 // significant bits per operand); the next map is loaded meanwhile.
