@@ -1325,11 +1325,18 @@ __global__ __launch_bounds__((64 * ChainSplitCols<D, CS>::NW)) void seg_chain_ke
   };
 
   auto last = [&](int p) { return p < p1 ? p : p1 - 1; };   // clamped map index
-  PRegs pr;       // P of the next step's map
+  // P maps in flight: a whole chain (CS: one wavefront per SIMD, registers to
+  // spare) fetches P two steps ahead, so that a map's loads have a step and a
+  // half to arrive before it is staged; the split chain's launches one step
+  // ahead.
+  constexpr int AHEAD = CS ? 2 : 1;
+  PRegs prA, prB;
   f32x4 qn[MD];   // Q of the current step's map, then of the next one
   // Step p: H_{p+1} = P_p H_p + Q_p with P_p staged in LDS buffer (p - p0) & 1;
-  // P_{p+1} is fetched meanwhile and staged at the end of the step.
-  auto step = [&](int p) {
+  // P_{p+AHEAD} is fetched into `fetch_dst` meanwhile, and P_{p+1} (in
+  // `stage_src`, fetched AHEAD - 1 steps earlier or meanwhile) is staged at
+  // the end of the step.
+  auto step = [&](int p, PRegs& stage_src, PRegs& fetch_dst) {
     // start state of position p (compose stores none: an empty range)
 #pragma unroll
     for (int md = 0; md < MD; ++md) tile_store_t(st, tso, (uint32_t)((p * D * D + 16 * md) * 4), H[md]);
@@ -1347,7 +1354,7 @@ __global__ __launch_bounds__((64 * ChainSplitCols<D, CS>::NW)) void seg_chain_ke
 #pragma unroll
     for (int md = 0; md < MD; ++md) acc[md] = qn[md];
     fetch_q(last(p + 1), qn);
-    fetch_p(last(p + 1), pr);
+    fetch_p(last(p + AHEAD), fetch_dst);
     const bh* phi = reinterpret_cast<const bh*>(smem + ((p - p0) & 1) * 2 * C::MAT);
     const bh* plo = phi + C::MAT / 2;
 #pragma unroll
@@ -1380,22 +1387,31 @@ __global__ __launch_bounds__((64 * ChainSplitCols<D, CS>::NW)) void seg_chain_ke
     }
 #pragma unroll
     for (int md = 0; md < MD; ++md) H[md] = acc[md];
-    stage((p + 1 - p0) & 1, pr);
+    stage((p + 1 - p0) & 1, stage_src);
     __syncthreads();
   };
 
   if (p1 > p0) {
-    fetch_p(p0, pr);
+    fetch_p(p0, prA);
     fetch_q(p0, qn);
     __syncthreads();   // zero fill done
-    stage(0, pr);
+    stage(0, prA);
+    if constexpr (AHEAD == 2) fetch_p(last(p0 + 1), prA);
     __syncthreads();
   }
   // Drain the prologue's loads here, once: otherwise the wait the compiler
   // needs for the seed state on the loop's entry path is placed at the loop
   // header and executed every step, where it waits for the prefetched maps.
   __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
-  for (int p = p0; p < p1; ++p) step(p);
+  if constexpr (AHEAD == 2) {
+    // prA holds P_{p+1} at even offsets p - p0, prB at odd ones
+    for (int p = p0; p < p1; p += 2) {
+      step(p, prA, prB);
+      if (p + 1 < p1) step(p + 1, prB, prA);
+    }
+  } else {
+    for (int p = p0; p < p1; ++p) step(p, prA, prA);
+  }
   if (mode == 1) {
     // the group's map: P_g row-major, Q_g transposed
     const __amdgpu_buffer_rsrc_t xr = block_rsrc(a.gmaps + (hs * a.ch_groups + grp) * (size_t)D * NX, act ? D * NX * 4 : 0);
