@@ -201,7 +201,7 @@ def main():
 
     if args.gpus != 1:
         sys.exit(f"bench.py measures one GPU only (got --gpus {args.gpus}); the layer's multi-GPU "
-                 "sharding is a design note, not a runnable path in this build")
+                 "sharding is described in the design notes and not implemented")
 
     import torch
     import gated_delta_rule_frame_amd as G

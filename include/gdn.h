@@ -68,7 +68,7 @@ typedef int32_t gdn_status;
 enum {
   GDN_OK = 0,
   GDN_ERR_INVALID_ARGUMENT = 1,     /* null pointer, bad size, bad enum, misalignment */
-  GDN_ERR_UNSUPPORTED = 2,          /* valid request this build does not implement */
+  GDN_ERR_UNSUPPORTED = 2,          /* valid request this library does not implement */
   GDN_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes < gdn_workspace_size() */
   GDN_ERR_HIP = 4                   /* a HIP runtime call or kernel launch failed */
 };
