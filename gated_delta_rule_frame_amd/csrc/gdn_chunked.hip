@@ -1852,7 +1852,12 @@ __global__ __launch_bounds__(64 * (D / 16)) void jac_out_kernel(Args a) {
   using G = Geo<D>;
   constexpr int MD = D / 16;
   constexpr int MAT = (KRows<D>::ELEMS * 2 + 15) / 16 * 16;
-  __shared__ __attribute__((aligned(16))) char smem[2 * MAT];
+  // output staging: 64 rows of D fp32 values, OSL floats apart, so that the
+  // global stores cover whole rows (whole cache lines) instead of each strip
+  // wave's 64-byte share of a row
+  constexpr int OSL = D + 4, C4 = D / 4, NTH = 64 * (D / 16);
+  static_assert(CH * C4 == 4 * NTH, "four groups of four values per thread");
+  __shared__ __attribute__((aligned(16))) char smem[2 * MAT + CH * OSL * 4];
   const int wave = wave_id(), lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
   const int f = blockIdx.x, bh_ = blockIdx.y, b = bh_ / a.H, h = bh_ % a.H;
   const int S = a.L, F = a.NS - 1;
@@ -1863,6 +1868,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void jac_out_kernel(Args a) {
   const uint32_t tso = (uint32_t)((col * D + 4 * g) * 4);   // starts are transposed
   const long long HD = (long long)a.H * D;
   for (int i = threadIdx.x; i < 2 * MAT / 16; i += 64 * MD) reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
+  float* const os = reinterpret_cast<float*>(lds_at(smem, (uint32_t)(2 * MAT)));
   f32x4 Hs[MD];
 #pragma unroll
   for (int md = 0; md < MD; ++md) Hs[md] = zero4();
@@ -1936,13 +1942,20 @@ __global__ __launch_bounds__(64 * (D / 16)) void jac_out_kernel(Args a) {
     f32x4 O[4], Ol[4];
     state_times_rows_T<D>(qr, Ph, cl, g, O);
     state_times_rows_T<D>(qr, Pl, cl, g, Ol);
+    // staging rows: row 16 mt + cl, columns 16 wave + 4 g ..
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) *reinterpret_cast<f32x4*>(os + (16 * mt + cl) * OSL + 16 * wave + 4 * g) = O[mt] + Ol[mt];
+    __syncthreads();
+    // whole rows: thread t stores four pieces of four consecutive values (rows
+    // past the piece fall outside the buffer)
     const long long rowb = ((long long)b * a.T + tf + CH * p) * HD + (long long)h * D;
     const __amdgpu_buffer_rsrc_t rs =
         rows_rsrc(static_cast<char*>(a.out) + rowb * esz, (long long)piece_n(p) * HD * esz);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const f32x4 val = O[mt] + Ol[mt];
-      const uint32_t off = (uint32_t)(((16 * mt + cl) * (int)HD + 16 * wave + 4 * g) * esz);
+    for (int i = 0; i < 4; ++i) {
+      const int k = t + NTH * i, row = k / C4, c4 = k % C4;
+      const f32x4 val = ld4f(os + row * OSL + 4 * c4);
+      const uint32_t off = (uint32_t)((row * (int)HD + 4 * c4) * esz);
       if constexpr (half) {
         typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
         const u32x2_t w{f32_to_bf16_bits(val[0]) | ((uint32_t)f32_to_bf16_bits(val[1]) << 16),
