@@ -1178,7 +1178,8 @@ struct ChainLay {
 // SIMD's matrix core with another strip; a strip index past the state (D =
 // 112: 7 strips, 2 x 4 wavefronts) computes on zeros and stores nothing.
 // Faster per step (the whole chain, latency-bound: 0.40 -> 0.32 ms at the 60 s
-// clip) but less work per CU, so the split chain's many-workgroup launches,
+// clip; the split chain's chain of group maps, likewise serial) but less work
+// per CU, so the split chain's many-workgroup compose and expand launches,
 // bound by the GPU's capacity, keep one workgroup of MD wavefronts.
 template <int D, bool CS>
 struct ChainSplitCols {
@@ -2033,7 +2034,7 @@ hipError_t chain_launch(Args a, const ChainWs& cw, unsigned bhc, unsigned nsl, b
   if (!split) a.ch_m = a.ch_groups = 0;
   auto go = [&](int mode, unsigned gz, bool ptv) -> hipError_t {
     a.ch_mode = mode;
-    if (mode == 0) {   // the whole chain: two column-group workgroups per head
+    if (mode == 0 || mode == 2) {   // serial chains: two column-group workgroups per head
       using SC = ChainSplitCols<D, true>;
       const dim3 grid(bhc, nsl * SC::NH, gz), block(64 * SC::NW);
       if (ptv)
