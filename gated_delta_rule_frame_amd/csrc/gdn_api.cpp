@@ -30,7 +30,13 @@ gdn_status check_problem(const gdn_problem* pr, int direction, gdn::Problem* out
   if (!pr) return fail(GDN_ERR_INVALID_ARGUMENT, "problem is NULL");
   if (pr->abi_version != GDN_ABI_VERSION)
     return fail(GDN_ERR_INVALID_ARGUMENT, "abi_version %d != %d", pr->abi_version, GDN_ABI_VERSION);
-  if (pr->reserved[0] != 0) return fail(GDN_ERR_INVALID_ARGUMENT, "reserved[0] is not zero");
+  for (int i = 0; i < (int)(sizeof pr->reserved / sizeof pr->reserved[0]); ++i)
+    if (pr->reserved[i] != 0) return fail(GDN_ERR_INVALID_ARGUMENT, "reserved[%d] is not zero", i);
+  if (pr->flags & ~(GDN_FLAG_SERIAL_SCANS | GDN_FLAG_FORM_INVERSE))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "unknown flags 0x%x", (unsigned)pr->flags);
+  if (pr->segment_tokens < 0 || pr->segment_tokens > (1 << 30))
+    return fail(GDN_ERR_INVALID_ARGUMENT, "segment_tokens must be in [0, 2^30] (got %d)", pr->segment_tokens);
+  if (pr->chain_group < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "chain_group must be >= 0 (got %d)", pr->chain_group);
   if (pr->prologue != GDN_PROLOGUE_NONE && pr->prologue != GDN_PROLOGUE_FEATURES)
     return fail(GDN_ERR_INVALID_ARGUMENT, "unknown prologue %d", pr->prologue);
   if (pr->intra != GDN_INTRA_SEQUENTIAL && pr->intra != GDN_INTRA_JACOBI)
@@ -76,6 +82,10 @@ gdn_status check_problem(const gdn_problem* pr, int direction, gdn::Problem* out
   out->first_chunk_frames = pr->first_chunk_frames;
   out->chunk_frames = pr->chunk_frames;
   out->prologue = pr->prologue == GDN_PROLOGUE_FEATURES;
+  out->segment_tokens = pr->segment_tokens;
+  out->chain_group = pr->chain_group;
+  out->serial_scans = (pr->flags & GDN_FLAG_SERIAL_SCANS) != 0;
+  out->tm_reuse = (pr->flags & GDN_FLAG_FORM_INVERSE) == 0;
   return GDN_OK;
 }
 
@@ -153,14 +163,6 @@ const char* gdn_status_string(gdn_status s) {
 }
 
 const char* gdn_last_error_message(void) { return g_last_error.c_str(); }
-
-void gdn_set_segment_tokens(int32_t tokens) { gdn::set_segment_tokens(tokens); }
-
-void gdn_set_chain_group(int32_t maps) { gdn::set_chain_group(maps); }
-
-void gdn_set_concurrent_scans(int32_t on) { gdn::set_concurrent_scans(on != 0); }
-
-void gdn_set_inverse_reuse(int32_t on) { gdn::set_inverse_reuse(on != 0); }
 
 gdn_status gdn_plan_segment_tokens(const gdn_problem* pr, int32_t direction, int32_t* tokens_out) {
   try {

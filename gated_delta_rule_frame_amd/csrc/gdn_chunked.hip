@@ -59,7 +59,6 @@
 #include "gdn_internal.h"
 #include "gdn_mfma.h"
 
-#include <atomic>
 #include <mutex>
 
 namespace gdn {
@@ -71,14 +70,11 @@ constexpr int LDD = 24;         // row stride of the diagonal inverse blocks
 constexpr int ADB = 260;        // float stride of the fp32 diagonal blocks of A (16 x 16 + pad)
 constexpr float kLog2e = 1.4426950408889634f;
 
-std::atomic<int> g_segment_override{0};
-std::atomic<int> g_chain_group{0};
-
 // Maps per group of a split chain for `nsteps` steps, or 0 for the whole chain
-// in one pass.  Automatic: split chains of 16 steps or more into groups of
-// ceil(sqrt(nsteps / 2)) maps (serial steps 2m + G, minimal near that m).
-int chain_group(int nsteps) {
-  const int k = g_chain_group.load(std::memory_order_relaxed);
+// in one pass.  k: the problem's chain_group (0 automatic: split chains of 16
+// steps or more into groups of ceil(sqrt(nsteps / 2)) maps, whose serial steps
+// 2m + G are minimal near that m).
+int chain_group(int nsteps, int k) {
   if (k == 1) return 0;
   if (k >= 2) return nsteps > k ? k : 0;
   if (nsteps < 16) return 0;
@@ -92,9 +88,9 @@ struct ChainWs {
   int m = 0, groups = 0;
   size_t gmaps_bytes = 0, gstarts_bytes = 0;
 };
-ChainWs chain_ws(int nsteps, size_t heads_dirs, int dk, int dv) {
+ChainWs chain_ws(int nsteps, int k, size_t heads_dirs, int dk, int dv) {
   ChainWs c;
-  c.m = chain_group(nsteps);
+  c.m = chain_group(nsteps, k);
   if (c.m > 0) {
     c.groups = (nsteps + c.m - 1) / c.m;
     c.gmaps_bytes = align_up(heads_dirs * c.groups * (size_t)dk * (dk + dv) * sizeof(float), 256);
@@ -102,8 +98,6 @@ ChainWs chain_ws(int nsteps, size_t heads_dirs, int dk, int dv) {
   }
   return c;
 }
-std::atomic<bool> g_concurrent_scans{true};
-std::atomic<bool> g_tm_reuse{true};
 
 struct Args {
   const bh* q;
@@ -549,6 +543,116 @@ __device__ __forceinline__ void stage_gates(const Buf& B, const StageG& st, floa
 
 __device__ void tinv_diag(const Inv& I, const Buf& B);
 
+// Software-pipelined products.  The fragments of a product are read PD steps
+// ahead of the MFMAs that use them, and a scheduling fence after every step
+// keeps that order (left to itself the compiler places each read one or two
+// MFMAs before its use, so every MFMA waits out most of an LDS round trip).
+// PD fragments of two reads each stay within the 15 LDS operations a
+// wavefront can have in flight.  Measured on the 60 s clip: output launches
+// 0.67 -> 0.61 ms (the kernels are bound by their instruction issue: two
+// wavefronts per SIMD keep it busy about 80% of the time).
+constexpr int kPD = 6;
+#define GDN_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// acc[j][mt] = rows (16 mt ..) of `rows` (d-contracted fp16) times strip j
+// (TR: the transposed product, strip as the A operand).
+template <int D, int SPW, bool TR, int PD = kPD>
+__device__ __forceinline__ void wrows_state(const hb* rows, const f16x8_t (&Xp)[SPW][Geo<D>::NP], int cl, int g,
+                                            f32x4 (&acc)[SPW][4]) {
+  constexpr int NP = Geo<D>::NP, NF = NP * 4;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) acc[j][mt] = zero4();
+  f16x8_t fr[NF];
+  auto ld = [&](int i) { fr[i] = fragK<D>(rows + krow<D>(16 * (i & 3) + cl), i >> 2, g); };
+#pragma unroll
+  for (int i = 0; i < PD && i < NF; ++i) ld(i);
+#pragma unroll
+  for (int i = 0; i < NF; ++i) {
+    GDN_FENCE();
+    const int mt = i & 3, p = i >> 2;
+#pragma unroll
+    for (int j = 0; j < SPW; ++j)
+      acc[j][mt] = TR ? mfma32(Xp[j][p], fr[i], acc[j][mt]) : mfma32(fr[i], Xp[j][p], acc[j][mt]);
+    if (i + PD < NF) ld(i + PD);
+  }
+  GDN_FENCE();
+}
+
+// out[j][mt] (+)= lower-triangular token matrix M times the token-row tiles
+// of strip j (pairs vp[j][0] = (0, 1), vp[j][1] = (2, 3)); TR: transposed.
+template <int SPW, bool TR>
+__device__ __forceinline__ void wtri(const hb* M, const f16x8_t (&vp)[SPW][2], int cl, int g, f32x4 (&acc)[SPW][4]) {
+  constexpr int kP[6] = {0, 0, 0, 0, 1, 1}, kM[6] = {0, 1, 2, 3, 2, 3};
+  f16x8_t fr[6];
+#pragma unroll
+  for (int i = 0; i < 6; ++i) fr[i] = fragA2(M + (16 * kM[i] + cl) * LDT, 2 * kP[i], g);
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    GDN_FENCE();
+#pragma unroll
+    for (int j = 0; j < SPW; ++j)
+      acc[j][kM[i]] = TR ? mfma32(vp[j][kP[i]], fr[i], acc[j][kM[i]]) : mfma32(fr[i], vp[j][kP[i]], acc[j][kM[i]]);
+  }
+  GDN_FENCE();
+}
+
+// X[j] <- dec X[j] + K^T vs[j] (see state_update): K^T fragments by
+// transposing reads, pipelined like the products above.
+template <int D, int SPW, int PD = kPD>
+__device__ __forceinline__ void wstate_update(const hb* kr, const f16x8_t (&vs)[SPW][2], float dec, int cl, int g,
+                                              f32x4 (&X)[SPW][Geo<D>::MD]) {
+  constexpr int MD = Geo<D>::MD, NF = 2 * MD;
+  const hb* kt = kr + krow<D>(4 * g + (cl >> 2)) + 4 * (cl & 3);
+  f16x8_t fr[NF];
+  // fragment i: token half q = i / MD, component tile md = i % MD
+  auto ld = [&](int i) {
+    const int q = i / MD, md = i % MD;
+    fr[i] = cat8(ld4_tr(kt + krow<D>(32 * q) + 16 * md), ld4_tr(kt + krow<D>(32 * q + 16) + 16 * md));
+  };
+#pragma unroll
+  for (int i = 0; i < PD && i < NF; ++i) ld(i);
+#pragma unroll
+  for (int md = 0; md < MD; ++md)
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) X[j][md] = X[j][md] * dec;
+#pragma unroll
+  for (int i = 0; i < NF; ++i) {
+    GDN_FENCE();
+    const int q = i / MD, md = i % MD;
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) X[j][md] = mfma32(fr[i], vs[j][q], X[j][md]);
+    if (i + PD < NF) ld(i + PD);
+  }
+  GDN_FENCE();
+}
+
+// NK Gram tiles (see gram_tile), every k step's two fragments read PDG steps
+// ahead of its MFMA; consecutive MFMAs update different tiles.
+template <int D, int NK, int PDG = 3>
+__device__ __forceinline__ void gram_tiles_pl(const hb* const (&ar)[NK], const hb* const (&br)[NK], int g,
+                                              f32x4 (&acc)[NK]) {
+  constexpr int NP = Geo<D>::NP, NS = NP * NK;
+#pragma unroll
+  for (int k = 0; k < NK; ++k) acc[k] = zero4();
+  f16x8_t fa[NS], fb[NS];
+  // step i: k step i / NK of tile i % NK
+  auto ld = [&](int i) {
+    fa[i] = fragK<D>(ar[i % NK], i / NK, g);
+    fb[i] = fragK<D>(br[i % NK], i / NK, g);
+  };
+#pragma unroll
+  for (int i = 0; i < PDG && i < NS; ++i) ld(i);
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    GDN_FENCE();
+    acc[i % NK] = mfma32(fa[i], fb[i], acc[i % NK]);
+    if (i + PDG < NS) ld(i + PDG);
+  }
+  GDN_FENCE();
+}
+
 // --- Gram tiles -------------------------------------------------------------------
 // Tile (ta, tb), ta <= tb, of the products of the K rows of block ta with the
 // K (or Q) rows of block tb: lane holds rows y = 16 ta + 4g + r against row
@@ -581,14 +685,20 @@ constexpr uint32_t kPackA = pack_pairs(kPairA), kPackB = pack_pairs(kPairB);
 // inverses.  The four products are formed before any result is stored: a
 // load placed after an LDS store waits for it (the compiler cannot prove the
 // two apart), which would serialise the blocks.
-template <int D>
+template <int D, int PDG = 3>
 __device__ void gram_stage_helper(const Args& a, const Buf& B, const Inv& I) {
   const int lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
   const float c2 = a.c * a.c;
   {
     f32x4 sb[4];
+    if constexpr (PDG == 0) {
 #pragma unroll
-    for (int blk = 0; blk < 4; ++blk) sb[blk] = gram_tile<D>(B.kr, B.kr, blk, blk, cl, g);
+      for (int blk = 0; blk < 4; ++blk) sb[blk] = gram_tile<D>(B.kr, B.kr, blk, blk, cl, g);
+    } else {
+      const hb* const rows[4] = {B.kr + krow<D>(cl), B.kr + krow<D>(16 + cl), B.kr + krow<D>(32 + cl),
+                                 B.kr + krow<D>(48 + cl)};
+      gram_tiles_pl<D, 4, PDG>(rows, rows, g, sb);
+    }
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
       const f32x4 s = sb[blk];
@@ -619,18 +729,49 @@ struct GramStrips {
   static constexpr int NTILE = OUT ? 16 : 6;
   static constexpr int NK = (NTILE + Geo<D>::NSW - 1) / Geo<D>::NSW, NFULL = NTILE / Geo<D>::NSW;
 };
-template <int D, bool OUT>
+template <int D, bool OUT, int PDG = 3>
 __device__ __forceinline__ void gram_strips_products(const Buf& B, f32x4 (&sk)[GramStrips<D, OUT>::NK]) {
   using GS = GramStrips<D, OUT>;
   const int wave = wave_id(), lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
+  if constexpr (PDG == 0) {   // each tile's fragments read just before its MFMAs
 #pragma unroll
-  for (int k = 0; k < GS::NK; ++k) {
+    for (int k = 0; k < GS::NK; ++k) {
+      const int t = wave + k * Geo<D>::NSW;
+      if (k < GS::NFULL || t < GS::NTILE) {
+        const bool isp = t >= 6;
+        const int u = isp ? t - 6 : t;
+        const int ta = (kPackA >> (2 * u)) & 3, tb = (kPackB >> (2 * u)) & 3;
+        sk[k] = gram_tile<D>(B.kr, isp ? B.qr : B.kr, ta, tb, cl, g);
+      }
+    }
+    return;
+  }
+  auto rows = [&](int k, const hb*& ar, const hb*& br) {
     const int t = wave + k * Geo<D>::NSW;
-    if (k < GS::NFULL || t < GS::NTILE) {
-      const bool isp = t >= 6;
-      const int u = isp ? t - 6 : t;
-      const int ta = (kPackA >> (2 * u)) & 3, tb = (kPackB >> (2 * u)) & 3;
-      sk[k] = gram_tile<D>(B.kr, isp ? B.qr : B.kr, ta, tb, cl, g);
+    const bool isp = t >= 6;
+    const int u = isp ? t - 6 : t;
+    const int ta = (kPackA >> (2 * u)) & 3, tb = (kPackB >> (2 * u)) & 3;
+    ar = B.kr + krow<D>(16 * ta + cl);
+    br = (isp ? B.qr : B.kr) + krow<D>(16 * tb + cl);
+  };
+  if constexpr (GS::NFULL > 0) {
+    const hb* ar[GS::NFULL];
+    const hb* br[GS::NFULL];
+#pragma unroll
+    for (int k = 0; k < GS::NFULL; ++k) rows(k, ar[k], br[k]);
+    f32x4 acc[GS::NFULL];
+    gram_tiles_pl<D, GS::NFULL, PDG>(ar, br, g, acc);
+#pragma unroll
+    for (int k = 0; k < GS::NFULL; ++k) sk[k] = acc[k];
+  }
+  if constexpr (GS::NK > GS::NFULL) {
+    if (wave + GS::NFULL * Geo<D>::NSW < GS::NTILE) {   // wave-uniform
+      const hb* ar[1];
+      const hb* br[1];
+      rows(GS::NFULL, ar[0], br[0]);
+      f32x4 acc[1];
+      gram_tiles_pl<D, 1, PDG>(ar, br, g, acc);
+      sk[GS::NFULL] = acc[0];
     }
   }
 }
@@ -675,10 +816,10 @@ __device__ __forceinline__ void gram_strips_epilogues(const Args& a, const Buf& 
     }
   }
 }
-template <int D, bool OUT>
+template <int D, bool OUT, int PDG = 3>
 __device__ void gram_stage_strips(const Args& a, const Buf& B, const Inv& I) {
   f32x4 sk[GramStrips<D, OUT>::NK];
-  gram_strips_products<D, OUT>(B, sk);
+  gram_strips_products<D, OUT, PDG>(B, sk);
   gram_strips_epilogues<D, OUT>(a, B, I, sk);
 }
 
@@ -832,14 +973,18 @@ __device__ __forceinline__ void stage_tm(const Buf& B, const StageTm& st) {
 template <int D, int NK>
 __device__ __forceinline__ void gram_p_products(const Buf& B, int t0, int dt, f32x4 (&sk)[NK]) {
   const int lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
+  // every caller's tiles are all below 10 or (a single tile) none is (wave-uniform)
+  if (t0 + (NK - 1) * dt >= 10) return;
+  const hb* ar[NK];
+  const hb* br[NK];
 #pragma unroll
   for (int k = 0; k < NK; ++k) {
     const int u = t0 + k * dt;
-    if (u < 10) {
-      const int ta = (kPackA >> (2 * u)) & 3, tb = (kPackB >> (2 * u)) & 3;
-      sk[k] = gram_tile<D>(B.kr, B.qr, ta, tb, cl, g);
-    }
+    const int ta = (kPackA >> (2 * u)) & 3, tb = (kPackB >> (2 * u)) & 3;
+    ar[k] = B.kr + krow<D>(16 * ta + cl);
+    br[k] = B.qr + krow<D>(16 * tb + cl);
   }
+  gram_tiles_pl<D, NK>(ar, br, g, sk);
 }
 template <int NK>
 __device__ __forceinline__ void gram_p_epilogues(const Args& a, const Buf& B, int t0, int dt, const f32x4 (&sk)[NK]) {
@@ -943,13 +1088,6 @@ __device__ __forceinline__ void state_times_rows_T(const hb* rows, const f16x8_t
     for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma32(Xp[p], fragK<D>(rows + krow<D>(16 * mt + cl), p, g), acc[mt]);
 }
 
-__device__ __forceinline__ void tri_times_T(const hb* M, const f16x8_t (&vp)[2], int cl, int g, f32x4 (&acc)[4]) {
-#pragma unroll
-  for (int p = 0; p < 2; ++p)
-#pragma unroll
-    for (int mt = 2 * p; mt < 4; ++mt) acc[mt] = mfma32(vp[p], fragA2(M + (16 * mt + cl) * LDT, 2 * p, g), acc[mt]);
-}
-
 // X[j] <- dec X[j] + K^T vs[j]  (vs: fp16 pairs of token-row tiles).  The K^T
 // fragments are transposing reads of the K rows: lane (g, cl) = (g, a + 4 j)
 // addresses row 16 h + 4 g + j, components 16 md + 4 a .. + 3, so that lane
@@ -998,6 +1136,9 @@ __device__ __forceinline__ void seg_map_body(Args a) {
   using G = Geo<D>;
   using L = Lay<D, false>;
   constexpr int MD = G::MD, SPW = QO ? 1 : 2, JQ = SPW - 1;   // JQ: the Q strip
+  // Under the Q-only kernels' 128-register cap the products and Gram tiles
+  // read each fragment just before its MFMA (the pipelined forms spill there).
+  constexpr int PDG = QO ? 0 : 3;
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
   const int wave = wave_id(), lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
   const int pos = blockIdx.x;                       // scan position of the segment
@@ -1050,8 +1191,8 @@ __device__ __forceinline__ void seg_map_body(Args a) {
       fetch_v<D>(a, b, h, s1b, sv);
     }
     __syncthreads();
-    if (helper) gram_stage_helper<D>(a, buf_at<D, false>(smem, 0), I);
-    else gram_stage_strips<D, false>(a, buf_at<D, false>(smem, 0), I);
+    if (helper) gram_stage_helper<D, PDG>(a, buf_at<D, false>(smem, 0), I);
+    else gram_stage_strips<D, false, PDG>(a, buf_at<D, false>(smem, 0), I);
     __syncthreads();
   }
   if (helper) {
@@ -1063,7 +1204,7 @@ __device__ __forceinline__ void seg_map_body(Args a) {
       fetch_gates(a, b, h, piece(c + 2), sg);
       tinv_offdiag(I, Bc);
       __syncthreads();
-      if (c + 1 < nsub) gram_stage_helper<D>(a, Bn, I);
+      if (c + 1 < nsub) gram_stage_helper<D, PDG>(a, Bn, I);
       __syncthreads();
     }
     return;
@@ -1079,7 +1220,8 @@ __device__ __forceinline__ void seg_map_body(Args a) {
       f16x8_t Xp[SPW][G::NP];
 #pragma unroll
       for (int j = 0; j < SPW; ++j) state_pairs<D>(X[j], Xp[j]);
-      rows_times_state<D, SPW>(Bc.kr, Xp, cl, g, R);
+      if constexpr (QO) rows_times_state<D, SPW>(Bc.kr, Xp, cl, g, R);
+      else wrows_state<D, SPW, false>(Bc.kr, Xp, cl, g, R);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const f32x4 ce = ld4f(Bc.ce + 16 * mt + 4 * g);
@@ -1103,7 +1245,8 @@ __device__ __forceinline__ void seg_map_body(Args a) {
       for (int j = 0; j < SPW; ++j)
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) Vn[j][mt] = zero4();
-      tri_times<SPW>(Bc.tt, Rh, cl, g, Vn);
+      if constexpr (QO) tri_times<SPW>(Bc.tt, Rh, cl, g, Vn);
+      else wtri<SPW, false>(Bc.tt, Rh, cl, g, Vn);
       f16x8_t Vs[SPW][2];
       const f32x4 d0 = ld4f(Bc.dn + 4 * g), d1 = ld4f(Bc.dn + 16 + 4 * g);
       const f32x4 d2 = ld4f(Bc.dn + 32 + 4 * g), d3 = ld4f(Bc.dn + 48 + 4 * g);
@@ -1112,7 +1255,8 @@ __device__ __forceinline__ void seg_map_body(Args a) {
         Vs[j][0] = tof16x8(Vn[j][0] * d0, Vn[j][1] * d1);
         Vs[j][1] = tof16x8(Vn[j][2] * d2, Vn[j][3] * d3);
       }
-      state_update<D, SPW>(Bc.kr, Vs, Bc.eg[CH - 1], cl, g, X);
+      if constexpr (QO) state_update<D, SPW>(Bc.kr, Vs, Bc.eg[CH - 1], cl, g, X);
+      else wstate_update<D, SPW>(Bc.kr, Vs, Bc.eg[CH - 1], cl, g, X);
     }
     // The Q-only maps serve bidirectional calls, which never reuse Tm (their
     // a.tm is null: the stores fall outside an empty buffer).  Under the
@@ -1121,7 +1265,7 @@ __device__ __forceinline__ void seg_map_body(Args a) {
     // without it the prologue variant does (measured at the 60 s clip, per
     // Q-only launch: 0.29 against 0.33 ms, and 0.31 against 0.33 ms).
     if constexpr (!QO || !PRO) store_tm<D>(tm_rsrc(a, slot, b, h, piece(c)), Bc);
-    if (c + 1 < nsub) gram_stage_strips<D, false>(a, Bn, I);
+    if (c + 1 < nsub) gram_stage_strips<D, false, PDG>(a, Bn, I);
     __syncthreads();
   }
   // store X = [P | Q] ([D][2D], P row-major, Q transposed; QO: the Q half)
@@ -1631,7 +1775,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
       {
         f16x8_t Hp[SPW][G::NP];
         state_pairs<D>(H[0], Hp[0]);
-        rows_times_state<D, SPW>(Bc.kr, Hp, cl, g, R);
+        wrows_state<D, SPW, false>(Bc.kr, Hp, cl, g, R);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
           R[0][mt] = vals_tile<D>(Bc.vr, mt, wave, cl, g) - ld4f(Bc.ce + 16 * mt + 4 * g) * R[0][mt];
@@ -1641,11 +1785,11 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
       stage_v<D>(Bc, sv);
       fetch_v<D>(a, b, h, piece(c + 2), sv);
       {
-        f32x4 O[4];   // outputs, transposed tiles (lane: token 16 mt + cl, columns 4g ..)
+        f32x4 O[1][4];   // outputs, transposed tiles (lane: token 16 mt + cl, columns 4g ..)
         {
-          f16x8_t Hp[G::NP];
-          state_pairs<D>(H[0], Hp);
-          state_times_rows_T<D>(Bc.qr, Hp, cl, g, O);
+          f16x8_t Hp[1][G::NP];
+          state_pairs<D>(H[0], Hp[0]);
+          wrows_state<D, 1, true>(Bc.qr, Hp, cl, g, O);
         }
         fetch_kq<D, true, PRO>(a, b, h, piece(c + 2), sk);
         f16x8_t Rh[SPW][2];
@@ -1654,19 +1798,19 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
         f32x4 Vn[SPW][4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) Vn[0][mt] = zero4();
-        tri_times<SPW>(Bc.tt, Rh, cl, g, Vn);
+        wtri<SPW, false>(Bc.tt, Rh, cl, g, Vn);
         f16x8_t Vh[SPW][2];
         Vh[0][0] = tof16x8(Vn[0][0], Vn[0][1]);
         Vh[0][1] = tof16x8(Vn[0][2], Vn[0][3]);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) O[mt] = Bc.eg[16 * mt + cl] * O[mt];
-        tri_times_T(Bc.pp, Vh[0], cl, g, O);
+        for (int mt = 0; mt < 4; ++mt) O[0][mt] = Bc.eg[16 * mt + cl] * O[0][mt];
+        wtri<1, true>(Bc.pp, Vh, cl, g, O);
         f16x8_t Vs[SPW][2];
         const f32x4 d0 = ld4f(Bc.dn + 4 * g), d1 = ld4f(Bc.dn + 16 + 4 * g);
         const f32x4 d2 = ld4f(Bc.dn + 32 + 4 * g), d3 = ld4f(Bc.dn + 48 + 4 * g);
         Vs[0][0] = tof16x8(Vn[0][0] * d0, Vn[0][1] * d1);
         Vs[0][1] = tof16x8(Vn[0][2] * d2, Vn[0][3] * d3);
-        state_update<D, SPW>(Bc.kr, Vs, Bc.eg[CH - 1], cl, g, H);
+        wstate_update<D, SPW>(Bc.kr, Vs, Bc.eg[CH - 1], cl, g, H);
         // The Gram products of c+1, then the output staging, then the Gram
         // epilogues: every LDS read of the phase is placed before its first
         // LDS store, which it would otherwise wait behind.
@@ -1681,7 +1825,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
         // staging rows: row 16 mt + cl, columns 16 wave + 4 g ..
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
-          *reinterpret_cast<f32x4*>(I.os + (16 * mt + cl) * L::OSL + 16 * wave + 4 * g) = O[mt];
+          *reinterpret_cast<f32x4*>(I.os + (16 * mt + cl) * L::OSL + 16 * wave + 4 * g) = O[0][mt];
         if constexpr (TML) {
           if (more) gram_p_epilogues<1>(a, Bn, wave < SP ? wave : 10, 0, skp);
         } else {
@@ -1984,7 +2128,7 @@ Plan make_plan(const Problem& p, int direction) {
   pl.cc = direction == GDN_CHUNK_CAUSAL;
   pl.dirs = direction == GDN_FORWARD || pl.cc ? 1 : direction == GDN_BACKWARD ? 2 : 3;
   pl.ndir = pl.dirs == 3 ? 2 : 1;
-  int L = g_segment_override.load(std::memory_order_relaxed);
+  int L = p.segment_tokens;
   if (L <= 0) {
     // The output kernel runs one workgroup per CU (its LDS use), so aim for
     // five whole rounds of workgroups over the 256 CUs of a gfx950 part:
@@ -1992,7 +2136,16 @@ Plan make_plan(const Problem& p, int direction) {
     // rounds avoid a partly idle last round.
     constexpr long long kRounds = 5, kComputeUnits = 256;
     const long long hb = (long long)p.B * p.H;
-    const long long want = (kRounds * kComputeUnits + hb - 1) / hb;
+    long long want = (kRounds * kComputeUnits + hb - 1) / hb;
+    // Short sequences: the chain's serial steps (one per segment, each about
+    // as long as a sub-chunk step of the map and output kernels) would
+    // outweigh the per-segment work, so keep at most about 2 sqrt(U)
+    // segments for U sub-chunks (one 880-token frame: 7 segments of 128
+    // tokens, 60 against 92 us a step with 14 segments of 64).
+    const long long U = (p.T + CH - 1) / CH;
+    long long cap = 1;
+    while ((cap + 1) * (cap + 1) <= 4 * U) ++cap;
+    if (want > cap) want = cap;
     long long per = (p.T + want - 1) / want;
     L = (int)((per + CH - 1) / CH * CH);
   }
@@ -2011,14 +2164,15 @@ Plan make_plan(const Problem& p, int direction) {
   pl.acc_off = pl.starts_off + align_up(starts, 256);
   pl.fac_off = pl.acc_off + align_up(acc, 256);
   // bidirectional calls never split the chain (see launch_d)
-  if (pl.dirs != 3) pl.cw = chain_ws(pl.NS - 1, bhd, p.dk, p.dv);
+  if (pl.dirs != 3) pl.cw = chain_ws(pl.NS - 1, p.chain_group, bhd, p.dk, p.dv);
   pl.gmaps_off = pl.fac_off + align_up(prologue_bytes(p), 256);
   pl.gstarts_off = pl.gmaps_off + pl.cw.gmaps_bytes;
-  // Tm blocks of every sub-chunk of a forward- or backward-only call with
-  // maps (fp16, 5 KB per sub-chunk), whether or not their reuse is switched
-  // on (two-scan calls form them in both kernels: see launch_d)
+  // Tm blocks of every sub-chunk of each scan with maps (fp16, 5 KB per
+  // sub-chunk and head), whether or not the output kernels load them: both
+  // scans of a bidirectional call, the forward scan of a chunk-causal one
   const size_t U = (size_t)((p.T + CH - 1) / CH);
-  pl.tm_bytes = pl.NS >= 2 && pl.dirs != 3 && !pl.cc ? align_up(bhd * U * kTmElems * 2, 256) : 0;
+  const size_t tm_slots = pl.NS >= 2 ? (pl.cc ? 1 : (size_t)pl.ndir) : 0;
+  pl.tm_bytes = tm_slots ? align_up(tm_slots * p.B * p.H * U * kTmElems * 2, 256) : 0;
   pl.tm_off = pl.gstarts_off + pl.cw.gstarts_bytes;
   pl.bytes = pl.tm_off + pl.tm_bytes;
   return pl;
@@ -2058,32 +2212,45 @@ hipError_t chain_launch(Args a, const ChainWs& cw, unsigned bhc, unsigned nsl, b
   return go(3, cw.groups, pt);
 }
 
-// A library-owned stream per device (default priority) with a fork and a join
-// event, for the concurrent part of bidirectional calls.  Created on first use
-// and kept until the process ends.  The mutex makes a call's fork, launches and
-// join one unit with respect to calls from other host threads.
+// Library-owned side streams (default priority) with a fork and a join event,
+// for the concurrent part of two-scan calls: per device, one for each of up
+// to kSides caller streams, bound on first use and kept until the process
+// ends.  A call whose stream finds no free entry (or whose side stream cannot
+// be created) runs in order on its own stream.  The entry's mutex makes a
+// call's fork, launches and join one unit with respect to calls on the same
+// caller stream from other host threads; calls on different streams do not
+// wait for each other.
 struct Side {
   std::mutex mu;
   hipStream_t stream = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
 };
 
-// The side stream of the current device, or null if it cannot be created (the
-// call then runs everything on its own stream).
-Side* side_stream() {
-  constexpr int kMaxDevices = 64;
-  static Side sides[kMaxDevices];
-  static std::once_flag once[kMaxDevices];
-  static bool ok[kMaxDevices];
+Side* side_stream(hipStream_t caller) {
+  constexpr int kMaxDevices = 64, kSides = 8;
+  struct Dev {
+    std::mutex mu;                 // guards the binding of entries to caller streams
+    int used = 0;
+    hipStream_t owner[kSides] = {};
+    Side side[kSides];
+  };
+  static Dev devs[kMaxDevices];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  std::call_once(once[dev], [dev] {
-    Side& s = sides[dev];
-    ok[dev] = hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking) == hipSuccess &&
-              hipEventCreateWithFlags(&s.fork, hipEventDisableTiming) == hipSuccess &&
-              hipEventCreateWithFlags(&s.join, hipEventDisableTiming) == hipSuccess;
-  });
-  return ok[dev] ? &sides[dev] : nullptr;
+  Dev& d = devs[dev];
+  std::lock_guard<std::mutex> lk(d.mu);
+  for (int i = 0; i < d.used; ++i)
+    if (d.owner[i] == caller) return d.side[i].stream ? &d.side[i] : nullptr;
+  if (d.used == kSides) return nullptr;
+  Side& s = d.side[d.used];
+  d.owner[d.used++] = caller;
+  if (hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&s.fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&s.join, hipEventDisableTiming) != hipSuccess) {
+    s.stream = nullptr;   // this caller stream runs in order from now on
+    return nullptr;
+  }
+  return &s;
 }
 
 template <int D, bool PRO>
@@ -2118,14 +2285,13 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
   a.c = p.key_scale;
   a.gmaps = reinterpret_cast<float*>(ws + pl.gmaps_off);
   a.gstarts = reinterpret_cast<float*>(ws + pl.gstarts_off);
-  // Reuse of the map kernel's Tm blocks by the output kernel: forward- and
-  // backward-only calls (measured at the 60 s clip, output kernel alone:
-  // 0.613 -> 0.590 ms for a forward call; for the partial-storing and -adding
-  // launches of a bidirectional call 0.597 -> 0.612 ms, so two-scan calls
-  // form their own).
-  a.tm = pl.tm_bytes && g_tm_reuse.load(std::memory_order_relaxed) ? reinterpret_cast<hb*>(ws + pl.tm_off) : nullptr;
-  const unsigned bhc = (unsigned)(p.B * p.H);
   const bool both = pl.dirs == 3;
+  // The output kernels load the map kernels' Tm blocks (the wide-strip
+  // kernel has no wavefront to spare for the inverse).  With the feature
+  // prologue, two-scan calls form them in the output kernels (the Q-only map
+  // kernel's prologue variant stores none: see seg_map_body).
+  a.tm = pl.tm_bytes && p.tm_reuse && (!PRO || (!both && !pl.cc)) ? reinterpret_cast<hb*>(ws + pl.tm_off) : nullptr;
+  const unsigned bhc = (unsigned)(p.B * p.H);
   // Workgroups are dealt to the 8 XCDs (each with its own L2) in turn.  With
   // the segment index padded to a multiple of 8, a segment of neighbouring
   // heads lands on the same XCD, so the cache lines their rows share (a head's
@@ -2159,14 +2325,14 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
   // The split chain (many workgroups for a short time) pays off where the
   // chain stands alone on the critical path; beside the other scan's maps
   // and outputs in the two-stream bidirectional schedule, the single
-  // workgroup per head is faster (measured: 2.46 against 2.33 ms per step at
-  // the 60 s clip), so bidirectional calls never split (in either schedule,
-  // which keeps the two schedules' results identical).
-  const bool split = !both;
+  // workgroup pair per head is faster (measured at the 60 s clip: splitting
+  // both chains 2.46 against 2.33 ms per step, splitting the forward chain
+  // alone 2.32 against 2.10 ms), so bidirectional calls never split (in
+  // either schedule, which keeps the two schedules' results identical).
   auto chain_k = [&](int slot, hipStream_t st) -> hipError_t {
     a.slot0 = slot;
     prof_begin(st, GDN_KERNEL_SEG_CHAIN);
-    const hipError_t e = chain_launch<D>(a, pl.cw, bhc, 1, both && slot == 1, st, split);
+    const hipError_t e = chain_launch<D>(a, pl.cw, bhc, 1, both && slot == 1, st, !both);
     if (e != hipSuccess) return e;
     prof_end(st, GDN_KERNEL_SEG_CHAIN);
     return hipSuccess;
@@ -2239,7 +2405,7 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
       prof_end(st, GDN_KERNEL_SEG_OUT);
       return hipSuccess;
     };
-    Side* side = g_concurrent_scans.load(std::memory_order_relaxed) ? side_stream() : nullptr;
+    Side* side = p.serial_scans ? nullptr : side_stream(stream);
     if (!side) {
       if ((e = rev_chunks(stream)) != hipSuccess) return e;
       if ((e = maps_k(0, stream)) != hipSuccess) return e;
@@ -2261,7 +2427,7 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
     if ((e = chain_k(0, stream)) != hipSuccess) return e;
     return outputs(pl.dirs == 1 ? 0 : 1, stream);
   }
-  Side* side = g_concurrent_scans.load(std::memory_order_relaxed) ? side_stream() : nullptr;
+  Side* side = p.serial_scans ? nullptr : side_stream(stream);
   if (!side) {
     if ((e = maps_k(0, stream)) != hipSuccess) return e;
     if ((e = maps_k(1, stream)) != hipSuccess) return e;
@@ -2338,7 +2504,7 @@ JacPlan jac_plan(const Problem& p, int direction) {
   pl.maps_off = 0;
   pl.starts_off = align_up(per * p.dk * (p.dk + p.dv) * sizeof(float), 256);
   pl.fac_off = pl.starts_off + align_up(per * p.dk * p.dv * sizeof(float), 256);
-  pl.cw = chain_ws(p.F, (size_t)pl.ndir * p.B * p.H, p.dk, p.dv);
+  pl.cw = chain_ws(p.F, p.chain_group, (size_t)pl.ndir * p.B * p.H, p.dk, p.dv);
   pl.gmaps_off = pl.fac_off + align_up(prologue_bytes(p), 256);
   pl.gstarts_off = pl.gmaps_off + pl.cw.gmaps_bytes;
   pl.bytes = pl.gstarts_off + pl.cw.gstarts_bytes;
@@ -2420,9 +2586,5 @@ hipError_t jacobi_launch(const Problem& p, int direction, const Tensors& t, void
   }
 }
 
-void set_segment_tokens(int tokens) { g_segment_override.store(tokens > 0 ? tokens : 0); }
-void set_chain_group(int maps) { g_chain_group.store(maps > 0 ? maps : 0); }
-void set_concurrent_scans(bool on) { g_concurrent_scans.store(on); }
-void set_inverse_reuse(bool on) { g_tm_reuse.store(on); }
 
 }  // namespace gdn

@@ -20,6 +20,10 @@ struct Problem {
   bool jacobi;         // frame-level transition (GDN_INTRA_JACOBI)
   int first_chunk_frames, chunk_frames;   // GDN_CHUNK_CAUSAL chunking (frames)
   bool prologue;       // GDN_PROLOGUE_FEATURES
+  int segment_tokens;  // 0: automatic
+  int chain_group;     // 0: automatic, 1: whole, m >= 2: groups of m
+  bool serial_scans;   // GDN_FLAG_SERIAL_SCANS
+  bool tm_reuse;       // !GDN_FLAG_FORM_INVERSE
 };
 
 // Device pointers of one call.
@@ -59,10 +63,6 @@ hipError_t jacobi_launch(const Problem& p, int direction, const Tensors& t,
 size_t prologue_bytes(const Problem& p);
 hipError_t prologue_launch(const Problem& p, const Tensors& t, float* fac, hipStream_t stream);
 
-void set_segment_tokens(int tokens);
-void set_chain_group(int maps);
-void set_concurrent_scans(bool on);
-void set_inverse_reuse(bool on);
 int chunked_segment_tokens(const Problem& p, int direction);
 
 // Kernel timing hooks (gdn_profile.cpp): no-ops unless profiling is enabled.

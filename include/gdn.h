@@ -40,10 +40,10 @@
  *
  * Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream)
  * and return after enqueueing.  `stream` must belong to the current device.
- * A bidirectional call of the chunked path also runs part of its work on a
- * stream the library owns on that device (created on first use, default
- * priority, kept until the process ends), joined back into `stream` with
- * events before the call's last kernel; see gdn_set_concurrent_scans().  The library allocates no device memory: the
+ * A bidirectional or chunk-causal call of the chunked path also runs part of
+ * its work on a stream the library owns (see GDN_FLAG_SERIAL_SCANS), joined
+ * back into `stream` with events before the call's last kernel.  The library
+ * keeps no other state between calls and allocates no device memory: the
  * caller passes a workspace of at least gdn_workspace_size() bytes.  All
  * arguments are validated on the host before anything is enqueued; on any
  * error nothing is enqueued and a status other than GDN_OK is returned, with
@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef int32_t gdn_status;
 enum {
@@ -85,7 +85,34 @@ enum { GDN_FORWARD = 0, GDN_BACKWARD = 1, GDN_BIDIRECTIONAL = 2, GDN_CHUNK_CAUSA
 
 /* Algorithm selection.  AUTO picks the frame-chunked MFMA path for bf16 q/k/v
  * and the token-recurrent fp32 path for fp32 q/k/v (whose tolerance needs fp32
- * products).  RECURRENT forces the token-sequential kernel (any dtype). */
+ * products).  RECURRENT forces the token-sequential kernel (any dtype).
+ *
+ * Numeric domain of the chunked path (AUTO with bf16 q/k/v, or CHUNKED).  Its
+ * matrix-core products take fp16 operands with fp32 accumulation; states,
+ * gates and accumulations are fp32.
+ *   - Inputs: each bf16 value of q and k is converted to fp16 rounding
+ *     toward zero.  That is exact for magnitudes in [2^-14, 65504] (a bf16
+ *     value there has at most 8 significant bits, fp16 keeps 11), loses less
+ *     than 2^-24 in absolute value below 2^-14, and saturates at +-65504
+ *     above: such an input is taken as +-65504.  (With the feature prologue
+ *     the normalised q and k, at most sqrt(d_k) in magnitude, are rounded to
+ *     the nearest fp16.)  key_scale, the gates and beta enter as fp32
+ *     factors.  v enters an fp32 residual exactly (the frame-level
+ *     transition rounds c beta v to the nearest fp16).
+ *   - Intermediates: the state, the per-token residuals v - prediction and
+ *     the corrections they become after the sub-chunk's triangular solve,
+ *     and (bidirectional and chunk-causal calls) the first scan's outputs,
+ *     which are kept as an fp16 partial sum, are rounded to the nearest fp16
+ *     at each product; a magnitude above 65504 there becomes +-inf and
+ *     propagates.
+ *   - Hence the chunked path is accurate (within 2e-2 of the output RMS)
+ *     when every element of v, of the initial state and of each scan's
+ *     outputs stays below 2^15 in magnitude.  On the documented domain
+ *     (g <= 0, beta in [0, 1], |key_scale k| <= 1) the state and the
+ *     corrections stay within a small multiple of max|v| + max|initial
+ *     state|, so |v| and |initial state| up to about 2^12 keep every
+ *     intermediate in range.  Larger magnitudes need GDN_ALGO_RECURRENT,
+ *     which computes in fp32 throughout and has no such limit. */
 enum { GDN_ALGO_AUTO = 0, GDN_ALGO_CHUNKED = 1, GDN_ALGO_RECURRENT = 2 };
 
 /* Transition inside a frame.  SEQUENTIAL: the token-wise rule applied to every
@@ -131,8 +158,41 @@ typedef struct gdn_problem {
   int32_t first_chunk_frames; /* GDN_CHUNK_CAUSAL: frames of the first chunk (>= 1), else ignored */
   int32_t chunk_frames;       /* GDN_CHUNK_CAUSAL: frames of each later chunk (>= 1), else ignored */
   int32_t prologue;           /* GDN_PROLOGUE_* (0 = NONE) */
-  int32_t reserved[1];        /* must be zero */
+  /* Tuning of the chunked and frame-level paths (0 = the default).  They are
+   * part of the call's problem, so the plan and gdn_workspace_size() depend
+   * only on the arguments of the call; results do not depend on them beyond
+   * rounding (GDN_FLAG_* below: not at all). */
+  int32_t segment_tokens;     /* chunked path: tokens per segment, rounded up to
+                                 a multiple of 64; 0 = automatic (about five
+                                 rounds of workgroups over the compute units,
+                                 at most about 2 sqrt(T / 64) segments) */
+  int32_t chain_group;        /* chain of segment (or frame) maps: 0 = automatic
+                                 (a chain of 16 or more maps is split into groups
+                                 of about sqrt(maps / 2): the groups' maps are
+                                 composed in parallel, the group maps chained,
+                                 each group expanded from its start state); 1 =
+                                 never split; m >= 2 = groups of m maps whenever
+                                 the chain is longer than m.  Bidirectional calls
+                                 of the chunked path never split. */
+  int32_t flags;              /* GDN_FLAG_* bits, see below; 0 = default */
+  int32_t reserved[5];        /* must be zero */
 } gdn_problem;
+
+/* gdn_problem.flags.
+ * SERIAL_SCANS: a bidirectional or chunk-causal call of the chunked path runs
+ *   every kernel on the caller's stream, in order.  By default it forks part
+ *   of its work onto a second stream that the library owns (one per caller
+ *   stream, up to eight per device, created on first use with the default
+ *   priority and kept until the process ends; a call whose stream finds no
+ *   free one runs in order) and joins it back with events before its last
+ *   kernel.  Results are bit-identical either way.
+ * FORM_INVERSE: the output kernel of a forward- or backward-only call forms
+ *   each 64-token sub-chunk's triangular inverse Tm diag(beta) itself instead
+ *   of loading the one the scan's segment-map kernel formed (5 KB of fp16 per
+ *   sub-chunk and head in the workspace, allocated either way).  Results are
+ *   bit-identical (the same arithmetic on the same rows).  Two-scan calls and
+ *   calls with a single segment always form it. */
+enum { GDN_FLAG_SERIAL_SCANS = 1, GDN_FLAG_FORM_INVERSE = 2 };
 
 /* Version of this ABI (GDN_ABI_VERSION of the built library). */
 int32_t gdn_abi_version(void);
@@ -208,43 +268,6 @@ gdn_status gdn_profile_enable(int32_t on);
 gdn_status gdn_profile_reset(void);
 gdn_status gdn_profile_read(int32_t kernel, int64_t* launches, double* total_ms);
 const char* gdn_kernel_name(int32_t kernel);   /* static text; "" if unknown */
-
-/* Tuning knob of the chunked path: tokens per segment (rounded up to a
- * multiple of 64; 0 restores the automatic choice).  Process-wide; results do
- * not depend on it beyond rounding, but gdn_workspace_size() does, so size
- * the workspace after setting it.  Thread-safe. */
-void gdn_set_segment_tokens(int32_t tokens);
-
-/* Tuning knob of the chunked and frame-level paths: how the serial chain of
- * segment (or frame) maps is evaluated.  0 (default): automatic; a chain of 16
- * or more maps is split into groups of about sqrt(maps / 2): each group's maps
- * are composed in parallel, the group maps chained, then each group expanded
- * from its start state (about 2 sqrt(2 maps) serial steps instead of one per
- * map).  1: never split.  m >= 2: groups of m maps whenever the chain is
- * longer than m.  Bidirectional calls of the chunked path never split (there
- * the two scans' chains run beside the other scan's kernels).  Results differ
- * only by rounding.  Process-wide; thread-safe; gdn_workspace_size() depends
- * on it, so size the workspace after setting it. */
-void gdn_set_chain_group(int32_t maps);
-
-/* Tuning knob of the chunked path: 1 (default) lets a bidirectional call run
- * the two scans' segment maps and chains partly concurrently on a second,
- * library-owned stream; 0 runs every kernel on the call's stream, in order
- * (maps, chain, reversed outputs, forward outputs), e.g. to time kernels one
- * at a time.  Results are identical.  Process-wide; thread-safe. */
-void gdn_set_concurrent_scans(int32_t on);
-
-/* Tuning knob of the chunked path: 1 (default) lets the output kernel of a
- * forward- or backward-only call load each sub-chunk's inverse Tm diag(beta)
- * (the solve of the sub-chunk's triangular system, 5 KB of fp16 per sub-chunk
- * and head in the workspace) as the scan's segment-map kernel formed it,
- * instead of forming it again; 0 forms it in both.  Results are identical
- * either way (the same arithmetic on the same rows); the map kernel then
- * covers every segment.  Bidirectional and chunk-causal calls (whose output
- * launches store or add a partial, where loading measured slower) and calls
- * with a single segment always form it.  gdn_workspace_size() does not depend
- * on it.  Process-wide; thread-safe. */
-void gdn_set_inverse_reuse(int32_t on);
 
 /* Tokens per segment the chunked path would use for (problem, direction), or
  * 0 when the call would take the token-recurrent path.  Host only. */

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     L = G.lib()
-    assert L.gdn_abi_version() == G.ABI_VERSION == 1
+    assert L.gdn_abi_version() == G.ABI_VERSION == 2
     for s, text in enumerate(["GDN_OK", "GDN_ERR_INVALID_ARGUMENT", "GDN_ERR_UNSUPPORTED",
                               "GDN_ERR_WORKSPACE_TOO_SMALL", "GDN_ERR_HIP"]):
         assert L.gdn_status_string(s).decode() == text
@@ -51,8 +51,9 @@ def test_recurrent_workspace_is_the_bidirectional_accumulator():
 
 
 @pytest.mark.parametrize("field,value", [
-    ("abi_version", 2), ("batch", 0), ("heads", -1), ("frames", 0), ("tokens_per_frame", 0),
+    ("abi_version", 1), ("abi_version", 3), ("batch", 0), ("heads", -1), ("frames", 0), ("tokens_per_frame", 0),
     ("d_k", 20), ("d_k", 144), ("d_v", 8), ("qkv_dtype", 7), ("out_dtype", -1), ("algo", 9),
+    ("segment_tokens", -64), ("chain_group", -1), ("flags", 4), ("flags", -1),
 ])
 def test_bad_problem_fields_are_rejected(field, value):
     p = prob()
@@ -64,10 +65,11 @@ def test_bad_problem_fields_are_rejected(field, value):
 
 
 def test_reserved_and_key_scale_and_direction_checks():
-    p = prob()
-    p.reserved[0] = 1
-    with pytest.raises(G.GdnError):
-        G.workspace_size(p, "bidir")
+    for i in range(5):
+        p = prob()
+        p.reserved[i] = 1
+        with pytest.raises(G.GdnError):
+            G.workspace_size(p, "bidir")
     p = prob(key_scale=float("nan"))
     with pytest.raises(G.GdnError):
         G.workspace_size(p, "bidir")
@@ -156,8 +158,8 @@ def test_chunk_causal_validation_and_workspace():
     p32 = prob(first_chunk_frames=2, chunk_frames=1, algo="chunked", out_dtype=G.F32)
     pbf = prob(first_chunk_frames=2, chunk_frames=1, algo="chunked", out_dtype=G.BF16)
     assert G.workspace_size(pbf, "chunk_causal") == G.workspace_size(p32, "chunk_causal")
-    tm = 2 * ((300 + 63) // 64) * 5120   # the forward-only call's sub-chunk inverse blocks (5 segments)
-    assert G.workspace_size(p32, "chunk_causal") - (G.workspace_size(p32, "fwd") - tm) >= 1 * 300 * 2 * 64 * 2
+    # the forward scan's maps, states and inverse blocks, and the fp16 partial of the reversed chunks
+    assert G.workspace_size(p32, "chunk_causal") - G.workspace_size(p32, "fwd") >= 1 * 300 * 2 * 64 * 2
     assert G.workspace_size(p32, "chunk_causal") < G.workspace_size(p32, "bidir")
 
 
@@ -184,46 +186,55 @@ def test_feature_prologue_validation_and_workspace():
 
 def test_split_chain_workspace():
     """A split chain adds group maps and group start states to the workspace;
-    the knob is process-wide and restored."""
-    p = prob(frames=40, tokens_per_frame=100, algo="chunked")
-    try:
-        G.set_segment_tokens(64)
-        G.set_chain_group(1)
-        whole = G.workspace_size(p, "fwd")
-        G.set_chain_group(4)
-        split = G.workspace_size(p, "fwd")
-        bidir = G.workspace_size(p, "bidir")
-        G.set_chain_group(1)
-        assert bidir == G.workspace_size(p, "bidir")   # bidirectional chains are never split
-    finally:
-        G.set_chain_group(0)
-        G.set_segment_tokens(0)
+    the plan is part of the call's problem (no state in the library)."""
+    p = prob(frames=40, tokens_per_frame=100, algo="chunked", tuning=G.Tuning(segment_tokens=64, chain_group=1))
+    whole = G.workspace_size(p, "fwd")
+    whole_bi = G.workspace_size(p, "bidir")
+    p4 = prob(frames=40, tokens_per_frame=100, algo="chunked", tuning=G.Tuning(segment_tokens=64, chain_group=4))
+    split = G.workspace_size(p4, "fwd")
+    assert G.workspace_size(p, "fwd") == whole          # sizing leaves nothing behind
     steps = (40 * 100 + 63) // 64 - 1
     groups = (steps + 3) // 4
     extra = 1 * 2 * groups * 64 * (128 + 64) * 4
     assert split - whole == pytest.approx(extra, abs=512)
+    assert G.workspace_size(p4, "bidir") == whole_bi   # bidirectional chains are never split
+
+
+def test_tuning_context_fills_the_problem():
+    """The binding's tuning() context sets the problem's tuning fields for
+    calls inside it and restores them after; explicit Tuning wins."""
+    assert prob().segment_tokens == 0 and prob().flags == 0
+    with G.tuning(segment_tokens=512, serial_scans=True, form_inverse=True):
+        p = prob()
+        assert (p.segment_tokens, p.chain_group, p.flags) == (512, 0, 3)
+        assert prob(tuning=G.Tuning()).flags == 0
+        with G.tuning(chain_group=3):
+            assert (prob().segment_tokens, prob().chain_group) == (512, 3)
+    assert (prob().segment_tokens, prob().chain_group, prob().flags) == (0, 0, 0)
+
+
+def test_segment_plan_follows_the_problem():
+    p = prob(frames=40, tokens_per_frame=100, algo="chunked")
+    auto = G.segment_plan(p, "bidir")
+    assert auto % 64 == 0 and auto > 0
+    assert G.segment_plan(prob(frames=40, tokens_per_frame=100, algo="chunked",
+                               tuning=G.Tuning(segment_tokens=100)), "bidir") == 128
+    assert G.segment_plan(prob(algo="recurrent"), "bidir") == 0
 
 
 def test_inverse_reuse_workspace():
-    """A forward-only chunked call with more than one segment holds 5 KB of
-    fp16 inverse blocks per 64-token sub-chunk and head, whether or not their
-    reuse is switched on; a bidirectional call holds none."""
-    p = prob(frames=40, tokens_per_frame=100, algo="chunked")   # 4000 tokens: 63 sub-chunks
-    try:
-        G.set_chain_group(1)
-        G.set_segment_tokens(4096)      # one segment: no maps, no inverse blocks
-        one = G.workspace_size(p, "fwd")
-        one_bi = G.workspace_size(p, "bidir")
-        G.set_segment_tokens(512)       # 8 segments
-        on = G.workspace_size(p, "fwd")
-        on_bi = G.workspace_size(p, "bidir")
-        G.set_inverse_reuse(False)
-        assert G.workspace_size(p, "fwd") == on
-    finally:
-        G.set_inverse_reuse(True)
-        G.set_chain_group(0)
-        G.set_segment_tokens(0)
+    """A chunked call with more than one segment holds 5 KB of fp16 inverse
+    blocks per 64-token sub-chunk, head and scan with maps (both scans of a
+    bidirectional call), whether or not the output kernels load them."""
+    def p_(seg, form=False):   # 4000 tokens: 63 sub-chunks
+        return prob(frames=40, tokens_per_frame=100, algo="chunked",
+                    tuning=G.Tuning(segment_tokens=seg, chain_group=1, form_inverse=form))
+    one = G.workspace_size(p_(4096), "fwd")      # one segment: no maps, no inverse blocks
+    one_bi = G.workspace_size(p_(4096), "bidir")
+    on = G.workspace_size(p_(512), "fwd")        # 8 segments
+    on_bi = G.workspace_size(p_(512), "bidir")
+    assert G.workspace_size(p_(512, form=True), "fwd") == on
     per_seg = 2 * 64 * (128 + 64) * 4           # one scan's map and start state, 2 heads
     tm = 2 * 63 * 5120
     assert on - one == pytest.approx(7 * per_seg + tm, abs=1024)
-    assert on_bi - one_bi == pytest.approx(2 * 7 * per_seg, abs=1024)
+    assert on_bi - one_bi == pytest.approx(2 * 7 * per_seg + 2 * tm, abs=1024)

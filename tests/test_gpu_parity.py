@@ -148,16 +148,11 @@ def test_concurrent_scans_match_in_order_schedule(name, seg):
     7, 14, 7 and 3 segments, batch 2 with an initial state, a ragged tail."""
     w = SMALL[name]
     x = make_inputs(w, 5)
-    G.set_segment_tokens(seg)
-    try:
-        G.set_concurrent_scans(False)
-        a = run_gpu(w, x, "bidir", "chunked")
-        G.set_concurrent_scans(True)
+    with G.tuning(segment_tokens=seg):
+        with G.tuning(serial_scans=True):
+            a = run_gpu(w, x, "bidir", "chunked")
         b = run_gpu(w, x, "bidir", "chunked")
         c = run_gpu(w, x, "bidir", "chunked")
-    finally:
-        G.set_concurrent_scans(True)
-        G.set_segment_tokens(0)
     for u, v in ((a, b), (a, c)):
         assert np.array_equal(u[0], v[0]) and np.array_equal(u[1], v[1])
     ro, rH = O.bidir(*oracle_args(x)[0], x["h0"])
@@ -182,15 +177,10 @@ def test_inverse_reuse_is_bit_identical(direction, prologue):
             return run_pro(w, x, direction, c, algo="chunked")
         return run_gpu(w, x, direction, "chunked")
 
-    G.set_segment_tokens(192)
-    try:
-        G.set_inverse_reuse(False)
-        a = run()
-        G.set_inverse_reuse(True)
+    with G.tuning(segment_tokens=192):
+        with G.tuning(form_inverse=True):
+            a = run()
         b = run()
-    finally:
-        G.set_inverse_reuse(True)
-        G.set_segment_tokens(0)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
     args = features(x) if prologue else list(oracle_args(x)[0])
     ro, rH = O.forward(direction, *args, x["h0"], key_scale=c)
@@ -212,11 +202,8 @@ def test_chunked_every_head_width(d, direction):
     maps, the chain and the outputs of every width are exercised."""
     w = WORKLOADS[4].resized(frames=2, tokens_per_frame=150, heads=3, d_k=d, d_v=d)
     x = make_inputs(w, 40 + d)
-    G.set_segment_tokens(128)
-    try:
+    with G.tuning(segment_tokens=128):
         check(w, x, direction, "chunked")
-    finally:
-        G.set_segment_tokens(0)
 
 
 @pytest.mark.parametrize("d", DIMS)
@@ -252,12 +239,9 @@ def test_many_segments_and_heads():
     B = 3, H = 7, 4 frames of 97 tokens (388 tokens, 7 segments)."""
     w = WORKLOADS[4].resized(batch=3, heads=7, frames=4, tokens_per_frame=97)
     x = make_inputs(w, 80)
-    G.set_segment_tokens(64)
-    try:
+    with G.tuning(segment_tokens=64):
         for direction in ("fwd", "bidir"):
             check(w, x, direction, "chunked")
-    finally:
-        G.set_segment_tokens(0)
 
 
 # ---------------------------------------------------------------- degenerate sizes
@@ -316,16 +300,11 @@ def test_split_chain_chunked(group, direction):
     600 tokens in segments of 64 (10 segments, 9 chain steps)."""
     w = WORKLOADS[4].resized(frames=4, tokens_per_frame=150, heads=3)
     x = make_inputs(w, 90 + group)
-    G.set_segment_tokens(64)
-    try:
-        G.set_chain_group(1)
+    with G.tuning(segment_tokens=64, chain_group=1):
         whole = run_gpu(w, x, direction, "chunked")
-        G.set_chain_group(group)
+    with G.tuning(segment_tokens=64, chain_group=group):
         split = check(w, x, direction, "chunked")
         o, hT = run_gpu(w, x, direction, "chunked")
-    finally:
-        G.set_chain_group(0)
-        G.set_segment_tokens(0)
     # both are within the bar of the oracle; between them only the chain's
     # rounding differs (start states feed the output kernel's fp16 operands,
     # so a flipped fp16 rounding of a state element shows at ~2^-11 relative)
@@ -336,11 +315,8 @@ def test_split_chain_chunked(group, direction):
 def test_split_chain_jacobi(group):
     w = WORKLOADS[4].resized(frames=11, tokens_per_frame=40, heads=2)
     x = make_inputs(w, 95)
-    G.set_chain_group(group)
-    try:
+    with G.tuning(chain_group=group):
         o, hT = run_jacobi(w, x, "bidir")
-    finally:
-        G.set_chain_group(0)
     ro, rH = O.jacobi_bidir(*oracle_args(x)[0], x["h0"], key_scale=w.tokens_per_frame ** -0.5,
                             tokens_per_frame=w.tokens_per_frame)
     assert rel_err(o, ro) <= TOL["bf16"] and rel_err(hT, rH) <= TOL["bf16"]
@@ -349,13 +325,8 @@ def test_split_chain_jacobi(group):
 def test_split_chain_chunk_causal():
     w = WORKLOADS[4].resized(frames=6, tokens_per_frame=100, heads=2)
     x = make_inputs(w, 96)
-    G.set_segment_tokens(64)
-    G.set_chain_group(3)
-    try:
+    with G.tuning(segment_tokens=64, chain_group=3):
         o, hT = run_cc(w, x, 2, 2, "chunked")
-    finally:
-        G.set_chain_group(0)
-        G.set_segment_tokens(0)
     ro, rH = O.chunk_causal(*oracle_args(x)[0], x["h0"], tokens_per_frame=w.tokens_per_frame,
                             first_chunk_frames=2, chunk_frames=2)
     assert rel_err(o, ro) <= TOL["bf16"] and rel_err(hT, rH) <= TOL["bf16"]
@@ -409,14 +380,10 @@ def test_chunk_causal_bf16_output_and_schedules():
     schedules give bit-identical results."""
     w, first, every = CC["clip60s_4_3"]
     x = make_inputs(w, 13)
-    G.set_segment_tokens(512)
-    try:
+    with G.tuning(segment_tokens=512):
         a = run_cc(w, x, first, every, "chunked", out_dtype=torch.bfloat16)
-        G.set_concurrent_scans(False)
-        b = run_cc(w, x, first, every, "chunked", out_dtype=torch.bfloat16)
-    finally:
-        G.set_concurrent_scans(True)
-        G.set_segment_tokens(0)
+        with G.tuning(serial_scans=True):
+            b = run_cc(w, x, first, every, "chunked", out_dtype=torch.bfloat16)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
     ro, rH = O.chunk_causal(*oracle_args(x)[0], x["h0"], tokens_per_frame=w.tokens_per_frame,
                             first_chunk_frames=first, chunk_frames=every)
@@ -606,7 +573,8 @@ def test_feature_prologue_is_invariant_to_token_magnitudes():
     assert rel_err(a[0], b[0]) <= 5e-3 and rel_err(a[1], b[1]) <= 5e-3
 
 
-FULL = [(1, "bidir", [0, 19]), (2, "bidir", [7]), (2, "fwd", [13]), (4, "bidir", [(0, 3), (1, 34)])]
+FULL = [(1, "bidir", [0, 19]), (1, "fwd", [5]), (2, "bidir", [7]), (2, "fwd", [13]),
+        (4, "bidir", [(0, 3), (1, 34)]), (4, "fwd", [(1, 20)])]
 
 
 @pytest.mark.slow
@@ -645,3 +613,91 @@ def test_full_size_feature_prologue_sampled_head():
     eo, eh = rel_err(o[:, :, h:h + 1], ro), rel_err(hT[:, h:h + 1], rH)
     print(f"[parity-full] {w.name} prologue bidir h{h}: out {eo:.3e} state {eh:.3e}", flush=True)
     assert eo <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
+@pytest.mark.slow
+def test_full_size_stream_121_steps_sampled_heads():
+    """The chunk-causal streaming workload at full size: 121 gdn_step calls of
+    one 880-token frame each on 20 heads x 112 with the long-memory gates, the
+    fp32 state carried in place between calls, in the launch configuration the
+    bench times.  Two sampled heads' outputs (all 106,480 tokens) and final
+    states against the oracle's forward scan over the whole sequence."""
+    w = WORKLOADS[3]
+    x = make_inputs(w, 0)
+    d = to_device(x, w.qkv_dtype)
+    S = w.tokens_per_frame
+    state = torch.zeros((w.batch, w.heads, w.d_k, w.d_v), dtype=torch.float32, device="cuda")
+    out = torch.empty((w.batch, w.tokens, w.heads, w.d_v), dtype=torch.float32, device="cuda")
+    for f in range(w.frames):
+        sl = slice(f * S, (f + 1) * S)
+        G.step(*(d[n][:, sl] for n in ("q", "k", "v", "log_gate", "beta")), state, state, out=out[:, sl])
+    torch.cuda.synchronize()
+    o, hT = to_numpy(out), to_numpy(state)
+    for h in (4, 17):
+        a = [t[:, :, h:h + 1] for t in (x["q"], x["k"], x["v"], x["log_gate"], x["beta"])]
+        ro, rH = O.fwd(*a, x["h0"][:, h:h + 1])
+        eo, eh = rel_err(o[:, :, h:h + 1], ro), rel_err(hT[:, h:h + 1], rH)
+        print(f"[parity-full] {w.name} 121 steps h{h}: out {eo:.3e} state {eh:.3e}", flush=True)
+        assert eo <= TOL["bf16"] and eh <= TOL["bf16"], (h, eo, eh)
+
+
+def test_chunked_at_the_edge_of_its_fp16_domain():
+    """The chunked path's documented range: values scaled by 2^11 (exact in
+    bf16) so that outputs reach about 1e4 and the fp16 partial of the
+    bidirectional sum about that too; the relative error is that of the
+    unscaled inputs (the layer is linear in v and the initial state)."""
+    w = SMALL["batched"]
+    x = make_inputs(w, 120)
+    x["v"] = x["v"] * 2.0 ** 11
+    x["h0"] = x["h0"] * 2.0 ** 11
+    with G.tuning(segment_tokens=192):
+        o, hT = run_gpu(w, x, "bidir", "chunked")
+    ro, rH = O.bidir(*oracle_args(x)[0], x["h0"])
+    assert 4e3 < np.max(np.abs(ro)) < 3e4, np.max(np.abs(ro))
+    eo, eh = rel_err(o, ro), rel_err(hT, rH)
+    print(f"[parity] fp16 domain edge: max|out| {np.max(np.abs(ro)):.3g}, out {eo:.3e} state {eh:.3e}", flush=True)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(hT))
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"], (eo, eh)
+
+
+@pytest.mark.parametrize("direction", ["fwd", "bidir"])
+def test_recurrent_takes_bf16_values_beyond_fp16(direction):
+    """Values past fp16's range (v scaled by 2^17, so |v| reaches about 5e5):
+    the token-recurrent path computes in fp32 throughout and stays within the
+    bf16 bar."""
+    w = SMALL["clip5s"]
+    x = make_inputs(w, 121)
+    x["v"] = x["v"] * 2.0 ** 17
+    assert np.max(np.abs(x["v"])) > 65504
+    o, hT = run_gpu(w, x, direction, "recurrent")
+    ro, rH = O.forward(direction, *oracle_args(x)[0], x["h0"])
+    eo, eh = rel_err(o, ro), rel_err(hT, rH)
+    print(f"[parity] beyond fp16 {direction}: max|v| {np.max(np.abs(x['v'])):.3g}, out {eo:.3e} state {eh:.3e}",
+          flush=True)
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"], (eo, eh)
+
+
+def test_binding_checks_out_and_workspace():
+    """A supplied ``out`` sets the output dtype (bf16 here: the fp32 result
+    rounded once); a wrong shape, a dtype that contradicts ``out_dtype``, or a
+    workspace on another device raise before anything is enqueued."""
+    w = SMALL["clip60s"]
+    x = make_inputs(w, 122)
+    d = to_device(x, w.qkv_dtype)
+    args = [d[n] for n in ("q", "k", "v", "log_gate", "beta")]
+    kw = dict(tokens_per_frame=w.tokens_per_frame)
+    ref, _ = G.forward(*args, None, "bidir", **kw)
+    out = torch.empty(ref.shape, dtype=torch.bfloat16, device="cuda")
+    o, _ = G.forward(*args, None, "bidir", out=out, **kw)
+    torch.cuda.synchronize()
+    assert o is out and o.dtype == torch.bfloat16
+    assert torch.equal(o, ref.to(torch.bfloat16))
+    with pytest.raises(ValueError):
+        G.forward(*args, None, "bidir", out=torch.empty(ref.shape[:-1] + (8,), device="cuda"), **kw)
+    with pytest.raises(TypeError):
+        G.forward(*args, None, "bidir", out=out, out_dtype=torch.float32, **kw)
+    with pytest.raises(ValueError):
+        G.forward(*args, None, "bidir", workspace=torch.empty(1 << 20, dtype=torch.uint8), **kw)
+    with pytest.raises(ValueError):
+        G.forward(*args, None, "bidir", out=torch.empty(ref.shape, device="cuda").transpose(1, 2).contiguous()
+                  .transpose(1, 2), **kw)
