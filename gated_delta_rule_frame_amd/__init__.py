@@ -17,7 +17,7 @@ import ctypes
 import dataclasses
 import os
 
-__all__ = ["forward", "step", "workspace_size", "make_problem", "lib", "GdnError", "Tuning", "tuning",
+__all__ = ["forward", "step", "step_noalloc", "workspace_size", "NOALLOC_SCRATCH_BYTES", "make_problem", "lib", "GdnError", "Tuning", "tuning",
            "segment_plan", "profile_enable", "profile_reset", "profile_read",
            "FORWARD", "BACKWARD", "BIDIRECTIONAL", "CHUNK_CAUSAL", "ABI_VERSION", "LIB_PATH"]
 
@@ -31,6 +31,7 @@ ALGO = {"auto": 0, "chunked": 1, "recurrent": 2}
 INTRA = {"sequential": 0, "jacobi": 1}
 PROLOGUE = {"none": 0, "features": 1}
 FLAG_SERIAL_SCANS, FLAG_FORM_INVERSE = 1, 2
+NOALLOC_SCRATCH_BYTES = 64 << 20   # GDN_NOALLOC_SCRATCH_BYTES
 DIRECTION = {"fwd": FORWARD, "bwd": BACKWARD, "bidir": BIDIRECTIONAL, "chunk_causal": CHUNK_CAUSAL,
              FORWARD: FORWARD, BACKWARD: BACKWARD, BIDIRECTIONAL: BIDIRECTIONAL, CHUNK_CAUSAL: CHUNK_CAUSAL}
 
@@ -118,6 +119,8 @@ def lib():
         L.gdn_plan_segment_tokens.argtypes = [P, i32, ctypes.POINTER(i32)]
         L.gdn_step.restype = i32
         L.gdn_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.gdn_step_noalloc.restype = i32
+        L.gdn_step_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         if L.gdn_abi_version() != ABI_VERSION:
             raise ImportError(f"libgdn ABI {L.gdn_abi_version()} != binding ABI {ABI_VERSION}")
         _lib = L
@@ -329,4 +332,26 @@ def step(q, k, v, log_gate, beta, state_in=None, state_out=None, *, key_scale=1.
     _check(lib().gdn_step(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(log_gate), _ptr(beta),
                           _ptr(state_in), _ptr(state_out), _ptr(out), _ptr(ws), ws_bytes,
                           ctypes.c_void_p(stream)))
+    return out, state_out
+
+
+def step_noalloc(q, k, v, log_gate, beta, state_in=None, state_out=None, *, key_scale=1.0,
+                 out_dtype=None, algo="auto", out=None, intra="sequential", prologue="none", tuning=None):
+    """gdn_step_noalloc: one frame like ``step`` with the library's static device
+    scratch in place of a workspace; returns (out, state_out).  The library
+    allocates nothing; pass ``out`` and ``state_out`` to keep this call free of
+    torch allocations too."""
+    torch = _torch()
+    p, (B, T, H, dk, dv), odt = _prepare(q, k, v, log_gate, beta, 1, None, out, out_dtype, algo,
+                                         key_scale, intra, (0, 0), prologue, tuning)
+    shape = (B, H, dk, dv)
+    state_in = _state_tensor(state_in, shape, "state_in", q.device)
+    if state_out is None:
+        state_out = torch.empty(shape, dtype=torch.float32, device=q.device)
+    state_out = _state_tensor(state_out, shape, "state_out", q.device)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=odt, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(lib().gdn_step_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(log_gate), _ptr(beta),
+                                  _ptr(state_in), _ptr(state_out), _ptr(out), ctypes.c_void_p(stream)))
     return out, state_out

@@ -226,4 +226,36 @@ gdn_status gdn_step(const gdn_problem* pr, const void* q, const void* k, const v
   }
 }
 
+gdn_status gdn_step_noalloc(const gdn_problem* pr, const void* q, const void* k, const void* v,
+                            const float* log_gate, const float* beta, const float* state_in,
+                            float* state_out, void* out, void* stream) {
+  try {
+    if (pr && pr->frames != 1)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "gdn_step_noalloc takes exactly one frame (frames = %d)",
+                  pr->frames);
+    if (!state_out) return fail(GDN_ERR_INVALID_ARGUMENT, "state_out must be non-NULL");
+    // size the step on the host first: an oversized one is rejected before any HIP call
+    gdn::Problem p;
+    gdn_status s = check_problem(pr, GDN_FORWARD, &p);
+    if (s != GDN_OK) return s;
+    Path path;
+    s = choose_path(pr, p, &path);
+    if (s != GDN_OK) return s;
+    const size_t need = workspace_for(path, p, GDN_FORWARD);
+    if (need > (size_t)GDN_NOALLOC_SCRATCH_BYTES)
+      return fail(GDN_ERR_WORKSPACE_TOO_SMALL,
+                  "gdn_step_noalloc: this step needs %zu bytes of scratch, the library's static scratch "
+                  "holds %zu; call gdn_step with a workspace instead", need, (size_t)GDN_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if (need > 0) {
+      const hipError_t e = gdn::noalloc_scratch(&ws);
+      if (e != hipSuccess) return fail(GDN_ERR_HIP, "HIP error taking the scratch address: %s", hipGetErrorString(e));
+    }
+    gdn::Tensors t{q, k, v, log_gate, beta, state_in, out, state_out};
+    return run(pr, GDN_FORWARD, t, ws, need, stream);
+  } catch (...) {
+    return fail(GDN_ERR_HIP, "internal error while enqueueing");
+  }
+}
+
 }  // extern "C"

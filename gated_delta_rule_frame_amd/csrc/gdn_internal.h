@@ -65,6 +65,11 @@ hipError_t prologue_launch(const Problem& p, const Tensors& t, float* fac, hipSt
 
 int chunked_segment_tokens(const Problem& p, int direction);
 
+// Device address of the allocation-free step's scratch array on the current
+// device (gdn_noalloc.hip; GDN_NOALLOC_SCRATCH_BYTES bytes, 256-byte aligned),
+// taken once per device.
+hipError_t noalloc_scratch(void** ptr);
+
 // Kernel timing hooks (gdn_profile.cpp): no-ops unless profiling is enabled.
 void prof_begin(hipStream_t stream, int kernel);
 void prof_end(hipStream_t stream, int kernel);

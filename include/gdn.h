@@ -249,6 +249,27 @@ gdn_status gdn_step(const gdn_problem* problem,
                     void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/* Allocation-free variant of gdn_step, for callers that cannot allocate
+ * device memory or hand over a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Arguments, results and
+ * kernels are gdn_step's; in place of a workspace it uses a scratch array of
+ * GDN_NOALLOC_SCRATCH_BYTES that is part of the library's code object (each
+ * device the library runs on holds its own copy until the process ends; the
+ * first call on a device takes the copy's address).  It allocates nothing.
+ *   GDN_ERR_WORKSPACE_TOO_SMALL, with nothing enqueued, when the step's
+ *   gdn_workspace_size(problem, GDN_FORWARD) exceeds the scratch (one
+ *   880-token frame of 20 heads x 112 needs about 23 MB).
+ * Every call on a device shares that device's scratch, which keeps the last
+ * call's contents (nothing in it has to start at zero): calls that overlap on
+ * one device (different streams, or threads without ordering) race on it and
+ * must be serialised by the caller; calls on one stream are ordered. */
+#define GDN_NOALLOC_SCRATCH_BYTES (64u << 20)
+gdn_status gdn_step_noalloc(const gdn_problem* problem,
+                            const void* q, const void* k, const void* v,
+                            const float* log_gate, const float* beta,
+                            const float* state_in, float* state_out,
+                            void* out, void* stream);
+
 /* Kernel timing (diagnostics).  While enabled, every kernel launch made by
  * libgdn is bracketed by two HIP events recorded on the call's stream;
  * gdn_profile_read() waits for the recorded events and returns, per kernel,

@@ -238,3 +238,25 @@ def test_inverse_reuse_workspace():
     tm = 2 * 63 * 5120
     assert on - one == pytest.approx(7 * per_seg + tm, abs=1024)
     assert on_bi - one_bi == pytest.approx(2 * 7 * per_seg + 2 * tm, abs=1024)
+
+
+def test_step_noalloc_rejects_oversized_steps_before_any_hip_call():
+    """gdn_step_noalloc sizes the step on the host: one frame whose workspace
+    exceeds the static scratch returns WORKSPACE_TOO_SMALL with nothing
+    enqueued (fake pointers, no GPU); frames != 1 and a NULL state_out are
+    argument errors as for gdn_step."""
+    L = G.lib()
+    vp = ctypes.c_void_p
+    big = prob(batch=8, heads=64, d_k=112, d_v=112, frames=1, tokens_per_frame=60000, algo="chunked")
+    assert G.workspace_size(big, "fwd") > G.NOALLOC_SCRATCH_BYTES
+    args = [vp(FAKE)] * 5
+    assert L.gdn_step_noalloc(ctypes.byref(big), *args, None, vp(FAKE), vp(FAKE), None) \
+        == G.ERR_WORKSPACE_TOO_SMALL
+    assert "static scratch" in L.gdn_last_error_message().decode()
+    two = prob(frames=2, algo="chunked")
+    assert L.gdn_step_noalloc(ctypes.byref(two), *args, None, vp(FAKE), vp(FAKE), None) == G.ERR_INVALID_ARGUMENT
+    one = prob(frames=1, algo="chunked")
+    assert L.gdn_step_noalloc(ctypes.byref(one), *args, None, None, vp(FAKE), None) == G.ERR_INVALID_ARGUMENT
+    # one 880-token frame of 20 heads x 112 fits
+    frame = prob(heads=20, d_k=112, d_v=112, frames=1, tokens_per_frame=880, algo="chunked")
+    assert 0 < G.workspace_size(frame, "fwd") <= G.NOALLOC_SCRATCH_BYTES
