@@ -37,8 +37,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{IN
 # not know the feature; that warning is harmless).  (LLVM's option to force
 # MFMA accumulators into architectural VGPRs is deliberately not used: with
 # this toolchain it produced wrong results on gfx950.)
-DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-munsafe-fp-atomics"]
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
 def _run(cmd):
