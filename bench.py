@@ -27,6 +27,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import dataclasses
 import hashlib
 import json
 import os
@@ -321,7 +322,7 @@ class Run:
                     key_scale=self.key_scale, out=self.outs[f], workspace=self.ws, prologue=self.prologue,
                     tuning=self.tuning)
 
-    def step(self):
+    def step(self, tuning=None):
         if self.stream_mode:
             if self.h0 is None:
                 self.hT.zero_()
@@ -335,7 +336,7 @@ class Run:
                        tokens_per_frame=self.w.tokens_per_frame, out=self.out, final_state=self.hT,
                        workspace=self.ws, key_scale=self.key_scale, intra=self.intra,
                        first_chunk_frames=self.chunks[0], chunk_frames=self.chunks[1], prologue=self.prologue,
-                       tuning=self.tuning)
+                       tuning=tuning or self.tuning)
 
     def kind(self):
         return ("fwd" if self.stream_mode else self.direction, self.intra, self.prologue == "features")
@@ -370,14 +371,14 @@ class Run:
         return res, secs
 
 
-def time_steps(torch, run, steps, warmup):
+def time_steps(torch, run, steps, warmup, tuning=None):
     for _ in range(warmup):
-        run.step()
+        run.step(tuning)
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
     for _ in range(steps):
-        run.step()
+        run.step(tuning)
     ev1.record()
     torch.cuda.synchronize()
     return ev0.elapsed_time(ev1) / steps
@@ -467,14 +468,24 @@ def measure(G, torch, run, steps, warmup, peak_tflops, tag):
     B, T, H, dk, dv = w.batch, w.tokens, w.heads, w.d_k, w.d_v
     ndir = 2 if run.direction in ("bidir", "chunk_causal") else 1
     ms = time_steps(torch, run, steps, warmup)
-    # per-kernel durations: HIP events recorded by the library on each kernel's stream
-    G.profile_reset()
-    G.profile_enable(True)
-    time_steps(torch, run, max(3, steps // 2), 0)
-    G.profile_enable(False)
-    prof = G.profile_read()
+    # Per-kernel durations: HIP events recorded by the library on each
+    # kernel's stream.  "kernels": each kernel alone (the in-order schedule of
+    # the same call), the figures the roofline uses; "kernels_in_schedule":
+    # in the timed schedule, where a two-scan call runs kernels of both scans
+    # side by side and each duration includes the sharing.
     psteps = max(3, steps // 2)
-    kern = {k: {"launches_per_step": n / psteps, "avg_ms": t / n} for k, (n, t) in prof.items() if n}
+
+    def kernel_times(tuning):
+        G.profile_reset()
+        G.profile_enable(True)
+        time_steps(torch, run, psteps, 1, tuning)
+        G.profile_enable(False)
+        prof = G.profile_read()
+        return {k: {"launches_per_step": n / (psteps + 1), "avg_ms": t / n} for k, (n, t) in prof.items() if n}
+
+    shared = kernel_times(None)
+    serial = dataclasses.replace(run.tuning, serial_scans=True)
+    kern = kernel_times(serial) if serial != run.tuning and run.direction in ("bidir", "chunk_causal") else shared
     own, own_mt, fl, alg_out = flops_of(run, B, H, dk, dv, T, ndir)
     for k, v in fl.items():
         if k in kern:
@@ -504,6 +515,7 @@ def measure(G, torch, run, steps, warmup, peak_tflops, tag):
             "frac": hbm_step / (ms / 1e3) / 1e9 / PEAK_HBM_GBS,
             "source": f"profiles/<kernel>_{tag}_counters.json (rocprofv3 FETCH_SIZE, WRITE_SIZE)"},
         "kernels": kern,
+        "kernels_in_schedule": shared if shared is not kern else None,
     }
     return res, alg_out
 

@@ -1617,7 +1617,6 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
   {
     const int dir = a.dir;
     const bool rev = dir == 1;
-    const int mode = a.mode;
     const int slot = slot_of_dir(a.dirs, dir);
     const int pos = rev ? a.NS - 1 - seg : seg;
     f32x4 H[SPW][MD];
@@ -1711,15 +1710,19 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
     // may not have been issued and wait for later stores where it waits for
     // earlier loads): 0 fp32 outputs, 1 bf16 outputs, 2 the fp16 partial of
     // mode 1 (half the bytes of fp32 each way; it adds a rounding of 2^-11 of
-    // the partial's magnitude to the sum).
+    // the partial's magnitude to the sum), 3 and 4: fp32 and bf16 outputs
+    // with the partial added (mode 2; only these load it).
+    constexpr bool ADD = ST >= 3;
+    constexpr int SO = ADD ? ST - 3 : ST;
     typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-    const long long esz = ST == 0 ? 4 : 2;
-    char* const dstb = static_cast<char*>(ST == 2 ? static_cast<void*>(a.part) : a.out);
+    const long long esz = SO == 0 ? 4 : 2;
+    char* const dstb = static_cast<char*>(SO == 2 ? static_cast<void*>(a.part) : a.out);
     u32x2_t pre[4] = {u32x2_t{0u, 0u}, u32x2_t{0u, 0u}, u32x2_t{0u, 0u}, u32x2_t{0u, 0u}};   // fp16 partial
     auto rows_of = [&](int c) { return ((long long)b * a.T + piece(c).t0) * HD + (long long)h * D; };
     auto load_pre = [&](int c) {
+      if constexpr (!ADD) return;
       const Sub sb = piece(c);
-      const __amdgpu_buffer_rsrc_t rs = rows_rsrc(a.part + rows_of(c), mode == 2 ? (long long)sb.n * HD * 2 : 0);
+      const __amdgpu_buffer_rsrc_t rs = rows_rsrc(a.part + rows_of(c), (long long)sb.n * HD * 2);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int k = t + NTS * i, row = k / C4, c4 = k % C4;
@@ -1745,13 +1748,14 @@ __global__ __launch_bounds__(Geo<D>::NT) void seg_out_kernel(Args a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int k = t + NTS * i, row = k / C4, c4 = k % C4;
-        const f32x4 val = ld4f(I.os + row * L::OSL + 4 * c4) + pre_f32(pre[i]);
+        f32x4 val = ld4f(I.os + row * L::OSL + 4 * c4);
+        if constexpr (ADD) val = val + pre_f32(pre[i]);
         const uint32_t off = (uint32_t)(((sb.r0 + sb.sgn * row) * (int)HD + 4 * c4) * esz);
-        if constexpr (ST == 1) {
+        if constexpr (SO == 1) {
           const u32x2_t w{f32_to_bf16_bits(val[0]) | ((uint32_t)f32_to_bf16_bits(val[1]) << 16),
                           f32_to_bf16_bits(val[2]) | ((uint32_t)f32_to_bf16_bits(val[3]) << 16)};
           __builtin_amdgcn_raw_buffer_store_b64(w, rs, off, 0, 0);
-        } else if constexpr (ST == 2) {
+        } else if constexpr (SO == 2) {
           const u32x2_t w{(uint32_t)f2h(val[0]) | ((uint32_t)f2h(val[1]) << 16),
                           (uint32_t)f2h(val[2]) | ((uint32_t)f2h(val[3]) << 16)};
           __builtin_amdgcn_raw_buffer_store_b64(w, rs, off, 0, 0);
@@ -2167,12 +2171,11 @@ Plan make_plan(const Problem& p, int direction) {
   if (pl.dirs != 3) pl.cw = chain_ws(pl.NS - 1, p.chain_group, bhd, p.dk, p.dv);
   pl.gmaps_off = pl.fac_off + align_up(prologue_bytes(p), 256);
   pl.gstarts_off = pl.gmaps_off + pl.cw.gmaps_bytes;
-  // Tm blocks of every sub-chunk of each scan with maps (fp16, 5 KB per
-  // sub-chunk and head), whether or not the output kernels load them: both
-  // scans of a bidirectional call, the forward scan of a chunk-causal one
+  // Tm blocks of every sub-chunk of a forward- or backward-only call with
+  // maps (fp16, 5 KB per sub-chunk), whether or not the output kernel loads
+  // them (two-scan calls form them in both kernels: see launch_d)
   const size_t U = (size_t)((p.T + CH - 1) / CH);
-  const size_t tm_slots = pl.NS >= 2 ? (pl.cc ? 1 : (size_t)pl.ndir) : 0;
-  pl.tm_bytes = tm_slots ? align_up(tm_slots * p.B * p.H * U * kTmElems * 2, 256) : 0;
+  pl.tm_bytes = pl.NS >= 2 && pl.dirs != 3 && !pl.cc ? align_up(bhd * U * kTmElems * 2, 256) : 0;
   pl.tm_off = pl.gstarts_off + pl.cw.gstarts_bytes;
   pl.bytes = pl.tm_off + pl.tm_bytes;
   return pl;
@@ -2286,11 +2289,12 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
   a.gmaps = reinterpret_cast<float*>(ws + pl.gmaps_off);
   a.gstarts = reinterpret_cast<float*>(ws + pl.gstarts_off);
   const bool both = pl.dirs == 3;
-  // The output kernels load the map kernels' Tm blocks (the wide-strip
-  // kernel has no wavefront to spare for the inverse).  With the feature
-  // prologue, two-scan calls form them in the output kernels (the Q-only map
-  // kernel's prologue variant stores none: see seg_map_body).
-  a.tm = pl.tm_bytes && p.tm_reuse && (!PRO || (!both && !pl.cc)) ? reinterpret_cast<hb*>(ws + pl.tm_off) : nullptr;
+  // Reuse of the map kernel's Tm blocks by the output kernel: forward- and
+  // backward-only calls (measured at the 60 s clip, output kernel alone:
+  // 0.613 -> 0.590 ms for a forward call).  Two-scan calls form their own:
+  // loading them there measured no faster (bidirectional 2.19 against 2.17 ms
+  // per step) and would move 0.67 GB more per step through HBM.
+  a.tm = pl.tm_bytes && p.tm_reuse ? reinterpret_cast<hb*>(ws + pl.tm_off) : nullptr;
   const unsigned bhc = (unsigned)(p.B * p.H);
   // Workgroups are dealt to the 8 XCDs (each with its own L2) in turn.  With
   // the segment index padded to a multiple of 8, a segment of neighbouring
@@ -2339,19 +2343,23 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
   };
   // One output launch (x.mode and x.out_bf16 select the store type).
   // x.tm: load the map kernel's Tm blocks.
+  // (Loaded Tm blocks only occur in single-scan calls, mode 0.)
   auto launch_out = [&](const Args& x, unsigned gx, hipStream_t st) {
     const dim3 grid(gx, bhc, 1), block(Geo<D>::NT);
     if (x.tm) {
-      if (x.mode == 1)
-        hipLaunchKernelGGL((seg_out_kernel<D, PRO, 2, true>), grid, block, 0, st, x);
-      else if (x.out_bf16)
+      if (x.out_bf16)
         hipLaunchKernelGGL((seg_out_kernel<D, PRO, 1, true>), grid, block, 0, st, x);
       else
         hipLaunchKernelGGL((seg_out_kernel<D, PRO, 0, true>), grid, block, 0, st, x);
+    } else if (x.mode == 1) {
+      hipLaunchKernelGGL((seg_out_kernel<D, PRO, 2, false>), grid, block, 0, st, x);
+    } else if (x.mode == 2) {
+      if (x.out_bf16)
+        hipLaunchKernelGGL((seg_out_kernel<D, PRO, 4, false>), grid, block, 0, st, x);
+      else
+        hipLaunchKernelGGL((seg_out_kernel<D, PRO, 3, false>), grid, block, 0, st, x);
     } else {
-      if (x.mode == 1)
-        hipLaunchKernelGGL((seg_out_kernel<D, PRO, 2, false>), grid, block, 0, st, x);
-      else if (x.out_bf16)
+      if (x.out_bf16)
         hipLaunchKernelGGL((seg_out_kernel<D, PRO, 1, false>), grid, block, 0, st, x);
       else
         hipLaunchKernelGGL((seg_out_kernel<D, PRO, 0, false>), grid, block, 0, st, x);
