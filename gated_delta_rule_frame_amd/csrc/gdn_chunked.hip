@@ -2127,6 +2127,16 @@ struct Plan {
   size_t maps_off, starts_off, acc_off, fac_off, gmaps_off, gstarts_off, tm_off, tm_bytes, bytes;
 };
 
+// Whether the output kernels of a two-scan call load the map kernels' Tm
+// blocks instead of forming them.  At d_k <= 64 the helper wavefront's
+// triangular inverse, the same work at every width, is the longest step of an
+// output sub-chunk (the batched 2 x 35 x 64 workload, bidirectional: output
+// launches 1.78 -> 1.36 ms, 6.43 -> 5.57 ms a step); at d_k = 112 the strips
+// are, and loading measured no faster while moving 0.67 GB more per step
+// through HBM.  The feature prologue's Q-only map kernel stores none (see
+// seg_map_body).
+bool tm_two_scan(const Problem& p) { return p.dk <= 64 && !p.prologue; }
+
 Plan make_plan(const Problem& p, int direction) {
   Plan pl{};
   pl.cc = direction == GDN_CHUNK_CAUSAL;
@@ -2171,11 +2181,15 @@ Plan make_plan(const Problem& p, int direction) {
   if (pl.dirs != 3) pl.cw = chain_ws(pl.NS - 1, p.chain_group, bhd, p.dk, p.dv);
   pl.gmaps_off = pl.fac_off + align_up(prologue_bytes(p), 256);
   pl.gstarts_off = pl.gmaps_off + pl.cw.gmaps_bytes;
-  // Tm blocks of every sub-chunk of a forward- or backward-only call with
-  // maps (fp16, 5 KB per sub-chunk), whether or not the output kernel loads
-  // them (two-scan calls form them in both kernels: see launch_d)
+  // Tm blocks of every sub-chunk of each scan with maps (fp16, 5 KB per
+  // sub-chunk and head), whether or not the output kernels load them: the
+  // scan of a forward- or backward-only call, and for d_k <= 64 (without
+  // the feature prologue) both scans of a bidirectional call and the forward
+  // scan of a chunk-causal one (see launch_d)
   const size_t U = (size_t)((p.T + CH - 1) / CH);
-  pl.tm_bytes = pl.NS >= 2 && pl.dirs != 3 && !pl.cc ? align_up(bhd * U * kTmElems * 2, 256) : 0;
+  const bool two_scan = pl.dirs == 3 || pl.cc;
+  const size_t tm_slots = pl.NS < 2 ? 0 : !two_scan ? 1 : !tm_two_scan(p) ? 0 : pl.cc ? 1 : 2;
+  pl.tm_bytes = tm_slots ? align_up(tm_slots * p.B * p.H * U * kTmElems * 2, 256) : 0;
   pl.tm_off = pl.gstarts_off + pl.cw.gstarts_bytes;
   pl.bytes = pl.tm_off + pl.tm_bytes;
   return pl;
@@ -2291,9 +2305,8 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
   const bool both = pl.dirs == 3;
   // Reuse of the map kernel's Tm blocks by the output kernel: forward- and
   // backward-only calls (measured at the 60 s clip, output kernel alone:
-  // 0.613 -> 0.590 ms for a forward call).  Two-scan calls form their own:
-  // loading them there measured no faster (bidirectional 2.19 against 2.17 ms
-  // per step) and would move 0.67 GB more per step through HBM.
+  // 0.613 -> 0.590 ms for a forward call), and two-scan calls at d_k <= 64
+  // (see tm_two_scan).
   a.tm = pl.tm_bytes && p.tm_reuse ? reinterpret_cast<hb*>(ws + pl.tm_off) : nullptr;
   const unsigned bhc = (unsigned)(p.B * p.H);
   // Workgroups are dealt to the 8 XCDs (each with its own L2) in turn.  With
@@ -2343,14 +2356,25 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
   };
   // One output launch (x.mode and x.out_bf16 select the store type).
   // x.tm: load the map kernel's Tm blocks.
-  // (Loaded Tm blocks only occur in single-scan calls, mode 0.)
+  // (Loaded Tm blocks occur in single-scan calls, mode 0, and in two-scan
+  // calls only where tm_two_scan allows: the partial-storing and -adding
+  // variants with loaded blocks are built for d_k <= 64 without the prologue.)
   auto launch_out = [&](const Args& x, unsigned gx, hipStream_t st) {
     const dim3 grid(gx, bhc, 1), block(Geo<D>::NT);
-    if (x.tm) {
+    if (x.tm && x.mode == 0) {
       if (x.out_bf16)
         hipLaunchKernelGGL((seg_out_kernel<D, PRO, 1, true>), grid, block, 0, st, x);
       else
         hipLaunchKernelGGL((seg_out_kernel<D, PRO, 0, true>), grid, block, 0, st, x);
+    } else if (x.tm) {
+      if constexpr (D <= 64 && !PRO) {
+        if (x.mode == 1)
+          hipLaunchKernelGGL((seg_out_kernel<D, PRO, 2, true>), grid, block, 0, st, x);
+        else if (x.out_bf16)
+          hipLaunchKernelGGL((seg_out_kernel<D, PRO, 4, true>), grid, block, 0, st, x);
+        else
+          hipLaunchKernelGGL((seg_out_kernel<D, PRO, 3, true>), grid, block, 0, st, x);
+      }
     } else if (x.mode == 1) {
       hipLaunchKernelGGL((seg_out_kernel<D, PRO, 2, false>), grid, block, 0, st, x);
     } else if (x.mode == 2) {

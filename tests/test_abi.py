@@ -178,10 +178,15 @@ def test_feature_prologue_validation_and_workspace():
         for d in ("fwd", "bwd", "bidir"):
             a = G.workspace_size(prob(**kw), d)
             b = G.workspace_size(prob(prologue="features", **kw), d)
+            if kw == dict(algo="chunked") and d == "bidir":
+                # at d_k <= 64 a bidirectional call without the prologue also
+                # holds both scans' sub-chunk inverse blocks (5 KB per 64 tokens)
+                a -= 2 * 1 * 2 * ((300 + 63) // 64) * 5120
             assert b - a in (fac, rounded), (kw, d, a, b)
     p = prob(prologue="features", first_chunk_frames=2, chunk_frames=1)
-    assert G.workspace_size(p, "chunk_causal") > G.workspace_size(prob(first_chunk_frames=2, chunk_frames=1),
-                                                                  "chunk_causal")
+    # without the prologue the chunk-causal call at d_k <= 64 holds the forward scan's inverse blocks
+    plain = G.workspace_size(prob(first_chunk_frames=2, chunk_frames=1), "chunk_causal") - 2 * 5 * 5120
+    assert G.workspace_size(p, "chunk_causal") - plain in (fac, rounded)
 
 
 def test_split_chain_workspace():
@@ -225,7 +230,8 @@ def test_segment_plan_follows_the_problem():
 def test_inverse_reuse_workspace():
     """A forward-only chunked call with more than one segment holds 5 KB of
     fp16 inverse blocks per 64-token sub-chunk and head, whether or not the
-    output kernel loads them; a bidirectional call holds none."""
+    output kernel loads them; a bidirectional call holds them for both scans
+    at d_k <= 64 and none at larger widths."""
     def p_(seg, form=False):   # 4000 tokens: 63 sub-chunks
         return prob(frames=40, tokens_per_frame=100, algo="chunked",
                     tuning=G.Tuning(segment_tokens=seg, chain_group=1, form_inverse=form))
@@ -237,7 +243,11 @@ def test_inverse_reuse_workspace():
     per_seg = 2 * 64 * (128 + 64) * 4           # one scan's map and start state, 2 heads
     tm = 2 * 63 * 5120
     assert on - one == pytest.approx(7 * per_seg + tm, abs=1024)
-    assert on_bi - one_bi == pytest.approx(2 * 7 * per_seg, abs=1024)
+    assert on_bi - one_bi == pytest.approx(2 * 7 * per_seg + 2 * tm, abs=1024)
+    wide = dict(frames=40, tokens_per_frame=100, algo="chunked", d_k=96, d_v=96)
+    one96 = G.workspace_size(prob(**wide, tuning=G.Tuning(segment_tokens=4096, chain_group=1)), "bidir")
+    on96 = G.workspace_size(prob(**wide, tuning=G.Tuning(segment_tokens=512, chain_group=1)), "bidir")
+    assert on96 - one96 == pytest.approx(2 * 7 * 2 * 96 * (192 + 96) * 4, abs=1024)
 
 
 def test_step_noalloc_rejects_oversized_steps_before_any_hip_call():
