@@ -626,7 +626,8 @@ def main():
             dom = max(kern, key=lambda k: kern[k]["avg_ms"] * kern[k]["launches_per_step"])
             achieved = by.get(dom, 0) / kern[dom]["launches_per_step"] / (kern[dom]["avg_ms"] / 1e3) / 1e9
             roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": achieved / PEAK_HBM_GBS, "traffic": read_traffic(dom, tag), "kernel": dom}
+                    "frac": achieved / PEAK_HBM_GBS, "traffic": read_traffic(dom, tag), "kernel": dom,
+                    "bytes_per_launch": by.get(dom, 0) / kern[dom]["launches_per_step"], "avg_ms": kern[dom]["avg_ms"]}
         elif "seg_out_kernel" in kern and alg_out:
             k = kern["seg_out_kernel"]
             # credited flops of one launch: a launch covers one scan direction of
