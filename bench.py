@@ -542,6 +542,8 @@ def main():
     ap.add_argument("--inverse-reuse", default="on", choices=["on", "off"],
                     help="on: the output kernel of a forward- or backward-only call loads the "
                          "segment-map kernel's sub-chunk inverses (identical results); off: it forms them again")
+    ap.add_argument("--no-strip-scan", action="store_true",
+                    help="short single-scan calls (one streaming frame) through segment maps and chain")
     ap.add_argument("--parity-procs", type=int, default=16,
                     help="processes of the all-cores oracle run (capped by the host's CPUs)")
     ap.add_argument("--no-parity", action="store_true", help="skip the oracle check and CPU baseline")
@@ -570,14 +572,14 @@ def main():
     direction = "stream" if stream else (args.direction or "bidir")
     chunks = tuple(int(c) for c in args.chunks.split(","))
     tun = G.Tuning(segment_tokens=args.segment, serial_scans=args.serial_scans,
-                   form_inverse=args.inverse_reuse == "off")
+                   form_inverse=args.inverse_reuse == "off", no_strip_scan=args.no_strip_scan)
     jac = args.intra == "jacobi"
     cc = direction == "chunk_causal"
     # name of the committed counter summaries for this configuration
     tag = w.name + ("_" + direction if direction in ("fwd", "bwd") else "") + ("_jacobi" if jac else "") + \
         ("_features" if pro else "") + ("_chunk_causal" if cc else "") + \
         ("" if args.inverse_reuse == "on" or jac or direction in ("bidir", "chunk_causal", "stream")
-         else "_inverse_formed")
+         else "_inverse_formed") + ("_no_strip_scan" if args.no_strip_scan else "")
     print(f"[bench] {w.name} {direction}: generating inputs", file=sys.stderr, flush=True)
     run = Run(G, torch, w, direction, args.seed, args.intra, args.prologue, chunks, tun)
     B, T, H, dk, dv = w.batch, w.tokens, w.heads, w.d_k, w.d_v

@@ -30,7 +30,7 @@ FORWARD, BACKWARD, BIDIRECTIONAL, CHUNK_CAUSAL = 0, 1, 2, 3
 ALGO = {"auto": 0, "chunked": 1, "recurrent": 2}
 INTRA = {"sequential": 0, "jacobi": 1}
 PROLOGUE = {"none": 0, "features": 1}
-FLAG_SERIAL_SCANS, FLAG_FORM_INVERSE = 1, 2
+FLAG_SERIAL_SCANS, FLAG_FORM_INVERSE, FLAG_NO_STRIP_SCAN = 1, 2, 4
 NOALLOC_SCRATCH_BYTES = 64 << 20   # GDN_NOALLOC_SCRATCH_BYTES
 DIRECTION = {"fwd": FORWARD, "bwd": BACKWARD, "bidir": BIDIRECTIONAL, "chunk_causal": CHUNK_CAUSAL,
              FORWARD: FORWARD, BACKWARD: BACKWARD, BIDIRECTIONAL: BIDIRECTIONAL, CHUNK_CAUSAL: CHUNK_CAUSAL}
@@ -62,12 +62,15 @@ class Tuning:
     chain_group: 0 automatic, 1 whole chain, m >= 2 groups of m maps;
     serial_scans: run a two-scan call's kernels in order on the caller's
     stream; form_inverse: the output kernel of a single-scan call forms its
-    sub-chunk inverses instead of loading the map kernel's."""
+    sub-chunk inverses instead of loading the map kernel's; no_strip_scan:
+    a short single-scan call (T <= 2048) runs through segment maps and their
+    chain instead of the strip scan."""
 
     segment_tokens: int = 0
     chain_group: int = 0
     serial_scans: bool = False
     form_inverse: bool = False
+    no_strip_scan: bool = False
 
 
 _TUNING = contextvars.ContextVar("gdn_tuning", default=Tuning())
@@ -150,7 +153,8 @@ def make_problem(batch, heads, d_k, d_v, frames, tokens_per_frame, qkv_dtype=BF1
     p.first_chunk_frames, p.chunk_frames = int(first_chunk_frames), int(chunk_frames)
     p.prologue = PROLOGUE[prologue] if isinstance(prologue, str) else int(prologue)
     p.segment_tokens, p.chain_group = int(t.segment_tokens), int(t.chain_group)
-    p.flags = (FLAG_SERIAL_SCANS if t.serial_scans else 0) | (FLAG_FORM_INVERSE if t.form_inverse else 0)
+    p.flags = (FLAG_SERIAL_SCANS if t.serial_scans else 0) | (FLAG_FORM_INVERSE if t.form_inverse else 0) | \
+        (FLAG_NO_STRIP_SCAN if t.no_strip_scan else 0)
     return p
 
 
@@ -161,7 +165,7 @@ def workspace_size(problem: Problem, direction=BIDIRECTIONAL) -> int:
 
 
 KERNELS = ("seg_map_kernel", "seg_chain_kernel", "seg_out_kernel", "recurrent_kernel", "jac_map_kernel",
-           "jac_out_kernel", "prologue_kernel")
+           "jac_out_kernel", "prologue_kernel", "scan_prep_kernel", "scan_kernel")
 
 
 def profile_enable(on: bool = True) -> None:

@@ -32,7 +32,7 @@ gdn_status check_problem(const gdn_problem* pr, int direction, gdn::Problem* out
     return fail(GDN_ERR_INVALID_ARGUMENT, "abi_version %d != %d", pr->abi_version, GDN_ABI_VERSION);
   for (int i = 0; i < (int)(sizeof pr->reserved / sizeof pr->reserved[0]); ++i)
     if (pr->reserved[i] != 0) return fail(GDN_ERR_INVALID_ARGUMENT, "reserved[%d] is not zero", i);
-  if (pr->flags & ~(GDN_FLAG_SERIAL_SCANS | GDN_FLAG_FORM_INVERSE))
+  if (pr->flags & ~(GDN_FLAG_SERIAL_SCANS | GDN_FLAG_FORM_INVERSE | GDN_FLAG_NO_STRIP_SCAN))
     return fail(GDN_ERR_INVALID_ARGUMENT, "unknown flags 0x%x", (unsigned)pr->flags);
   if (pr->segment_tokens < 0 || pr->segment_tokens > (1 << 30))
     return fail(GDN_ERR_INVALID_ARGUMENT, "segment_tokens must be in [0, 2^30] (got %d)", pr->segment_tokens);
@@ -86,6 +86,7 @@ gdn_status check_problem(const gdn_problem* pr, int direction, gdn::Problem* out
   out->chain_group = pr->chain_group;
   out->serial_scans = (pr->flags & GDN_FLAG_SERIAL_SCANS) != 0;
   out->tm_reuse = (pr->flags & GDN_FLAG_FORM_INVERSE) == 0;
+  out->strip_scan = (pr->flags & GDN_FLAG_NO_STRIP_SCAN) == 0;
   return GDN_OK;
 }
 

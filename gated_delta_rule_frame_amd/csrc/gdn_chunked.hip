@@ -128,6 +128,7 @@ struct Args {
   int ch_m, ch_groups;  // ... maps per group, groups
   float* gmaps;         // ... composed group maps [ndir][B][H][groups][DK][DK+DV]
   float* gstarts;       // ... group start states [ndir][B][H][groups][DK][DV] (transposed)
+  char* sc;             // strip scan: per sub-chunk and head, Tm diag(beta), P and gate factors
   hb* tm;               // Tm diag(beta) of every sub-chunk, [ndir][B][H][U][10][16][16] (U = ceil(T / 64),
                         // the 10 lower 16x16 blocks), stored by the map kernels and read by the output
                         // kernels; null: the map kernels store nothing
@@ -2120,12 +2121,412 @@ __global__ __launch_bounds__(64 * (D / 16)) void jac_out_kernel(Args a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// 5. Strip scan: short single-direction calls (one streaming frame).
+//
+// With few sub-chunks per head the segment maps and the chain are mostly
+// fixed latency (three launches, each about one sub-chunk long plus its ramp),
+// and a head's sub-chunks in sequence would be one workgroup's long chain.
+// But each column of the state evolves on its own (the update mixes rows
+// through k and beta, never columns), so the sequence can be split by value
+// columns instead of by tokens:
+//   sc_prep_kernel (one workgroup per sub-chunk and head, all in parallel):
+//     gate factors, the Gram tiles and the triangular inverse of the sub-chunk,
+//     stored as Tm diag(beta) and P = c tril(Q K^T) * E (fp16, the 10 lower
+//     16x16 blocks each) and the factors e^G, c e^G, c e^{G_n - G};
+//   sc_scan_kernel (one workgroup per 16-column strip of the state and head):
+//     the sub-chunks in scan order with short dependent steps.  Four compute
+//     wavefronts each own one 16-token row tile of the sub-chunk:
+//       K H and (Q H)^T for its rows      (the state strip read from LDS, fp16)
+//       R = V - c e^G * K H                -> LDS
+//       V' = Tm diag(beta) R               -> LDS (also scaled by c e^{G_n - G})
+//       O = e^G * Q H + P V'               -> global
+//       H <- e^{G_n} H + K^T (c e^{G_n - G} V')   (wave r: tiles r and r + 4)
+//     with three barriers per sub-chunk; four stager wavefronts convert and
+//     stage the next sub-chunk's rows meanwhile, their loads issued two
+//     sub-chunks ahead.  The same algebra and rounding points as the output
+//     kernel, in another order of the sums.
+// Measured on one 880-token frame of 20 heads x 112 (the streaming shape):
+// 60 -> 35 us a call (captured in a HIP graph); the scan kernel takes about
+// 27 us, of which staging (bf16 -> fp16 conversion and scattered LDS writes,
+// bound by the CU's VALU issue) is about 9 us: a copy without it ran in 18 us.
+// Preparing the rows in fp16 in the prep kernel instead (a plain copy in the
+// scan) measured no faster: the prep kernel's extra stores cost what the
+// scan saved (prep 11 -> 15 us, scan 27 -> 25.5 us).
+
+// Per sub-chunk and head in the workspace: Tm diag(beta) and P as 320 pieces
+// of 16 bytes each (the piece order of the stored inverses), then e^G,
+// c e^G and c e^{G_n - G} (64 floats each).
+constexpr int kScanSubBytes = 2 * kTmPieces * 16 + 3 * CH * 4;
+
+template <int D>
+struct PrepLay {
+  static constexpr int KR = (KRows<D>::ELEMS * 2 + 15) / 16 * 16;
+  static constexpr int o_qr = 0, o_kr = KR, o_pp = 2 * KR, o_tt = o_pp + CH * LDT * 2, o_gt = o_tt + CH * LDT * 2;
+  static constexpr int o_ao = o_gt + 5 * CH * 4, o_td = o_ao + CH * LDT * 2, o_ad = o_td + CH * LDD * 2;
+  static constexpr int BYTES = o_ad + 4 * ADB * 4;
+};
+
+template <int D>
+__global__ __launch_bounds__(Geo<D>::NT) void sc_prep_kernel(Args a) {
+  using G = Geo<D>;
+  using PL = PrepLay<D>;
+  __shared__ __attribute__((aligned(16))) char smem[PL::BYTES];
+  const long long U = (a.T + CH - 1) / CH;
+  const int jc = blockIdx.x;   // sub-chunk in original order
+  if (jc >= U) return;
+  const int b = (int)blockIdx.y / a.H, h = (int)blockIdx.y % a.H;
+  const bool helper = wave_id() == G::HW;
+  const long long t0 = (long long)jc * CH;
+  const Sub sb = make_sub(t0, (int)(a.T - t0 < CH ? a.T - t0 : CH), a.dir == 1);
+  Buf B;
+  B.qr = reinterpret_cast<hb*>(smem + PL::o_qr);
+  B.kr = reinterpret_cast<hb*>(smem + PL::o_kr);
+  B.pp = reinterpret_cast<hb*>(smem + PL::o_pp);
+  B.tt = reinterpret_cast<hb*>(smem + PL::o_tt);
+  B.vr = nullptr;
+  float* gt = reinterpret_cast<float*>(smem + PL::o_gt);
+  B.g2 = gt;
+  B.eg = gt + CH;
+  B.ce = gt + 2 * CH;
+  B.dn = gt + 3 * CH;
+  B.bt = gt + 4 * CH;
+  Inv I;
+  I.ao = reinterpret_cast<hb*>(smem + PL::o_ao);
+  I.td = reinterpret_cast<hb*>(smem + PL::o_td);
+  I.ad = reinterpret_cast<float*>(smem + PL::o_ad);
+  I.os = nullptr;
+  for (int i = threadIdx.x; i < PL::BYTES / 16; i += G::NT) reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
+  StageG sg;
+  StageKQ sk;
+  if (helper)
+    fetch_gates(a, b, h, sb, sg);
+  else
+    fetch_kq<D, true, false>(a, b, h, sb, sk);
+  __syncthreads();
+  if (helper)
+    stage_gates(B, sg, a.c);
+  else
+    stage_kq<D, true, false>(B, sk);
+  __syncthreads();
+  if (helper)
+    gram_stage_helper<D>(a, B, I);
+  else
+    gram_stage_strips<D, true>(a, B, I);
+  __syncthreads();
+  if (helper) tinv_offdiag(I, B);
+  __syncthreads();
+  // pieces 0..319 Tm, 320..639 P, then 48 pieces of factors (e^G, c e^G,
+  // c e^{G_n - G}: contiguous from B.eg)
+  const __amdgpu_buffer_rsrc_t r =
+      rows_rsrc(a.sc + (((long long)b * a.H + h) * U + jc) * kScanSubBytes, kScanSubBytes);
+  constexpr int NPIECE = kScanSubBytes / 16;
+  for (int k = threadIdx.x; k < NPIECE; k += G::NT) {
+    const hb* src = k < kTmPieces ? B.tt + tm_piece_lds(k)
+                    : k < 2 * kTmPieces ? B.pp + tm_piece_lds(k - kTmPieces)
+                                        : reinterpret_cast<const hb*>(B.eg + 4 * (k - 2 * kTmPieces));
+    const uint4 x = *reinterpret_cast<const uint4*>(src);
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{x.x, x.y, x.z, x.w}, r, (uint32_t)(16 * k), 0, 0);
+  }
+}
+
+template <int D>
+struct ScanLay {
+  static constexpr int DP = Geo<D>::DP;
+  static constexpr int KR = (KRows<D>::ELEMS * 2 + 15) / 16 * 16;
+  static constexpr int TT = CH * LDT * 2;
+  static constexpr int LVT = CH + 4;   // fp32 stride of the transposed value strip
+  static constexpr int o_kr = 0, o_qr = KR, o_tt = 2 * KR, o_pp = o_tt + TT, o_gf = o_pp + TT;
+  static constexpr int o_vt = o_gf + 3 * CH * 4;
+  static constexpr int BUF = o_vt + 16 * LVT * 4;   // one sub-chunk buffer (two alternate)
+  static constexpr int LH = DP + 8;                 // fp16 stride of the transposed state strip
+  static constexpr int LR = CH + 8;                 // fp16 stride of the transposed token strips
+  static constexpr int o_hh = 2 * BUF;
+  static constexpr int o_rt = o_hh + 16 * LH * 2;
+  static constexpr int o_vp = o_rt + 16 * LR * 2;
+  static constexpr int o_vs = o_vp + 16 * LR * 2;
+  static constexpr int BYTES = o_vs + 16 * LR * 2;
+  static constexpr int NC = 256;                              // compute threads: four wavefronts
+  static constexpr int NS = 256;                              // stager threads: four wavefronts
+  static constexpr int NKQ = (CH * (D / 8) + NS - 1) / NS;    // 16-byte K (and Q) pieces per stager thread
+  static constexpr int NM = (2 * kTmPieces + NS - 1) / NS;    // Tm and P pieces per stager thread
+  static_assert(BYTES <= 160 * 1024, "workgroup LDS budget exceeded");
+  static_assert(BUF % 16 == 0 && KR % 16 == 0, "alignment");
+};
+
+// Rows of one sub-chunk of the strip scan in a stager thread's registers.
+template <int D>
+struct ScanStage {
+  uint4 k[ScanLay<D>::NKQ], q[ScanLay<D>::NKQ], m[ScanLay<D>::NM], v, gf;
+};
+
+template <int D, bool OB>
+__global__ __launch_bounds__(ScanLay<D>::NC + ScanLay<D>::NS) void sc_scan_kernel(Args a) {
+  using G = Geo<D>;
+  using SL = ScanLay<D>;
+  constexpr int MD = G::MD, NP = G::NP, NC = SL::NC, NS = SL::NS;
+  __shared__ __attribute__((aligned(16))) char smem[SL::BYTES];
+  // XCD-aware mapping: workgroups are dealt to the 8 XCDs in turn, so
+  // workgroup i = 8 j + x runs on XCD x; the strips of one head share an
+  // XCD (and its L2, through which each of them reads all of the head's rows).
+  const int x = (int)blockIdx.x & 7, j = (int)blockIdx.x >> 3;
+  const int bh_ = x + 8 * (j / MD), s = j % MD;
+  if (bh_ >= a.B * a.H) return;
+  const int b = bh_ / a.H, h = bh_ % a.H;
+  // waves 0-3 compute (wave r: row tile r of each sub-chunk), waves 4-7
+  // stage the rows of the sub-chunks ahead (thread t of the stagers)
+  const int r = wave_id(), lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15;
+  const bool stager = r >= 4;
+  const int t = (int)threadIdx.x - NC;
+  const bool rev = a.dir == 1;
+  const long long U = (a.T + CH - 1) / CH;
+  const int HD = a.H * D;
+  const long long hbase = ((long long)b * a.T) * HD + (long long)h * D;   // element of (b, token 0, h, 0)
+  for (int i = threadIdx.x; i < SL::BYTES / 16; i += NC + NS) reinterpret_cast<uint4*>(smem)[i] = make_uint4(0, 0, 0, 0);
+  auto sub = [&](long long jj) {   // sub-chunk jj in scan order (past the end: empty)
+    const long long jc = rev ? U - 1 - jj : jj;
+    const long long t0 = jj < U ? jc * CH : 0;
+    return make_sub(t0, jj < U ? (int)(a.T - t0 < CH ? a.T - t0 : CH) : 0, rev);
+  };
+  auto fetch = [&](long long jj, ScanStage<D>& st) {
+    const Sub sb = sub(jj);
+    const __amdgpu_buffer_rsrc_t rk = rows_rsrc(a.k + hbase + sb.t0 * HD, (long long)sb.n * HD * 2);
+    const __amdgpu_buffer_rsrc_t rq = rows_rsrc(a.q + hbase + sb.t0 * HD, (long long)sb.n * HD * 2);
+#pragma unroll
+    for (int i = 0; i < SL::NKQ; ++i) {   // pieces past the rows read past the buffer
+      const int k = t + NS * i, row = k / (D / 8), c8 = k % (D / 8);
+      const uint32_t off = (uint32_t)((sb.r0 + sb.sgn * row) * HD * 2 + 16 * c8);
+      const u32x4_t vk = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+      const u32x4_t vq = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+      st.k[i] = make_uint4(vk[0], vk[1], vk[2], vk[3]);
+      st.q[i] = make_uint4(vq[0], vq[1], vq[2], vq[3]);
+    }
+    const __amdgpu_buffer_rsrc_t rm = rows_rsrc(a.sc + (((long long)b * a.H + h) * U + sb.t0 / CH) * kScanSubBytes,
+                                                sb.n > 0 ? kScanSubBytes : 0);
+#pragma unroll
+    for (int i = 0; i < SL::NM; ++i) {
+      const u32x4_t vm = __builtin_amdgcn_raw_buffer_load_b128(rm, (uint32_t)(16 * (t + NS * i)), 0, 0);
+      st.m[i] = make_uint4(vm[0], vm[1], vm[2], vm[3]);
+    }
+    // factors: pieces 640 .. 687 (threads 0..47; the others read past the end)
+    const u32x4_t vg = __builtin_amdgcn_raw_buffer_load_b128(rm, (uint32_t)(16 * (2 * kTmPieces + (t < 48 ? t : 64))), 0, 0);
+    st.gf = make_uint4(vg[0], vg[1], vg[2], vg[3]);
+    // value strip: row t / 2, columns 16 s + 8 (t % 2) .. + 7 (threads 0..127)
+    const __amdgpu_buffer_rsrc_t rv = rows_rsrc(a.v + hbase + sb.t0 * HD, (long long)sb.n * HD * 2);
+    const int vrow = t >> 1;
+    const u32x4_t vv = __builtin_amdgcn_raw_buffer_load_b128(
+        rv, (uint32_t)(((sb.r0 + sb.sgn * vrow) * HD + 16 * s + 8 * (t & 1)) * 2), 0, 0);
+    st.v = make_uint4(vv[0], vv[1], vv[2], vv[3]);
+  };
+  auto stage = [&](int buf, const ScanStage<D>& st) {
+    char* p = smem + buf * SL::BUF;
+    hb* kr = reinterpret_cast<hb*>(p + SL::o_kr);
+    hb* qr = reinterpret_cast<hb*>(p + SL::o_qr);
+#pragma unroll
+    for (int i = 0; i < SL::NKQ; ++i) {
+      const int k = t + NS * i, row = k / (D / 8), c8 = k % (D / 8);
+      if (k < CH * (D / 8)) {
+        *reinterpret_cast<uint4*>(kr + krow<D>(row) + 8 * c8) = bf16x8_to_f16x8(st.k[i]);
+        *reinterpret_cast<uint4*>(qr + krow<D>(row) + 8 * c8) = bf16x8_to_f16x8(st.q[i]);
+      }
+    }
+    hb* tt = reinterpret_cast<hb*>(p + SL::o_tt);
+    hb* pp = reinterpret_cast<hb*>(p + SL::o_pp);
+#pragma unroll
+    for (int i = 0; i < SL::NM; ++i) {
+      const int k = t + NS * i;
+      if (k < kTmPieces)
+        *reinterpret_cast<uint4*>(tt + tm_piece_lds(k)) = st.m[i];
+      else if (k < 2 * kTmPieces)
+        *reinterpret_cast<uint4*>(pp + tm_piece_lds(k - kTmPieces)) = st.m[i];
+    }
+    if (t < 48) *reinterpret_cast<uint4*>(p + SL::o_gf + 16 * t) = st.gf;
+    if (t < 128) {
+      float* vt = reinterpret_cast<float*>(p + SL::o_vt);
+      const int row = t >> 1, c0 = 8 * (t & 1);
+      const uint32_t w[4] = {st.v.x, st.v.y, st.v.z, st.v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vt[(c0 + 2 * e) * SL::LVT + row] = __uint_as_float(w[e] << 16);
+        vt[(c0 + 2 * e + 1) * SL::LVT + row] = __uint_as_float(w[e] & 0xffff0000u);
+      }
+    }
+  };
+  hb* const hh = reinterpret_cast<hb*>(smem + SL::o_hh);
+  hb* const rt = reinterpret_cast<hb*>(smem + SL::o_rt);
+  hb* const vp = reinterpret_cast<hb*>(smem + SL::o_vp);
+  hb* const vs = reinterpret_cast<hb*>(smem + SL::o_vs);
+  // state tiles of this wave: rows 16 md .. of the strip, md = r and r + 4
+  constexpr int NMT = (MD + 3) / 4;
+  f32x4 Hm[NMT];
+  const size_t sbase = ((size_t)b * a.H + h) * D * D;
+  const uint32_t so = (uint32_t)((4 * g * D + 16 * s + cl) * 4);   // lane byte offset within a state
+  if (!stager) {
+    const __amdgpu_buffer_rsrc_t hr = block_rsrc(a.h0 ? a.h0 + sbase : nullptr, a.h0 ? D * D * 4 : 0);
+#pragma unroll
+    for (int i = 0; i < NMT; ++i) {
+      const int md = r + 4 * i;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Hm[i][e] = block_load(hr, so, (uint32_t)(((md < MD ? md : 0) * 16 + e) * D * 4));
+    }
+  }
+  constexpr bool half = OB;
+  const long long esz = half ? 2 : 4;
+  // The two roles run their own loops with the same barriers (three per
+  // sub-chunk), so that the compiler's waits before staging count only the
+  // stagers' loads: with the register sets of two sub-chunks in flight, the
+  // rows staged during sub-chunk jj were requested two sub-chunks earlier.
+  // Both loops take an even number of steps (a last, empty one when U is odd:
+  // its rows read as zeros, its stores fall outside the buffers, and it leaves
+  // the state alone).
+  if (stager) {
+    ScanStage<D> s0, s1;   // rows of the even and the odd sub-chunks
+    fetch(0, s0);
+    __syncthreads();   // zero fill done
+    stage(0, s0);
+    fetch(1, s1);
+    fetch(2, s0);
+    __syncthreads();
+    // during sub-chunk jj: stage jj + 1 into the other buffer (last read
+    // before the end of jj - 1), then request jj + 3 into the same set
+    auto sstep = [&](long long jj, ScanStage<D>& st) {
+      stage((int)((jj + 1) & 1), st);
+      fetch(jj + 3, st);
+      __syncthreads();
+      __syncthreads();
+      __syncthreads();
+    };
+    for (long long jj = 0; jj < U; jj += 2) {
+      sstep(jj, s1);
+      sstep(jj + 1, s0);
+    }
+    return;
+  }
+  __syncthreads();   // zero fill done
+#pragma unroll
+  for (int i = 0; i < NMT; ++i) {
+    const int md = r + 4 * i;
+    if (md < MD) store4_h(hh + cl * SL::LH + 16 * md + 4 * g, Hm[i][0], Hm[i][1], Hm[i][2], Hm[i][3]);
+  }
+  __syncthreads();
+  auto cstep = [&](long long jj) {
+    const Sub sb = sub(jj);
+    const char* pc = smem + (jj & 1) * SL::BUF;
+    const hb* kr = reinterpret_cast<const hb*>(pc + SL::o_kr);
+    const hb* qr = reinterpret_cast<const hb*>(pc + SL::o_qr);
+    const hb* tt = reinterpret_cast<const hb*>(pc + SL::o_tt);
+    const hb* pp = reinterpret_cast<const hb*>(pc + SL::o_pp);
+    const float* vt = reinterpret_cast<const float*>(pc + SL::o_vt);
+    const float* eg = reinterpret_cast<const float*>(pc + SL::o_gf);
+    const float* ce = eg + CH;
+    const float* dn = eg + 2 * CH;
+    f32x4 qh = zero4();
+    // K H (lane: rows 16 r + 4 g .., column cl) and (Q H)^T (lane: token
+    // 16 r + cl, columns 4 g ..) for this wave's row tile
+    f32x4 kh = zero4();
+    {
+      f16x8_t Hf[NP];
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+        Hf[p] = cat8(ld4(hh + cl * SL::LH + 32 * p + 4 * g), ld4(hh + cl * SL::LH + 32 * p + 16 + 4 * g));
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        kh = mfma32(fragK<D>(kr + krow<D>(16 * r + cl), p, g), Hf[p], kh);
+        qh = mfma32(Hf[p], fragK<D>(qr + krow<D>(16 * r + cl), p, g), qh);
+      }
+    }
+    {
+      const f32x4 v4 = ld4f(vt + cl * SL::LVT + 16 * r + 4 * g), c4 = ld4f(ce + 16 * r + 4 * g);
+      const f32x4 R = v4 - c4 * kh;
+      store4_h(rt + cl * SL::LR + 16 * r + 4 * g, R[0], R[1], R[2], R[3]);
+    }
+    __syncthreads();
+    // V' rows of this wave's tile: Tm diag(beta) (lower triangular) times R
+    {
+      f32x4 vn = mfma32(fragA2(tt + (16 * r + cl) * LDT, 0, g),
+                        cat8(ld4(rt + cl * SL::LR + 4 * g), ld4(rt + cl * SL::LR + 16 + 4 * g)), zero4());
+      if (r >= 2)
+        vn = mfma32(fragA2(tt + (16 * r + cl) * LDT, 2, g),
+                    cat8(ld4(rt + cl * SL::LR + 32 + 4 * g), ld4(rt + cl * SL::LR + 48 + 4 * g)), vn);
+      const f32x4 d4 = ld4f(dn + 16 * r + 4 * g);
+      store4_h(vp + cl * SL::LR + 16 * r + 4 * g, vn[0], vn[1], vn[2], vn[3]);
+      store4_h(vs + cl * SL::LR + 16 * r + 4 * g, vn[0] * d4[0], vn[1] * d4[1], vn[2] * d4[2], vn[3] * d4[3]);
+    }
+    __syncthreads();
+    // outputs: O^T = e^G (Q H)^T + (P V')^T, lane: token 16 r + cl, columns 16 s + 4 g ..
+    {
+      f32x4 O = eg[16 * r + cl] * qh;
+      O = mfma32(cat8(ld4(vp + cl * SL::LR + 4 * g), ld4(vp + cl * SL::LR + 16 + 4 * g)),
+                 fragA2(pp + (16 * r + cl) * LDT, 0, g), O);
+      if (r >= 2)
+        O = mfma32(cat8(ld4(vp + cl * SL::LR + 32 + 4 * g), ld4(vp + cl * SL::LR + 48 + 4 * g)),
+                   fragA2(pp + (16 * r + cl) * LDT, 2, g), O);
+      const __amdgpu_buffer_rsrc_t ro =
+          rows_rsrc(static_cast<char*>(a.out) + (hbase + sb.t0 * HD) * esz, (long long)sb.n * HD * esz);
+      const uint32_t off = (uint32_t)(((sb.r0 + sb.sgn * (16 * r + cl)) * HD + 16 * s + 4 * g) * esz);
+      if constexpr (half) {
+        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+        const u32x2_t w{f32_to_bf16_bits(O[0]) | ((uint32_t)f32_to_bf16_bits(O[1]) << 16),
+                        f32_to_bf16_bits(O[2]) | ((uint32_t)f32_to_bf16_bits(O[3]) << 16)};
+        __builtin_amdgcn_raw_buffer_store_b64(w, ro, off, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, O), ro, off, 0, 0);
+      }
+    }
+    // state: H <- e^{G_n} H + K^T (c e^{G_n - G} V') for this wave's tiles
+    if (jj < U) {
+      const f16x8_t vs0 = cat8(ld4(vs + cl * SL::LR + 4 * g), ld4(vs + cl * SL::LR + 16 + 4 * g));
+      const f16x8_t vs1 = cat8(ld4(vs + cl * SL::LR + 32 + 4 * g), ld4(vs + cl * SL::LR + 48 + 4 * g));
+      const hb* kt = kr + krow<D>(4 * g + (cl >> 2)) + 4 * (cl & 3);
+      const float dec = eg[CH - 1];
+#pragma unroll
+      for (int i = 0; i < NMT; ++i) {
+        const int md = r + 4 * i;
+        if (md < MD) {
+          const f16x8_t k0 = cat8(ld4_tr(kt + 16 * md), ld4_tr(kt + krow<D>(16) + 16 * md));
+          const f16x8_t k1 = cat8(ld4_tr(kt + krow<D>(32) + 16 * md), ld4_tr(kt + krow<D>(48) + 16 * md));
+          f32x4 X = Hm[i] * dec;
+          X = mfma32(k0, vs0, X);
+          X = mfma32(k1, vs1, X);
+          Hm[i] = X;
+          store4_h(hh + cl * SL::LH + 16 * md + 4 * g, X[0], X[1], X[2], X[3]);
+        }
+      }
+    }
+    __syncthreads();
+  };
+  for (long long jj = 0; jj < U; jj += 2) {
+    cstep(jj);
+    cstep(jj + 1);
+  }
+  if (a.hT) {
+    const __amdgpu_buffer_rsrc_t hr = block_rsrc(a.hT + sbase, D * D * 4);
+#pragma unroll
+    for (int i = 0; i < NMT; ++i) {
+      const int md = r + 4 * i;
+      if (md < MD) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) block_store(hr, so, (uint32_t)((md * 16 + e) * D * 4), Hm[i][e]);
+      }
+    }
+  }
+}
+
 struct Plan {
   int L, NS, ndir, dirs;
   bool cc;       // chunk-causal: forward maps and chain only; the reversed scan runs per chunk
+  bool scan;     // strip scan (no maps, no chain): short single-direction calls
   ChainWs cw;    // split of the chain
   size_t maps_off, starts_off, acc_off, fac_off, gmaps_off, gstarts_off, tm_off, tm_bytes, bytes;
 };
+
+// Single-direction calls of at most this many 64-token sub-chunks per head
+// take the strip scan.
+constexpr long long kScanMaxSub = 32;
+bool strip_scan(const Problem& p, int direction) {
+  return (direction == GDN_FORWARD || direction == GDN_BACKWARD) && !p.prologue && p.strip_scan &&
+         (p.T + CH - 1) / CH <= kScanMaxSub;
+}
 
 // Whether the output kernels of a two-scan call load the map kernels' Tm
 // blocks instead of forming them.  At d_k <= 64 the helper wavefront's
@@ -2142,6 +2543,14 @@ Plan make_plan(const Problem& p, int direction) {
   pl.cc = direction == GDN_CHUNK_CAUSAL;
   pl.dirs = direction == GDN_FORWARD || pl.cc ? 1 : direction == GDN_BACKWARD ? 2 : 3;
   pl.ndir = pl.dirs == 3 ? 2 : 1;
+  if (strip_scan(p, direction)) {
+    // one segment of the whole sequence; the workspace holds the prepared sub-chunks
+    pl.scan = true;
+    pl.NS = 1;
+    pl.L = (int)((p.T + CH - 1) / CH * CH);
+    pl.bytes = align_up((size_t)p.B * p.H * (size_t)((p.T + CH - 1) / CH) * kScanSubBytes, 256);
+    return pl;
+  }
   int L = p.segment_tokens;
   if (L <= 0) {
     // The output kernel runs one workgroup per CU (its LDS use), so aim for
@@ -2302,6 +2711,29 @@ hipError_t launch_d(const Problem& p, const Plan& pl, const Tensors& t, char* ws
   a.c = p.key_scale;
   a.gmaps = reinterpret_cast<float*>(ws + pl.gmaps_off);
   a.gstarts = reinterpret_cast<float*>(ws + pl.gstarts_off);
+  if constexpr (!PRO) {
+    if (pl.scan) {
+      a.sc = ws;
+      a.dir = pl.dirs == 1 ? 0 : 1;
+      const unsigned U = (unsigned)((p.T + CH - 1) / CH), nbh = (unsigned)(p.B * p.H);
+      prof_begin(stream, GDN_KERNEL_SCAN_PREP);
+      hipLaunchKernelGGL((sc_prep_kernel<D>), dim3(U, nbh, 1), dim3(Geo<D>::NT), 0, stream, a);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      prof_end(stream, GDN_KERNEL_SCAN_PREP);
+      // 8 x (strips x ceil(heads / 8)) workgroups: the strips of a head on one XCD
+      const unsigned gx = 8u * (unsigned)Geo<D>::MD * ((nbh + 7u) / 8u);
+      prof_begin(stream, GDN_KERNEL_SCAN);
+      if (p.out_bf16)
+        hipLaunchKernelGGL((sc_scan_kernel<D, true>), dim3(gx, 1, 1), dim3(ScanLay<D>::NC + ScanLay<D>::NS), 0, stream, a);
+      else
+        hipLaunchKernelGGL((sc_scan_kernel<D, false>), dim3(gx, 1, 1), dim3(ScanLay<D>::NC + ScanLay<D>::NS), 0, stream, a);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      prof_end(stream, GDN_KERNEL_SCAN);
+      return hipSuccess;
+    }
+  }
   const bool both = pl.dirs == 3;
   // Reuse of the map kernel's Tm blocks by the output kernel: forward- and
   // backward-only calls (measured at the 60 s clip, output kernel alone:

@@ -24,6 +24,7 @@ struct Problem {
   int chain_group;     // 0: automatic, 1: whole, m >= 2: groups of m
   bool serial_scans;   // GDN_FLAG_SERIAL_SCANS
   bool tm_reuse;       // !GDN_FLAG_FORM_INVERSE
+  bool strip_scan;     // !GDN_FLAG_NO_STRIP_SCAN
 };
 
 // Device pointers of one call.

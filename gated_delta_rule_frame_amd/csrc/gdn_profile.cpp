@@ -104,6 +104,8 @@ const char* gdn_kernel_name(int32_t kernel) {
     case GDN_KERNEL_JAC_MAP: return "jac_map_kernel";
     case GDN_KERNEL_JAC_OUT: return "jac_out_kernel";
     case GDN_KERNEL_PROLOGUE: return "prologue_kernel";
+    case GDN_KERNEL_SCAN_PREP: return "scan_prep_kernel";
+    case GDN_KERNEL_SCAN: return "scan_kernel";
     default: return "";
   }
 }

@@ -191,8 +191,18 @@ typedef struct gdn_problem {
  *   of loading the one the scan's segment-map kernel formed (5 KB of fp16 per
  *   sub-chunk and head in the workspace, allocated either way).  Results are
  *   bit-identical (the same arithmetic on the same rows).  Two-scan calls and
- *   calls with a single segment always form it. */
-enum { GDN_FLAG_SERIAL_SCANS = 1, GDN_FLAG_FORM_INVERSE = 2 };
+ *   calls with a single segment always form it.
+ * NO_STRIP_SCAN: a forward- or backward-only call of the chunked path with at
+ *   most 32 sub-chunks of 64 tokens per head (T <= 2048; one streaming frame)
+ *   runs through segment maps and their chain like longer calls.  By default
+ *   such a call (without the feature prologue) takes the strip scan instead:
+ *   one launch prepares every sub-chunk (its triangular inverse, its
+ *   intra-chunk product and gate factors: 11008 bytes per sub-chunk and head
+ *   in the workspace) and one runs the sub-chunks in order with a workgroup
+ *   per 16 value columns of the state and head (the state's columns evolve
+ *   independently).  Same algebra and rounding points; results agree to
+ *   rounding (sums in another order). */
+enum { GDN_FLAG_SERIAL_SCANS = 1, GDN_FLAG_FORM_INVERSE = 2, GDN_FLAG_NO_STRIP_SCAN = 4 };
 
 /* Version of this ABI (GDN_ABI_VERSION of the built library). */
 int32_t gdn_abi_version(void);
@@ -283,7 +293,9 @@ enum {
   GDN_KERNEL_JAC_MAP = 4,     /* frame-level path: per-frame maps */
   GDN_KERNEL_JAC_OUT = 5,     /* frame-level path: outputs and final state */
   GDN_KERNEL_PROLOGUE = 6,    /* feature prologue: per-token key and query factors */
-  GDN_KERNEL_COUNT = 7
+  GDN_KERNEL_SCAN_PREP = 7,   /* strip scan: per-sub-chunk inverses, intra-chunk products, gate factors */
+  GDN_KERNEL_SCAN = 8,        /* strip scan: sub-chunks in order per state strip; outputs and final state */
+  GDN_KERNEL_COUNT = 9
 };
 gdn_status gdn_profile_enable(int32_t on);
 gdn_status gdn_profile_reset(void);

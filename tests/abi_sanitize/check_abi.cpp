@@ -63,7 +63,7 @@ int main() {
                      {&gdn_problem::tokens_per_frame, -1}, {&gdn_problem::qkv_dtype, 5},
                      {&gdn_problem::out_dtype, -2}, {&gdn_problem::algo, 7}, {&gdn_problem::intra, 3},
                      {&gdn_problem::prologue, 9}, {&gdn_problem::segment_tokens, -64},
-                     {&gdn_problem::chain_group, -1}, {&gdn_problem::flags, 64}};
+                     {&gdn_problem::chain_group, -1}, {&gdn_problem::flags, 64}, {&gdn_problem::flags, 8}};
   for (const Bad& b : bad) {
     gdn_problem q = base();
     q.*(b.f) = b.v;
@@ -134,7 +134,7 @@ int main() {
     q.chunk_frames = (int32_t)draw(0, 5);
     q.segment_tokens = (int32_t)(draw(0, 3) == 0 ? draw(0, 1 << 20) : 0);
     q.chain_group = (int32_t)draw(0, 40);
-    q.flags = (int32_t)draw(0, 3);
+    q.flags = (int32_t)draw(0, 7);
     const int32_t dir = (int32_t)draw(0, 3);
     const gdn_status s = gdn_workspace_size(&q, dir, &n);
     EXPECT(s == GDN_OK || s == GDN_ERR_INVALID_ARGUMENT || s == GDN_ERR_UNSUPPORTED);

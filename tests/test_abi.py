@@ -53,7 +53,7 @@ def test_recurrent_workspace_is_the_bidirectional_accumulator():
 @pytest.mark.parametrize("field,value", [
     ("abi_version", 1), ("abi_version", 3), ("batch", 0), ("heads", -1), ("frames", 0), ("tokens_per_frame", 0),
     ("d_k", 20), ("d_k", 144), ("d_v", 8), ("qkv_dtype", 7), ("out_dtype", -1), ("algo", 9),
-    ("segment_tokens", -64), ("chain_group", -1), ("flags", 4), ("flags", -1),
+    ("segment_tokens", -64), ("chain_group", -1), ("flags", 8), ("flags", -1),
 ])
 def test_bad_problem_fields_are_rejected(field, value):
     p = prob()
@@ -176,7 +176,10 @@ def test_feature_prologue_validation_and_workspace():
     for kw in (dict(algo="recurrent"), dict(algo="chunked"), dict(intra="jacobi"),
                dict(algo="recurrent", qkv_dtype=G.F32)):
         for d in ("fwd", "bwd", "bidir"):
-            a = G.workspace_size(prob(**kw), d)
+            # (short single-scan calls without the prologue would take the
+            # strip scan, whose workspace is laid out differently)
+            with G.tuning(no_strip_scan=True):
+                a = G.workspace_size(prob(**kw), d)
             b = G.workspace_size(prob(prologue="features", **kw), d)
             if kw == dict(algo="chunked") and d == "bidir":
                 # at d_k <= 64 a bidirectional call without the prologue also
@@ -270,3 +273,31 @@ def test_step_noalloc_rejects_oversized_steps_before_any_hip_call():
     # one 880-token frame of 20 heads x 112 fits
     frame = prob(heads=20, d_k=112, d_v=112, frames=1, tokens_per_frame=880, algo="chunked")
     assert 0 < G.workspace_size(frame, "fwd") <= G.NOALLOC_SCRATCH_BYTES
+
+
+def test_strip_scan_plan_and_workspace():
+    """Forward- and backward-only calls of the chunked path with at most 32
+    sub-chunks per head (T <= 2048) and no prologue take the strip scan: one
+    segment of the whole (rounded) sequence and a workspace of 11008 bytes per
+    sub-chunk and head (fp16 Tm diag(beta) and P, 5120 bytes each, and three
+    rows of 64 fp32 gate factors); NO_STRIP_SCAN, longer calls, two-scan calls
+    and the prologue keep segment maps."""
+    sub = 2 * 5120 + 3 * 64 * 4
+    for T, heads, d in ((300, 2, 64), (880, 20, 112), (2048, 3, 16), (1, 1, 32)):
+        kw = dict(batch=2, heads=heads, d_k=d, d_v=d, frames=1, tokens_per_frame=T, qkv_dtype=G.BF16, algo="chunked")
+        p = G.make_problem(**kw)
+        U = (T + 63) // 64
+        for direction in ("fwd", "bwd"):
+            assert G.segment_plan(p, direction) == 64 * U
+            assert G.workspace_size(p, direction) == (2 * heads * U * sub + 255) // 256 * 256
+        with G.tuning(no_strip_scan=True):
+            q = G.make_problem(**kw)
+        assert G.workspace_size(q, "fwd") != G.workspace_size(p, "fwd")
+    # just past the limit, and the other cases, keep segment maps
+    p = G.make_problem(batch=1, heads=2, d_k=64, d_v=64, frames=1, tokens_per_frame=2049, qkv_dtype=G.BF16,
+                       algo="chunked")
+    assert G.segment_plan(p, "fwd") < 2049
+    for kw, d in ((dict(), "bidir"), (dict(), "chunk_causal"), (dict(prologue="features"), "fwd")):
+        p = G.make_problem(batch=1, heads=2, d_k=64, d_v=64, frames=4, tokens_per_frame=300, qkv_dtype=G.BF16,
+                           algo="chunked", first_chunk_frames=1, chunk_frames=1, **kw)
+        assert G.segment_plan(p, d) < 1200

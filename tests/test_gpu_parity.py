@@ -177,7 +177,7 @@ def test_inverse_reuse_is_bit_identical(direction, prologue):
             return run_pro(w, x, direction, c, algo="chunked")
         return run_gpu(w, x, direction, "chunked")
 
-    with G.tuning(segment_tokens=192):
+    with G.tuning(segment_tokens=192, no_strip_scan=True):
         with G.tuning(form_inverse=True):
             a = run()
         b = run()
@@ -202,8 +202,74 @@ def test_chunked_every_head_width(d, direction):
     maps, the chain and the outputs of every width are exercised."""
     w = WORKLOADS[4].resized(frames=2, tokens_per_frame=150, heads=3, d_k=d, d_v=d)
     x = make_inputs(w, 40 + d)
-    with G.tuning(segment_tokens=128):
+    with G.tuning(segment_tokens=128, no_strip_scan=True):
         check(w, x, direction, "chunked")
+
+
+# ---------------------------------------------------------------- strip scan
+
+def run_both(w, x, direction, out_dtype=None):
+    """The strip scan (the default for short single-scan calls) and segment
+    maps with their chain, on the same inputs."""
+    a = run_gpu(w, x, direction, "chunked", out_dtype)
+    with G.tuning(no_strip_scan=True):
+        b = run_gpu(w, x, direction, "chunked", out_dtype)
+    return a, b
+
+
+@pytest.mark.parametrize("d", DIMS + [64, 112])
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+def test_strip_scan_every_head_width(d, direction):
+    """Short forward- and backward-only calls take the strip scan: 300 tokens
+    (4 whole sub-chunks and a ragged one), batch 2, per-frame gates and an
+    initial state, every head width; against the oracle, and close to the
+    segment path (the same rounding points, sums in another order)."""
+    w = WORKLOADS[4].resized(batch=2, frames=2, tokens_per_frame=150, heads=3, d_k=d, d_v=d)
+    x = make_inputs(w, 140 + d)
+    (o, hT), (so, sH) = run_both(w, x, direction)
+    ro, rH = O.forward(direction, *oracle_args(x)[0], x["h0"])
+    eo, eh = rel_err(o, ro), rel_err(hT, rH)
+    print(f"[parity] strip scan d={d} {direction}: out {eo:.3e} state {eh:.3e}", flush=True)
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"], (eo, eh)
+    assert rel_err(o, so) <= 1e-2 and rel_err(hT, sH) <= 1e-2
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 880, 2048])
+def test_strip_scan_lengths(T):
+    """One frame of T tokens at d = 112 (the streaming shape, 2 heads):
+    from a single token to the longest call that takes the strip scan (32
+    sub-chunks)."""
+    w = WORKLOADS[3].resized(frames=1, tokens_per_frame=T, heads=2, h0_sigma=0.1)
+    x = make_inputs(w, 150 + T)
+    for direction in ("fwd", "bwd"):
+        check(w, x, direction, "chunked")
+
+
+def test_strip_scan_bf16_output_and_degenerate_gates():
+    """bf16 outputs (the fp32 result rounded once: the bar widens by
+    2^-8 max|ref| / RMS(ref)) and the degenerate gates through the strip scan."""
+    w = WORKLOADS[3].resized(frames=1, tokens_per_frame=700, heads=2, h0_sigma=0.1)
+    x = make_inputs(w, 160)
+    o, hT = run_gpu(w, x, "fwd", "chunked", out_dtype=torch.bfloat16)
+    ro, rH = O.fwd(*oracle_args(x)[0], x["h0"])
+    bound = TOL["bf16"] + 2.0 ** -8 * np.max(np.abs(ro)) / np.sqrt(np.mean(ro * ro))
+    assert rel_err(o, ro) <= bound and rel_err(hT, rH) <= TOL["bf16"]
+    for case in ("beta0", "nodecay", "strongdecay", "beta1"):
+        y = {k: v.copy() for k, v in x.items()}
+        if case == "beta0":
+            y["beta"][:] = 0.0
+        elif case == "nodecay":
+            y["log_gate"][:] = 0.0
+        elif case == "strongdecay":
+            y["log_gate"][:] = -20.0
+        else:
+            y["beta"][:] = 1.0
+        o, hT = run_gpu(w, y, "fwd", "chunked")
+        assert np.all(np.isfinite(o)) and np.all(np.isfinite(hT))
+        ro, rH = O.fwd(*oracle_args(y)[0], y["h0"])
+        eo, eh = rel_err(o, ro), rel_err(hT, rH)
+        print(f"[parity] strip scan degenerate {case}: out {eo:.3e} state {eh:.3e}", flush=True)
+        assert eo <= TOL["bf16"] and eh <= TOL["bf16"], (case, eo, eh)
 
 
 @pytest.mark.parametrize("d", DIMS)
@@ -239,7 +305,7 @@ def test_many_segments_and_heads():
     B = 3, H = 7, 4 frames of 97 tokens (388 tokens, 7 segments)."""
     w = WORKLOADS[4].resized(batch=3, heads=7, frames=4, tokens_per_frame=97)
     x = make_inputs(w, 80)
-    with G.tuning(segment_tokens=64):
+    with G.tuning(segment_tokens=64, no_strip_scan=True):
         for direction in ("fwd", "bidir"):
             check(w, x, direction, "chunked")
 
@@ -300,9 +366,9 @@ def test_split_chain_chunked(group, direction):
     600 tokens in segments of 64 (10 segments, 9 chain steps)."""
     w = WORKLOADS[4].resized(frames=4, tokens_per_frame=150, heads=3)
     x = make_inputs(w, 90 + group)
-    with G.tuning(segment_tokens=64, chain_group=1):
+    with G.tuning(segment_tokens=64, chain_group=1, no_strip_scan=True):
         whole = run_gpu(w, x, direction, "chunked")
-    with G.tuning(segment_tokens=64, chain_group=group):
+    with G.tuning(segment_tokens=64, chain_group=group, no_strip_scan=True):
         split = check(w, x, direction, "chunked")
         o, hT = run_gpu(w, x, direction, "chunked")
     # both are within the bar of the oracle; between them only the chain's
