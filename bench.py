@@ -13,15 +13,16 @@ With ``--workload stream60s_121x880_h20d112`` a step is the chunk-causal
 streaming loop: 121 gdn_step calls of one 880-token frame each, the state
 carried in place.
 
-Before timing, outputs and final states are checked against the float64 CPU
-oracle on sampled heads over the whole sequence (heads are independent, so a
-head's outputs and final state are exact targets); the same oracle, timed on
-one thread and on a pool of processes, is the reported CPU baseline.  The
-default run also measures, as secondary figures in the same line, the
-forward-only scan of the clip, the 5 s clip, the batched 2 x 35 x 64 workload
-(bidirectional and forward-only) and the 121-call streaming loop (per call,
-whole loop, and the loop replayed as one HIP graph).  Prints exactly one JSON
-line.
+Before timing, the outputs and final states of every (batch, head) pair are
+checked against the float64 CPU oracle over the whole sequence (heads are
+independent, so a head's outputs and final state are exact targets; 16 worker
+processes of one thread each); that same oracle run, and one pair on one
+thread, are the reported CPU baseline.  The default run also measures, as
+secondary figures in the same line, the forward-only scan of the clip, the 5 s
+clip, the batched 2 x 35 x 64 workload (bidirectional and forward-only) and
+the 121-call streaming loop (per call, whole loop, and the loop replayed as
+one HIP graph), each checked on one (batch, head) pair.  Prints exactly one
+JSON line.
 """
 from __future__ import annotations
 

@@ -268,7 +268,8 @@ gdn_status gdn_step(const gdn_problem* problem,
  * first call on a device takes the copy's address).  It allocates nothing.
  *   GDN_ERR_WORKSPACE_TOO_SMALL, with nothing enqueued, when the step's
  *   gdn_workspace_size(problem, GDN_FORWARD) exceeds the scratch (one
- *   880-token frame of 20 heads x 112 needs about 23 MB).
+ *   880-token frame of 20 heads x 112 needs about 3 MB; at that width steps
+ *   of up to 5120 tokens fit).
  * Every call on a device shares that device's scratch, which keeps the last
  * call's contents (nothing in it has to start at zero): calls that overlap on
  * one device (different streams, or threads without ordering) race on it and
