@@ -2553,22 +2553,37 @@ Plan make_plan(const Problem& p, int direction) {
   }
   int L = p.segment_tokens;
   if (L <= 0) {
-    // The output kernel runs one workgroup per CU (its LDS use), so aim for
-    // five whole rounds of workgroups over the 256 CUs of a gfx950 part:
-    // longer segments mean fewer serial steps in the chain kernel, and whole
-    // rounds avoid a partly idle last round.
-    constexpr long long kRounds = 5, kComputeUnits = 256;
+    // Segments per (batch, head).  Map and output workgroups run about one
+    // per CU, and the grid's segment index is padded to a multiple of 8 with
+    // workgroups dealt to the 8 XCDs (32 CUs each) in turn, so the busiest
+    // XCD holds hb * ceil(ns / 8) of them: a launch takes about
+    // ceil(hb * ceil(ns / 8) / 32) rounds of ceil(U / ns) + 1 sub-chunk steps
+    // (one for a workgroup's start).  Take the count with the fewest such
+    // steps, the smaller on ties, among 1..8 and multiples of 8 (whole rounds
+    // of the XCDs).  Measured: the 60 s clip keeps 64 segments (2.07 ms a
+    // bidirectional step, the best of lengths from 1408 to 2816 tokens); the
+    // batched 2 x 35 x 64 workload 19 -> 40 segments, 5.60 -> 4.58 ms
+    // (forward 2.90 -> 2.46 ms); the 5 s clip 33 -> 23 segments, 0.560 ->
+    // 0.535 ms (forward 0.356 -> 0.305 ms).  Across 8 lengths of the batched
+    // workload this count predicted the step time within 4%.
     const long long hb = (long long)p.B * p.H;
-    long long want = (kRounds * kComputeUnits + hb - 1) / hb;
+    const long long U = (p.T + CH - 1) / CH;
     // Short sequences: the chain's serial steps (one per segment, each about
     // as long as a sub-chunk step of the map and output kernels) would
     // outweigh the per-segment work, so keep at most about 2 sqrt(U)
     // segments for U sub-chunks (one 880-token frame: 7 segments of 128
     // tokens, 60 against 92 us a step with 14 segments of 64).
-    const long long U = (p.T + CH - 1) / CH;
     long long cap = 1;
     while ((cap + 1) * (cap + 1) <= 4 * U) ++cap;
-    if (want > cap) want = cap;
+    long long want = 1, best = -1;
+    for (long long ns = 1; ns <= cap; ns = ns < 8 ? ns + 1 : ns + 8) {
+      const long long rounds = (hb * ((ns + 7) / 8) + 31) / 32;
+      const long long steps = rounds * ((U + ns - 1) / ns + 1);
+      if (best < 0 || steps < best) {
+        best = steps;
+        want = ns;
+      }
+    }
     long long per = (p.T + want - 1) / want;
     L = (int)((per + CH - 1) / CH * CH);
   }
