@@ -230,6 +230,37 @@ def test_segment_plan_follows_the_problem():
     assert G.segment_plan(prob(algo="recurrent"), "bidir") == 0
 
 
+def _plan_steps(hb, U, ns):
+    """Launch time of a segment count in sub-chunk steps: the busiest of the
+    8 XCDs (32 CUs each) holds hb * ceil(ns / 8) workgroups, one per CU, each
+    ceil(U / ns) sub-chunks plus one step to start."""
+    return -(-hb * -(-ns // 8) // 32) * (-(-U // ns) + 1)
+
+
+@pytest.mark.parametrize("B,H,d,F,S,want", [
+    (1, 20, 112, 121, 880, 1664),   # the 60 s clip: 64 segments, five whole rounds
+    (2, 35, 64, 121, 880, 2688),    # the batched workload: 40 segments
+    (1, 20, 112, 21, 880, 832),     # the 5 s clip: 23 segments
+    (1, 20, 112, 3, 880, 384),      # three frames: 7 segments (the 2 sqrt(U) cap leaves 1..8)
+])
+def test_automatic_segment_plan(B, H, d, F, S, want):
+    """The automatic segment length takes the count with the fewest launch
+    steps (_plan_steps) among 1..8 and multiples of 8, at most about 2 sqrt(U)
+    for U sub-chunks, the smaller count on ties; forward and bidirectional
+    calls plan alike."""
+    p = G.make_problem(batch=B, heads=H, d_k=d, d_v=d, frames=F, tokens_per_frame=S, qkv_dtype=G.BF16,
+                       algo="chunked", tuning=G.Tuning(no_strip_scan=True))
+    T = F * S
+    U = -(-T // 64)
+    assert G.segment_plan(p, "bidir") == want == G.segment_plan(p, "fwd")
+    cap = 1
+    while (cap + 1) ** 2 <= 4 * U:
+        cap += 1
+    cands = [n for n in range(1, cap + 1) if n <= 8 or n % 8 == 0]
+    best = min(cands, key=lambda n: (_plan_steps(B * H, U, n), n))
+    assert want == -(-(-(-T // best)) // 64) * 64
+
+
 def test_inverse_reuse_workspace():
     """A forward-only chunked call with more than one segment holds 5 KB of
     fp16 inverse blocks per 64-token sub-chunk and head, whether or not the
