@@ -2136,23 +2136,25 @@ __global__ __launch_bounds__(64 * (D / 16)) void jac_out_kernel(Args a) {
 //     16x16 blocks each) and the factors e^G, c e^G, c e^{G_n - G};
 //   sc_scan_kernel (one workgroup per 16-column strip of the state and head):
 //     the sub-chunks in scan order with short dependent steps.  Four compute
-//     wavefronts each own one 16-token row tile of the sub-chunk:
-//       K H and (Q H)^T for its rows      (the state strip read from LDS, fp16)
-//       R = V - c e^G * K H                -> LDS
-//       V' = Tm diag(beta) R               -> LDS (also scaled by c e^{G_n - G})
-//       O = e^G * Q H + P V'               -> global
-//       H <- e^{G_n} H + K^T (c e^{G_n - G} V')   (wave r: tiles r and r + 4)
-//     with three barriers per sub-chunk; four stager wavefronts convert and
-//     stage the next sub-chunk's rows meanwhile, their loads issued two
-//     sub-chunks ahead.  The same algebra and rounding points as the output
-//     kernel, in another order of the sums.
+//     wavefronts, wave r owning the outputs of 16-token row tile r and state
+//     tiles r and r + 4, each form in registers
+//       K H (all 64 rows) and (Q H)^T (its rows)   (the state strip from LDS, fp16)
+//       R = V - c e^G * K H,  V' = Tm diag(beta) R (all 64 rows)
+//       O = e^G * Q H + P V'               -> global (its rows)
+//       H <- e^{G_n} H + K^T (c e^{G_n - G} V')   (its state tiles -> LDS)
+//     with one barrier per sub-chunk (the state strip double-buffered in LDS);
+//     four stager wavefronts convert and stage the next sub-chunk's rows
+//     meanwhile, their loads issued two sub-chunks ahead.  The same algebra
+//     and rounding points as the output kernel, in another order of the sums.
 // Measured on one 880-token frame of 20 heads x 112 (the streaming shape):
-// 60 -> 35 us a call (captured in a HIP graph); the scan kernel takes about
-// 27 us, of which staging (bf16 -> fp16 conversion and scattered LDS writes,
-// bound by the CU's VALU issue) is about 9 us: a copy without it ran in 18 us.
-// Preparing the rows in fp16 in the prep kernel instead (a plain copy in the
-// scan) measured no faster: the prep kernel's extra stores cost what the
-// scan saved (prep 11 -> 15 us, scan 27 -> 25.5 us).
+// 60 -> 31 us a call (captured in a HIP graph).  Each wave repeating K H and
+// V' for the whole strip (16 and 6 products instead of 4 and 1-2) removed
+// the exchanges of R and V' through LDS and two of three barriers per
+// sub-chunk: the scan kernel 27.9 -> 24.2 us.  Staging (bf16 -> fp16
+// conversion and scattered LDS writes) cost about 9 us of the three-barrier
+// kernel's 27 (a copy without it ran in 18 us); preparing the rows in fp16
+// in the prep kernel instead measured no faster (prep 11 -> 15 us, scan
+// 27 -> 25.5 us).
 
 // Per sub-chunk and head in the workspace: Tm diag(beta) and P as 320 pieces
 // of 16 bytes each (the piece order of the stored inverses), then e^G,
@@ -2241,11 +2243,9 @@ struct ScanLay {
   static constexpr int BUF = o_vt + 16 * LVT * 4;   // one sub-chunk buffer (two alternate)
   static constexpr int LH = DP + 8;                 // fp16 stride of the transposed state strip
   static constexpr int LR = CH + 8;                 // fp16 stride of the transposed token strips
-  static constexpr int o_hh = 2 * BUF;
-  static constexpr int o_rt = o_hh + 16 * LH * 2;
-  static constexpr int o_vp = o_rt + 16 * LR * 2;
-  static constexpr int o_vs = o_vp + 16 * LR * 2;
-  static constexpr int BYTES = o_vs + 16 * LR * 2;
+  static constexpr int HH = 16 * LH * 2;            // one copy of the state strip
+  static constexpr int o_hh = 2 * BUF;              // two: read in one sub-chunk, written for the next
+  static constexpr int BYTES = o_hh + 2 * HH;
   static constexpr int NC = 256;                              // compute threads: four wavefronts
   static constexpr int NS = 256;                              // stager threads: four wavefronts
   static constexpr int NKQ = (CH * (D / 8) + NS - 1) / NS;    // 16-byte K (and Q) pieces per stager thread
@@ -2352,10 +2352,8 @@ __global__ __launch_bounds__(ScanLay<D>::NC + ScanLay<D>::NS) void sc_scan_kerne
       }
     }
   };
-  hb* const hh = reinterpret_cast<hb*>(smem + SL::o_hh);
-  hb* const rt = reinterpret_cast<hb*>(smem + SL::o_rt);
-  hb* const vp = reinterpret_cast<hb*>(smem + SL::o_vp);
-  hb* const vs = reinterpret_cast<hb*>(smem + SL::o_vs);
+  // the state strip of sub-chunk jj (fp16, transposed): copy jj & 1
+  auto hh = [&](long long jj) { return reinterpret_cast<hb*>(lds_at(smem, (uint32_t)(SL::o_hh + (jj & 1) * SL::HH))); };
   // state tiles of this wave: rows 16 md .. of the strip, md = r and r + 4
   constexpr int NMT = (MD + 3) / 4;
   f32x4 Hm[NMT];
@@ -2393,8 +2391,6 @@ __global__ __launch_bounds__(ScanLay<D>::NC + ScanLay<D>::NS) void sc_scan_kerne
       stage((int)((jj + 1) & 1), st);
       fetch(jj + 3, st);
       __syncthreads();
-      __syncthreads();
-      __syncthreads();
     };
     for (long long jj = 0; jj < U; jj += 2) {
       sstep(jj, s1);
@@ -2406,7 +2402,7 @@ __global__ __launch_bounds__(ScanLay<D>::NC + ScanLay<D>::NS) void sc_scan_kerne
 #pragma unroll
   for (int i = 0; i < NMT; ++i) {
     const int md = r + 4 * i;
-    if (md < MD) store4_h(hh + cl * SL::LH + 16 * md + 4 * g, Hm[i][0], Hm[i][1], Hm[i][2], Hm[i][3]);
+    if (md < MD) store4_h(hh(0) + cl * SL::LH + 16 * md + 4 * g, Hm[i][0], Hm[i][1], Hm[i][2], Hm[i][3]);
   }
   __syncthreads();
   auto cstep = [&](long long jj) {
@@ -2420,47 +2416,55 @@ __global__ __launch_bounds__(ScanLay<D>::NC + ScanLay<D>::NS) void sc_scan_kerne
     const float* eg = reinterpret_cast<const float*>(pc + SL::o_gf);
     const float* ce = eg + CH;
     const float* dn = eg + 2 * CH;
-    f32x4 qh = zero4();
-    // K H (lane: rows 16 r + 4 g .., column cl) and (Q H)^T (lane: token
-    // 16 r + cl, columns 4 g ..) for this wave's row tile
-    f32x4 kh = zero4();
+    // K H for all four row tiles (lane: rows 16 mt + 4 g .., column cl) and
+    // (Q H)^T for this wave's tile (lane: token 16 r + cl, columns 4 g ..).
+    // Every wave forms the whole R = V - c e^G K H and V' = Tm diag(beta) R
+    // of the strip in registers (products repeated in the four waves), so
+    // that a sub-chunk exchanges only the state strip: one barrier each.
+    f32x4 qh = zero4(), kh[4];
     {
+      const hb* hs = hh(jj);
       f16x8_t Hf[NP];
 #pragma unroll
       for (int p = 0; p < NP; ++p)
-        Hf[p] = cat8(ld4(hh + cl * SL::LH + 32 * p + 4 * g), ld4(hh + cl * SL::LH + 32 * p + 16 + 4 * g));
+        Hf[p] = cat8(ld4(hs + cl * SL::LH + 32 * p + 4 * g), ld4(hs + cl * SL::LH + 32 * p + 16 + 4 * g));
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) kh[mt] = zero4();
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        kh = mfma32(fragK<D>(kr + krow<D>(16 * r + cl), p, g), Hf[p], kh);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) kh[mt] = mfma32(fragK<D>(kr + krow<D>(16 * mt + cl), p, g), Hf[p], kh[mt]);
         qh = mfma32(Hf[p], fragK<D>(qr + krow<D>(16 * r + cl), p, g), qh);
       }
     }
+    // Lane holds R and V' rows 16 mt + 4 g .., column cl: tiles (0, 1) and
+    // (2, 3) are the fp16 operand pairs of the token contractions below.
+    f16x8_t Vh[2], Vs[2];
     {
-      const f32x4 v4 = ld4f(vt + cl * SL::LVT + 16 * r + 4 * g), c4 = ld4f(ce + 16 * r + 4 * g);
-      const f32x4 R = v4 - c4 * kh;
-      store4_h(rt + cl * SL::LR + 16 * r + 4 * g, R[0], R[1], R[2], R[3]);
+      f32x4 R[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        R[mt] = ld4f(vt + cl * SL::LVT + 16 * mt + 4 * g) - ld4f(ce + 16 * mt + 4 * g) * kh[mt];
+      const f16x8_t r0 = tof16x8(R[0], R[1]), r1 = tof16x8(R[2], R[3]);
+      f32x4 vn[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        vn[mt] = mfma32(fragA2(tt + (16 * mt + cl) * LDT, 0, g), r0, zero4());
+        if (mt >= 2) vn[mt] = mfma32(fragA2(tt + (16 * mt + cl) * LDT, 2, g), r1, vn[mt]);
+      }
+      Vh[0] = tof16x8(vn[0], vn[1]);
+      Vh[1] = tof16x8(vn[2], vn[3]);
+      f32x4 d4[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) d4[mt] = ld4f(dn + 16 * mt + 4 * g);
+      Vs[0] = tof16x8(vn[0] * d4[0], vn[1] * d4[1]);
+      Vs[1] = tof16x8(vn[2] * d4[2], vn[3] * d4[3]);
     }
-    __syncthreads();
-    // V' rows of this wave's tile: Tm diag(beta) (lower triangular) times R
-    {
-      f32x4 vn = mfma32(fragA2(tt + (16 * r + cl) * LDT, 0, g),
-                        cat8(ld4(rt + cl * SL::LR + 4 * g), ld4(rt + cl * SL::LR + 16 + 4 * g)), zero4());
-      if (r >= 2)
-        vn = mfma32(fragA2(tt + (16 * r + cl) * LDT, 2, g),
-                    cat8(ld4(rt + cl * SL::LR + 32 + 4 * g), ld4(rt + cl * SL::LR + 48 + 4 * g)), vn);
-      const f32x4 d4 = ld4f(dn + 16 * r + 4 * g);
-      store4_h(vp + cl * SL::LR + 16 * r + 4 * g, vn[0], vn[1], vn[2], vn[3]);
-      store4_h(vs + cl * SL::LR + 16 * r + 4 * g, vn[0] * d4[0], vn[1] * d4[1], vn[2] * d4[2], vn[3] * d4[3]);
-    }
-    __syncthreads();
     // outputs: O^T = e^G (Q H)^T + (P V')^T, lane: token 16 r + cl, columns 16 s + 4 g ..
     {
       f32x4 O = eg[16 * r + cl] * qh;
-      O = mfma32(cat8(ld4(vp + cl * SL::LR + 4 * g), ld4(vp + cl * SL::LR + 16 + 4 * g)),
-                 fragA2(pp + (16 * r + cl) * LDT, 0, g), O);
-      if (r >= 2)
-        O = mfma32(cat8(ld4(vp + cl * SL::LR + 32 + 4 * g), ld4(vp + cl * SL::LR + 48 + 4 * g)),
-                   fragA2(pp + (16 * r + cl) * LDT, 2, g), O);
+      O = mfma32(Vh[0], fragA2(pp + (16 * r + cl) * LDT, 0, g), O);
+      if (r >= 2) O = mfma32(Vh[1], fragA2(pp + (16 * r + cl) * LDT, 2, g), O);
       const __amdgpu_buffer_rsrc_t ro =
           rows_rsrc(static_cast<char*>(a.out) + (hbase + sb.t0 * HD) * esz, (long long)sb.n * HD * esz);
       const uint32_t off = (uint32_t)(((sb.r0 + sb.sgn * (16 * r + cl)) * HD + 16 * s + 4 * g) * esz);
@@ -2475,8 +2479,6 @@ __global__ __launch_bounds__(ScanLay<D>::NC + ScanLay<D>::NS) void sc_scan_kerne
     }
     // state: H <- e^{G_n} H + K^T (c e^{G_n - G} V') for this wave's tiles
     if (jj < U) {
-      const f16x8_t vs0 = cat8(ld4(vs + cl * SL::LR + 4 * g), ld4(vs + cl * SL::LR + 16 + 4 * g));
-      const f16x8_t vs1 = cat8(ld4(vs + cl * SL::LR + 32 + 4 * g), ld4(vs + cl * SL::LR + 48 + 4 * g));
       const hb* kt = kr + krow<D>(4 * g + (cl >> 2)) + 4 * (cl & 3);
       const float dec = eg[CH - 1];
 #pragma unroll
@@ -2486,10 +2488,10 @@ __global__ __launch_bounds__(ScanLay<D>::NC + ScanLay<D>::NS) void sc_scan_kerne
           const f16x8_t k0 = cat8(ld4_tr(kt + 16 * md), ld4_tr(kt + krow<D>(16) + 16 * md));
           const f16x8_t k1 = cat8(ld4_tr(kt + krow<D>(32) + 16 * md), ld4_tr(kt + krow<D>(48) + 16 * md));
           f32x4 X = Hm[i] * dec;
-          X = mfma32(k0, vs0, X);
-          X = mfma32(k1, vs1, X);
+          X = mfma32(k0, Vs[0], X);
+          X = mfma32(k1, Vs[1], X);
           Hm[i] = X;
-          store4_h(hh + cl * SL::LH + 16 * md + 4 * g, X[0], X[1], X[2], X[3]);
+          store4_h(hh(jj + 1) + cl * SL::LH + 16 * md + 4 * g, X[0], X[1], X[2], X[3]);
         }
       }
     }
