@@ -1340,15 +1340,21 @@ __device__ __forceinline__ bf16x8_t fragB2(const bh* arow, int q, int g) {
   return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// fp32 tile -> (hi, lo) bf16 halves, each as 4 raw values
+// fp32 tile -> (hi, lo) bf16 halves, each as 4 raw values: hi = x rounded to
+// bf16 (nearest, ties to even), lo = (x - hi) rounded likewise; the
+// conversions are packed two values at a time.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void split4(f32x4 v, s16x4_t& hi, s16x4_t& lo) {
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float x = v[r];
-    const bh h = f2bh(x);
-    hi[r] = (short)h;
-    lo[r] = (short)f2bh(x - bh2f(h));
-  }
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  const uint32_t h01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{v[0], v[1]}, bf16x2_t));
+  const uint32_t h23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{v[2], v[3]}, bf16x2_t));
+  const f32x2_t r01{v[0] - __uint_as_float(h01 << 16), v[1] - __uint_as_float(h01 & 0xffff0000u)};
+  const f32x2_t r23{v[2] - __uint_as_float(h23 << 16), v[3] - __uint_as_float(h23 & 0xffff0000u)};
+  const uint32_t l01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(r01, bf16x2_t));
+  const uint32_t l23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(r23, bf16x2_t));
+  hi = __builtin_bit_cast(s16x4_t, u32x2_t{h01, h23});
+  lo = __builtin_bit_cast(s16x4_t, u32x2_t{l01, l23});
 }
 
 // Modes (Args::ch_mode), for chains long enough to be worth splitting:
@@ -1550,11 +1556,16 @@ __global__ __launch_bounds__((64 * ChainSplitCols<D, CS>::NW)) void seg_chain_ke
   // header and executed every step, where it waits for the prefetched maps.
   __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
   if constexpr (AHEAD == 2) {
-    // prA holds P_{p+1} at even offsets p - p0, prB at odd ones
-    for (int p = p0; p < p1; p += 2) {
+    // prA holds P_{p+1} at even offsets p - p0, prB at odd ones.  The loop
+    // body has no branch (a step skipped on one path would leave its loads
+    // pending at the loop header, where the compiler would then wait for
+    // every load in flight); an odd last step runs after it.
+    int p = p0;
+    for (; p + 1 < p1; p += 2) {
       step(p, prA, prB);
-      if (p + 1 < p1) step(p + 1, prB, prA);
+      step(p + 1, prB, prA);
     }
+    if (p < p1) step(p, prA, prB);
   } else {
     for (int p = p0; p < p1; ++p) step(p, prA, prA);
   }

@@ -106,6 +106,32 @@ def test_bf16_output(algo):
     assert rel_err(o, ro) <= bound and rel_err(hT, rH) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("direction", ["fwd", "bidir"])
+@pytest.mark.parametrize("algo", ALGOS)
+def test_bf16_output_is_the_fp32_output_rounded(algo, direction):
+    """The bf16 output mode stores the fp32 result rounded once to the nearest
+    bf16 (ties to even): element for element it equals the fp32 output of the
+    same call rounded by torch, and that fp32 output meets the bar, so the
+    one rounding is the mode's only departure from it."""
+    w = SMALL["batched"]
+    need(algo, w)
+    x = make_inputs(w, 2)
+    d = to_device(x, w.qkv_dtype)
+    h0 = d["h0"] if np.any(x["h0"]) else None
+    outs = []
+    for odt in (torch.float32, torch.bfloat16):
+        out, _ = G.forward(d["q"], d["k"], d["v"], d["log_gate"], d["beta"], h0, direction,
+                           tokens_per_frame=w.tokens_per_frame, algo=algo, out_dtype=odt)
+        outs.append(out)
+    torch.cuda.synchronize()
+    rounded = outs[0].to(torch.bfloat16)
+    assert outs[1].dtype == torch.bfloat16
+    assert torch.equal(outs[1].view(torch.int16), rounded.view(torch.int16))
+    a, oh0 = oracle_args(x)
+    ro, _ = O.forward(direction, *a, oh0)
+    assert rel_err(to_numpy(outs[0]), ro) <= TOL[w.qkv_dtype]
+
+
 @pytest.mark.parametrize("algo", ALGOS)
 def test_step_chain_matches_oracle_and_forward(algo):
     """Chunk-causal streaming: chained one-frame steps, state carried (in place)."""
